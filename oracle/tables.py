@@ -78,7 +78,7 @@ class Table:
     cum: np.ndarray      # [M+1] int64, c_m = sum_{j<m} f_j
     cost: np.ndarray     # [M] int64, fixed-point cost of each symbol
     sym: np.ndarray      # [2^p] int64, slot -> symbol
-    inner: np.ndarray    # [M] int64, inward neighbour of each level (-1: none)
+    inner: np.ndarray    # [M] int64, drift target of each level (-1: none)
     f_min: int
     budget_fx: int       # (8C - sigma) * 2^16
     feasible: bool
@@ -150,20 +150,39 @@ def make_table(levels: int, container: int, step: float | None = None, alpha: fl
     for m in range(M):
         sym[cum[m]:cum[m + 1]] = m
 
-    # inward neighbour: one level toward zero; none for a level at zero
+    # drift target: the nearest level toward zero whose cost is strictly lower
+    # (section 4.3: expensive symbols drift to nearby cheaper ones). Where the
+    # costs grow outward this is the adjacent inner level; a tie (tail levels
+    # both at f_min) is skipped over. The walk stops after the first level at
+    # or across zero; -1 means the level never drifts.
     inner = np.full(M, -1, dtype=np.int64)
     for m in range(M):
-        if recon[m] > 0:
-            inner[m] = m - 1
-        elif recon[m] < 0:
-            inner[m] = m + 1
+        d = -1 if recon[m] > 0 else (1 if recon[m] < 0 else 0)
+        j = m + d
+        while d != 0 and 0 <= j < M:
+            if cost[j] < cost[m]:
+                inner[m] = j
+                break
+            if recon[j] * recon[m] <= 0:
+                break
+            j += d
 
     budget_fx = (8 * C - FLUSH_BITS) * COST_ONE
-    # the all-central stream must fit with a byte of rANS slack
-    central = int(cost.min()) if feasible else 0
-    if feasible and n * central + 8 * COST_ONE > budget_fx:
+    # Drift moves a symbol only to its (strictly cheaper) drift target, so
+    # from level m it can at most reach the end of that chain. Every stream
+    # must fit once all its symbols sit at such terminal levels, with a byte
+    # of rANS slack. (Where costs grow outward every chain ends at a central
+    # level.)
+    worst = 0
+    if feasible:
+        for m in range(M):
+            cur = m
+            while inner[cur] >= 0:
+                cur = int(inner[cur])
+            worst = max(worst, int(cost[cur]))
+    if feasible and n * worst + 8 * COST_ONE > budget_fx:
         feasible = False
-        notes.append("all-central stream does not fit the container")
+        notes.append("a stream of drift-terminal levels does not fit the container")
 
     return Table(levels=M, container=C, step=float(step), alpha=float(alpha), prob_bits=p, n=n,
                  recon=recon, bounds=bounds, mass=mass, sharpened=sharpened, freq=freq, cum=cum,

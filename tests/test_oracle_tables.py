@@ -107,3 +107,26 @@ def test_nearest_level_brute_force_and_ties(M, C):
         else:
             assert got == M // 2 - 1
         assert abs(t.recon[got]) <= abs(t.recon[j + (1 if got == j else 0)])
+
+
+def test_feasibility_follows_drift_reachability():
+    """Drift only moves a symbol inward to a strictly cheaper level (section 4.3),
+    so feasibility is judged on the levels drift can end at. A grid so narrow
+    that the outer cells are the likeliest (cheapest) cannot be drifted into
+    budget, and is rejected; every table judged feasible encodes adversarial
+    streams (all values in the outermost cells, alternating signs) without error."""
+    assert not oracle.make_table(6, 32, step=0.3).feasible
+    x = np.tile(np.array([9.0, -9.0] * 64), (4, 1))
+    x[1] = np.linspace(-3, 3, 128)
+    x[2, ::3] = 0.0
+    x[3] = np.random.default_rng(0).standard_normal(128)
+    checked = 0
+    for M in (4, 6, 8):
+        for C in (24, 28, 32, 37):
+            for step in (0.3, 0.6, 0.9, 1.2, 1.6):
+                t = oracle.make_table(M, C, step=step)
+                if t.feasible:
+                    r = oracle.encode_streams(x, t)
+                    assert (r.lengths <= C).all()
+                    checked += 1
+    assert checked > 10
