@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused D-Quant decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one decode step of the Qwen3-8B-shaped workload over all 36 layer
+caches (batch 128, 8192-token context, 32 query / 8 KV heads, 37-byte
+containers, 8 key / 6 value levels): 36 calls of dq_decode_attention, each
+reading one layer's compressed cache straight from HBM. Caches are built
+beforehand by the library's encoder from seeded synthetic N(0,1) rows and
+stay resident in HBM.
+
+Prints one JSON line: compressed-KV GB/s (the value), its fraction of the
+8 TB/s HBM peak, attention-only tokens/s, the roofline of the decode kernel
+(integer-ALU bound: 8 lane-ops per decoded symbol against the 39.3 T lane-op/s
+of 256 CUs x 64 lanes x 2.4 GHz) and the CPU oracle timed on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12      # int32 lane-ops per second, in T
+OPS_PER_SYMBOL = 8                            # lane-ops of one rANS decode step
+METRIC = "decode-attn compressed-KV GB/s (% HBM peak) and tokens/s at B=128, 8K ctx"
+
+
+def algorithmic_bytes(w, lens) -> int:
+    """Compressed bytes one attention call must read: K and V containers plus
+    their fp16 norms for every (token, KV head) of every sequence."""
+    per_stream_pair = (w.container + 2) * 2
+    return int(np.sum(lens)) * w.num_kv_heads * per_stream_pair
+
+
+def cpu_baseline(w, tables_host, samples: int, dq_units):
+    """The oracle, untouched, timed on `samples` (sequence, KV head) units of
+    the workload: rANS decode of every K and V container, reconstruction and
+    fp64 attention for the query heads of that KV head. The containers are
+    produced beforehand by the oracle's own encoder (not timed)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    from decode_attention_dq_amd import synth, workloads
+    tk, tv = tables_host
+    G = w.num_q_heads // w.num_kv_heads
+    q = workloads.query_rows(w, 0).float().cpu().numpy()
+    timed, nbytes = 0.0, 0
+    with threadpool_limits(1):
+        for (b, g) in dq_units[:samples]:
+            T = int(workloads.context_lengths(w)[b])
+            k = workloads.kv_rows(w, 0, synth.T_K, b, T)[:, g].float().cpu().numpy().astype(np.float64)
+            v = workloads.kv_rows(w, 0, synth.T_V, b, T)[:, g].float().cpu().numpy().astype(np.float64)
+            rk = oracle.encode_streams(k, tk)
+            rv = oracle.encode_streams(v, tv)
+            t0 = time.perf_counter()
+            sk, _ = oracle.decode_streams(rk.containers, tk)
+            sv, _ = oracle.decode_streams(rv.containers, tv)
+            kh = oracle.reconstruct(sk, rk.rho16, tk)
+            vh = oracle.reconstruct(sv, rv.rho16, tv)
+            oracle.attention(q[b:b + 1, g * G:(g + 1) * G], [kh[None]], [vh[None]])
+            timed += time.perf_counter() - t0
+            nbytes += T * (w.container + 2) * 2
+    return {"value": round(nbytes / timed / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{samples} (sequence, KV head) units x {T} tokens of {w.name}: decode K and V "
+                      f"containers, reconstruct, fp64 attention for {G} query heads; "
+                      f"{timed:.1f} s timed on {platform.processor() or platform.machine()}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_qwen3_8b")
+    ap.add_argument("--splits", type=int, default=0, help="token splits per (sequence, KV head); 0 = library rule")
+    ap.add_argument("--cpu-samples", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode-attention path has no "
+              f"multi-GPU mode in this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    from decode_attention_dq_amd import dq, workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    tables = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.container))
+    t_build = time.perf_counter()
+    caches = [workloads.build_cache(dq, tables, w, layer=l) for l in range(w.layers)]
+    qs = [workloads.query_rows(w, l) for l in range(w.layers)]
+    torch.cuda.synchronize()
+    t_build = time.perf_counter() - t_build
+    print(f"[bench] built {w.layers} layer caches of {w.name} in {t_build:.1f} s", file=sys.stderr, flush=True)
+
+    B, hq, hkv = w.batch, w.num_q_heads, w.num_kv_heads
+    lens = caches[0].lens
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dq.dq_workspace_size(B, hq, hkv, w.context, args.splits), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(l):
+        c = caches[l]
+        dq.dq_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
+                               c.context_lens, hkv, w.page_size, w.context, out, ws, num_splits=args.splits,
+                               err_word=err, stream=stream)
+
+    for _ in range(args.warmup):
+        for l in range(w.layers):
+            call(l)
+    torch.cuda.synchronize()
+
+    n_calls = args.steps * w.layers
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    i = 0
+    for _ in range(args.steps):
+        for l in range(w.layers):
+            ev[i][0].record(stream)
+            call(l)
+            ev[i][1].record(stream)
+            i += 1
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        print("[bench] device integrity error", file=sys.stderr)
+        return 1
+    ms_total = t_all0.elapsed_time(t_all1)
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = ms_total / args.steps
+    per_call_s = float(call_ms.mean()) / 1e3
+
+    nbytes = algorithmic_bytes(w, lens)
+    symbols = int(np.sum(lens)) * hkv * 128 * 2
+    gbs = nbytes / per_call_s / 1e9
+    tops = symbols * OPS_PER_SYMBOL / per_call_s / 1e12
+    splits = args.splits or dq._lib.dq_workspace_size(B, hq, hkv, w.context, 0) // (B * hq * 132 * 4)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "context": w.context, "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": 128, "layers": w.layers, "container_bytes": w.container,
+                   "levels": [w.k_levels, w.v_levels], "page_size": w.page_size, "splits": int(splits),
+                   "q_dtype": "bf16" if w.q_bf16 else "f32"},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
+        "us_per_layer_call": round(per_call_s * 1e6, 2),
+        "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
+                     "unit": "Tops/s", "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_call": nbytes, "symbols_per_call": symbols,
+                     "hbm_GBps": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        tk = oracle.make_table(w.k_levels, w.container)
+        tv = oracle.make_table(w.v_levels, w.container)
+        units = [(b, g) for b in range(B) for g in range(hkv)]
+        rng = np.random.default_rng(0)
+        units = [units[i] for i in rng.permutation(len(units))]
+        result["cpu_baseline"] = cpu_baseline(w, (tk, tv), args.cpu_samples, units)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,400 @@
+// Host side of libdq: table derivation, argument checks, split choice and
+// launches. Every entry point is extern "C" and returns a status code.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "dq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = hipGetErrorString(e);
+    return DQ_ERR_HIP;
+}
+
+// fp64 -> fp16 bits, one rounding to nearest even (host copy; only used for
+// the small exact level values stored in the decode table).
+uint16_t host_f64_to_f16(double d) {
+    uint64_t b;
+    memcpy(&b, &d, 8);
+    uint32_t sign = (uint32_t)(b >> 63) << 15;
+    int exp = (int)((b >> 52) & 0x7FF);
+    uint64_t mant = b & ((1ull << 52) - 1);
+    if (exp == 0x7FF) return (uint16_t)(sign | 0x7C00 | (mant ? 0x200 : 0));
+    if (exp == 0) return (uint16_t)sign;   // fp64 subnormals are far below fp16's range
+    int e = exp - 1023;
+    uint64_t m53 = mant | (1ull << 52);
+    int shift;            // bits dropped from m53
+    uint32_t base;        // exponent field contribution
+    if (e >= -14) {
+        shift = 42;
+        base = (uint32_t)(e + 15) << 10;
+        m53 &= (1ull << 52) - 1;   // implicit bit handled through `base`
+    } else {
+        shift = 28 - e;   // subnormal: value / 2^-24
+        base = 0;
+        if (shift > 62) return (uint16_t)sign;
+    }
+    uint64_t q = m53 >> shift;
+    uint64_t rem = m53 & ((1ull << shift) - 1);
+    uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (q & 1))) q++;
+    uint32_t r = base + (uint32_t)q;   // a mantissa carry bumps the exponent
+    if (r >= 0x7C00) return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | r);
+}
+
+double std_normal_cdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+double default_step(int levels, int container) {
+    if (container == 37 && levels == 8) return 0.92;
+    if (container == 37 && levels == 6) return 0.90;
+    if (container == 32 && levels == 8) return 1.12;
+    if (container == 32 && levels == 6) return 1.09;
+    return 0.0;
+}
+
+// Table derivation. The probability model is the N(0,1) mass of each
+// level's nearest-neighbour cell (the paper derives its model directly from
+// the standard normal: section 1, section 3.2), sharpened by p^alpha and
+// renormalised (section 4.4), then quantised to integer frequencies summing
+// to 2^p for the rANS pair of section 3.1.
+int describe(const dq_table_params* in, dq_table_info* t) {
+    if (!in || !t) return DQ_ERR_INVALID_ARG;
+    memset(t, 0, sizeof(*t));
+    const int M = in->levels, C = in->container;
+    const int p = in->prob_bits ? in->prob_bits : 10;
+    const double alpha = in->alpha > 0 ? in->alpha : 1.4;
+    double step = in->step > 0 ? in->step : default_step(M, C);
+    if (M < 2 || M > dq::kMaxLevels || p < 9 || p > dq::kMaxProbBits || C < 8 || C > 128)
+        return DQ_ERR_UNSUPPORTED;
+    if (!(step > 0) || !(alpha > 0) || !isfinite(step) || !isfinite(alpha)) return DQ_ERR_INVALID_ARG;
+    t->levels = M;
+    t->container = C;
+    t->prob_bits = p;
+    t->step = step;
+    t->alpha = alpha;
+    const uint32_t total = 1u << p;
+    const uint32_t f_min = 1u << (p - 8);
+
+    const double half = (M - 1) / 2.0;
+    for (int m = 0; m < M; ++m) t->recon[m] = step * ((double)m - half);
+    for (int j = 1; j < M; ++j) t->bounds[j - 1] = (t->recon[j - 1] + t->recon[j]) / 2.0;
+
+    // cell masses, lower half from the CDF (accurate tail), mirrored
+    for (int m = 0; m < M / 2; ++m) {
+        double lo = (m == 0) ? 0.0 : std_normal_cdf(t->bounds[m - 1]);
+        double hi = (M % 2 == 0 && m == M / 2 - 1) ? 0.5 : std_normal_cdf(t->bounds[m]);
+        t->mass[m] = hi - lo;
+        t->mass[M - 1 - m] = t->mass[m];
+    }
+    if (M % 2 == 1) {
+        int c = M / 2;
+        t->mass[c] = erf(-t->bounds[c - 1] / sqrt(2.0));
+    }
+
+    // sharpening, normalised by a left-to-right sum
+    double w[16], s = 0.0;
+    for (int m = 0; m < M; ++m) w[m] = pow(t->mass[m], alpha);
+    for (int m = 0; m < M; ++m) s += w[m];
+
+    int64_t sum = 0;
+    for (int m = 0; m < M / 2; ++m) {
+        double r = nearbyint((w[m] / s) * (double)total);   // round half to even
+        int64_t f = (int64_t)r;
+        if (f < (int64_t)f_min) f = f_min;
+        t->freq[m] = (uint32_t)f;
+        t->freq[M - 1 - m] = (uint32_t)f;
+        sum += 2 * f;
+    }
+    bool ok = true;
+    if (M % 2 == 0) {
+        int64_t resid = (int64_t)total - sum;      // even
+        int64_t a = t->freq[M / 2 - 1] + resid / 2;
+        int64_t b = t->freq[M / 2] + resid / 2;
+        if (a < (int64_t)f_min || b < (int64_t)f_min) ok = false;
+        t->freq[M / 2 - 1] = (uint32_t)(a < 0 ? 0 : a);
+        t->freq[M / 2] = (uint32_t)(b < 0 ? 0 : b);
+    } else {
+        int64_t c = (int64_t)total - sum;
+        if (c < (int64_t)f_min) ok = false;
+        t->freq[M / 2] = (uint32_t)(c < 0 ? 0 : c);
+    }
+    t->cum[0] = 0;
+    for (int m = 0; m < M; ++m) t->cum[m + 1] = t->cum[m] + t->freq[m];
+    if (t->cum[M] != total) ok = false;
+
+    for (int m = 0; m < M; ++m) {
+        if (t->freq[m] == 0) { ok = false; continue; }
+        t->cost[m] = (int64_t)nearbyint(((double)p - log2((double)t->freq[m])) * (double)(1 << dq::kCostFracBits));
+    }
+    // drift target: the nearest level toward zero with a strictly lower cost
+    // (expensive symbols drift to nearby cheaper ones, section 4.3); the walk
+    // ends after the first level at or across zero
+    for (int m = 0; m < M; ++m) {
+        t->inner[m] = -1;
+        const int d = t->recon[m] > 0 ? -1 : (t->recon[m] < 0 ? 1 : 0);
+        for (int j = m + d; d != 0 && j >= 0 && j < M; j += d) {
+            if (t->cost[j] < t->cost[m]) { t->inner[m] = j; break; }
+            if (t->recon[j] * t->recon[m] <= 0) break;
+        }
+    }
+    t->budget_fx = (int64_t)(8 * C - 8 * dq::kStateBytes) << dq::kCostFracBits;
+    // Drift moves a symbol only to its strictly cheaper drift target, so from
+    // level m it ends at most at the end of that chain; a stream made only of
+    // such terminal levels must fit with a byte of rANS slack.
+    int64_t worst = 0;
+    for (int m = 0; ok && m < M; ++m) {
+        int cur = m;
+        while (t->inner[cur] >= 0) cur = t->inner[cur];
+        if (t->cost[cur] > worst) worst = t->cost[cur];
+    }
+    if (ok && (int64_t)dq::kHeadDim * worst + (8ll << dq::kCostFracBits) > t->budget_fx) ok = false;
+    t->feasible = ok ? 1 : 0;
+    return ok ? DQ_OK : DQ_ERR_INFEASIBLE;
+}
+
+void fill_enc_table(const dq_table_info& t, dq::EncTable* e) {
+    memset(e, 0, sizeof(*e));
+    e->levels = t.levels;
+    e->container = t.container;
+    e->prob_bits = t.prob_bits;
+    e->budget_fx = (int32_t)t.budget_fx;
+    for (int m = 0; m < t.levels; ++m) {
+        const uint32_t f = t.freq[m];
+        e->cost[m] = (int32_t)t.cost[m];
+        e->inner[m] = t.inner[m];
+        e->freq[m] = f;
+        e->cum[m] = t.cum[m];
+        e->renorm_lim[m] = f << (24 - t.prob_bits);
+        // floor(x / f) = (x * magic) >> (31 + s) with s = floor(log2 f), magic =
+        // ceil(2^(31+s) / f) < 2^32; exact for x < 2^24 because the error
+        // x * (magic * f - 2^(31+s)) / (f * 2^(31+s)) < 2^(24-31-s) < 1/f.
+        int s = 31 - __builtin_clz(f);
+        unsigned __int128 num = ((unsigned __int128)1) << (31 + s);
+        uint64_t magic = (uint64_t)((num + f - 1) / f);
+        e->div_magic[m] = (uint32_t)magic;
+        e->div_shift[m] = (uint32_t)(s - 1);
+        e->recon[m] = t.recon[m];
+    }
+    for (int j = 0; j + 1 < t.levels; ++j) e->bounds[j] = t.bounds[j];
+}
+
+void fill_entries(const dq_table_info& t, uint32_t* ent) {
+    const uint32_t total = 1u << t.prob_bits;
+    for (int m = 0; m < t.levels; ++m) {
+        uint16_t h = host_f64_to_f16((double)m - (t.levels - 1) / 2.0);
+        for (uint32_t s = t.cum[m]; s < t.cum[m + 1]; ++s)
+            ent[s] = dq::entry_pack(h >> 8, s - t.cum[m], t.freq[m], (uint32_t)m);
+    }
+    for (uint32_t s = total; s < (uint32_t)dq::kTableSlots; ++s) ent[s] = 0;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+namespace dq {
+
+// Split rule: aim for about 2048 work-groups (8 per CU over 256 CUs) and never
+// split below one work-group tile of 256 tokens.
+int choose_splits(int batch, int num_kv_heads, int max_context) {
+    const long units = (long)batch * num_kv_heads;
+    const int tile = 256;
+    const int max_by_len = (max_context + tile - 1) / tile;
+    long want = (2048 + units - 1) / units;
+    if (want < 1) want = 1;
+    if (want > max_by_len) want = max_by_len;
+    if (want < 1) want = 1;
+    return (int)want;
+}
+
+int split_tokens(int max_context, int splits) {
+    const int tile = 256;
+    int per = (max_context + splits - 1) / splits;
+    per = (per + tile - 1) / tile * tile;
+    return per < tile ? tile : per;
+}
+
+}  // namespace dq
+
+extern "C" {
+
+const char* dq_strerror(int code) {
+    switch (code) {
+        case DQ_OK: return "ok";
+        case DQ_ERR_INVALID_ARG: return "invalid argument";
+        case DQ_ERR_UNSUPPORTED: return "unsupported parameter";
+        case DQ_ERR_INFEASIBLE: return "table parameters admit no fitting stream";
+        case DQ_ERR_WORKSPACE: return "workspace too small";
+        case DQ_ERR_HIP: return "HIP runtime error";
+        default: return "unknown error";
+    }
+}
+
+const char* dq_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+int dq_table_describe(const dq_table_params* params, dq_table_info* out) {
+    return describe(params, out);
+}
+
+int dq_tables_init(dq_tables** out, const dq_table_params* keys, const dq_table_params* values) {
+    if (!out || !keys || !values) return DQ_ERR_INVALID_ARG;
+    *out = nullptr;
+    dq_tables* t = new (std::nothrow) dq_tables();
+    if (!t) return DQ_ERR_INVALID_ARG;
+    int rc = describe(keys, &t->info[0]);
+    if (rc == DQ_OK) rc = describe(values, &t->info[1]);
+    if (rc != DQ_OK) { delete t; return rc; }
+    fill_enc_table(t->info[0], &t->enc[0]);
+    fill_enc_table(t->info[1], &t->enc[1]);
+    uint32_t host[2 * dq::kTableSlots];
+    fill_entries(t->info[0], host);
+    fill_entries(t->info[1], host + dq::kTableSlots);
+    hipError_t e = hipGetDevice(&t->device);
+    if (e != hipSuccess) { delete t; return hip_fail(e); }
+    const size_t ent_bytes = sizeof(uint32_t) * 2 * dq::kTableSlots;
+    const size_t total = ent_bytes + sizeof(dq::EncTable) * 2;
+    void* d = nullptr;
+    e = hipMalloc(&d, total);
+    if (e != hipSuccess) { delete t; return hip_fail(e); }
+    e = hipMemcpy(d, host, ent_bytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy((char*)d + ent_bytes, t->enc, sizeof(dq::EncTable) * 2, hipMemcpyHostToDevice);
+    if (e != hipSuccess) { (void)hipFree(d); delete t; return hip_fail(e); }
+    t->d_entries = (uint32_t*)d;
+    t->d_enc = (dq::EncTable*)((char*)d + ent_bytes);
+    *out = t;
+    return DQ_OK;
+}
+
+int dq_tables_destroy(dq_tables* t) {
+    if (!t) return DQ_OK;
+    hipError_t e = hipSuccess;
+    if (t->d_entries) e = hipFree(t->d_entries);
+    delete t;
+    return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
+int dq_tables_info(const dq_tables* t, int which, dq_table_info* out) {
+    if (!t || !out || (which != DQ_KEYS && which != DQ_VALUES)) return DQ_ERR_INVALID_ARG;
+    *out = t->info[which];
+    return DQ_OK;
+}
+
+int dq_encode_kv(const dq_tables* t, const void* k, const void* v, int dtype, int num_tokens,
+                 int num_kv_heads, int page_size, const int32_t* slot_mapping, uint8_t* k_cache,
+                 uint8_t* v_cache, uint16_t* k_norm, uint16_t* v_norm, uint16_t* drift_stats,
+                 uint32_t* err_word, void* stream) {
+    if (!t || num_tokens < 0 || num_kv_heads <= 0 || page_size <= 0 || page_size % 16)
+        return DQ_ERR_INVALID_ARG;
+    if (dtype != DQ_DTYPE_F32 && dtype != DQ_DTYPE_BF16) return DQ_ERR_INVALID_ARG;
+    if (num_tokens == 0) return DQ_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_norm || !v_norm)
+        return DQ_ERR_INVALID_ARG;
+    if ((long)num_tokens * num_kv_heads * 2 > (long)INT32_MAX / 2) return DQ_ERR_INVALID_ARG;
+    dq::EncArgs a;
+    a.k = k;
+    a.v = v;
+    a.dtype = dtype;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.page_size = page_size;
+    a.slot_mapping = slot_mapping;
+    a.cache[0] = k_cache;
+    a.cache[1] = v_cache;
+    a.norm[0] = k_norm;
+    a.norm[1] = v_norm;
+    a.drift_stats = drift_stats;
+    a.err_word = err_word;
+    a.tables = t->d_enc;
+    hipError_t e = dq::launch_encode(a, (hipStream_t)stream);
+    return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
+size_t dq_workspace_size(int batch, int num_q_heads, int num_kv_heads, int max_context, int num_splits) {
+    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context < 0 || num_splits < 0)
+        return 0;
+    int s = num_splits ? num_splits : dq::choose_splits(batch, num_kv_heads, max_context);
+    return (size_t)batch * num_q_heads * s * dq::kPartStride * sizeof(float);
+}
+
+int dq_decode_attention(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
+                        const uint8_t* v_cache, const uint16_t* k_norm, const uint16_t* v_norm,
+                        const int32_t* block_table, const int32_t* context_lens, int batch,
+                        int num_q_heads, int num_kv_heads, int max_pages_per_seq, int page_size,
+                        int max_context, float softmax_scale, int num_splits, float* out,
+                        void* workspace, size_t workspace_bytes, uint32_t* err_word, void* stream) {
+    if (!t || !q || !k_cache || !v_cache || !k_norm || !v_norm || !block_table || !context_lens ||
+        !out || !workspace)
+        return DQ_ERR_INVALID_ARG;
+    if (q_dtype != DQ_DTYPE_F32 && q_dtype != DQ_DTYPE_BF16) return DQ_ERR_INVALID_ARG;
+    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+        max_pages_per_seq <= 0 || page_size <= 0 || page_size % 16 || max_context < 0 ||
+        num_splits < 0 || (long)max_pages_per_seq * page_size < max_context)
+        return DQ_ERR_INVALID_ARG;
+    if (num_q_heads / num_kv_heads > 4) return DQ_ERR_UNSUPPORTED;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace)) return DQ_ERR_INVALID_ARG;
+    int splits = num_splits ? num_splits : dq::choose_splits(batch, num_kv_heads, max_context);
+    if (workspace_bytes < dq_workspace_size(batch, num_q_heads, num_kv_heads, max_context, splits))
+        return DQ_ERR_WORKSPACE;
+    if ((long)batch * num_kv_heads * splits > (long)INT32_MAX / 4) return DQ_ERR_INVALID_ARG;
+    dq::AttnArgs a;
+    a.q = q;
+    a.q_dtype = q_dtype;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_norm = k_norm;
+    a.v_norm = v_norm;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.max_pages_per_seq = max_pages_per_seq;
+    a.page_size = page_size;
+    a.num_splits = splits;
+    a.split_len = dq::split_tokens(max_context, splits);
+    a.ck = t->info[0].container;
+    a.cv = t->info[1].container;
+    a.pk = t->info[0].prob_bits;
+    a.pv = t->info[1].prob_bits;
+    a.step_k = (float)t->info[0].step;
+    a.step_v = (float)t->info[1].step;
+    a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
+    a.entries = t->d_entries;
+    a.partials = (float*)workspace;
+    a.out = out;
+    a.err_word = err_word;
+    hipError_t e = dq::launch_attention(a, (hipStream_t)stream);
+    return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
+int dq_decode_symbols(const dq_tables* t, int which, const uint8_t* containers, int n_streams,
+                      uint8_t* symbols_out, uint32_t* err_word, void* stream) {
+    if (!t || (which != DQ_KEYS && which != DQ_VALUES) || n_streams < 0) return DQ_ERR_INVALID_ARG;
+    if (n_streams == 0) return DQ_OK;
+    if (!containers || !symbols_out || !aligned16(containers) || !aligned16(symbols_out))
+        return DQ_ERR_INVALID_ARG;
+    const dq_table_info& ti = t->info[which];
+    hipError_t e = dq::launch_decode_symbols(t->d_entries + which * dq::kTableSlots, ti.prob_bits,
+                                             ti.levels, ti.container, containers, n_streams,
+                                             symbols_out, err_word, (hipStream_t)stream);
+    return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
+int dq_selftest_fp64(const double* a, const double* b, int n, double* sqrt_out, double* div_out,
+                     uint16_t* f16_out, void* stream) {
+    if (n < 0) return DQ_ERR_INVALID_ARG;
+    if (n == 0) return DQ_OK;
+    if (!a || !b || !sqrt_out || !div_out || !f16_out) return DQ_ERR_INVALID_ARG;
+    hipError_t e = dq::launch_selftest_fp64(a, b, n, sqrt_out, div_out, f16_out, (hipStream_t)stream);
+    return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Internal declarations shared by the host API and the kernels of libdq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dq.h"
+
+namespace dq {
+
+constexpr int kHeadDim = 128;
+constexpr int kStateLowBits = 16;            // rANS state interval [2^16, 2^24)
+constexpr uint32_t kStateLow = 1u << kStateLowBits;
+constexpr int kStateBytes = 3;               // flush size; sigma = 24 bits
+constexpr int kCostFracBits = 16;            // costs in units of 2^-16 bit
+constexpr int kMaxLevels = 9;
+constexpr int kMaxProbBits = 10;
+constexpr int kTableSlots = 1 << kMaxProbBits;
+
+// Decode-table entry, one per slot s of [0, 2^p):
+//   bits  0.. 7  high byte of the fp16 value of the centred level m - (M-1)/2
+//                (its low byte is zero for M <= 9)
+//   bits  8..17  bias = s - c_m (so that Dec(x) = f_m * (x >> p) + bias)
+//   bits 18..27  f_m
+//   bits 28..31  m
+__host__ __device__ inline uint32_t entry_pack(uint32_t lvl_hi, uint32_t bias, uint32_t f, uint32_t m) {
+    return lvl_hi | (bias << 8) | (f << 18) | (m << 28);
+}
+
+// Per-table constants the encoder needs (passed by value to kernels).
+struct EncTable {
+    int levels, container, prob_bits, pad0;
+    int32_t budget_fx;            // (8C - 24) * 2^16
+    int32_t cost[16];             // fixed-point symbol costs
+    int32_t inner[16];            // adjacent level toward zero or -1
+    uint32_t freq[16];
+    uint32_t cum[16];
+    uint32_t renorm_lim[16];      // 2^(24-p) * f: emit a byte while x >= this
+    uint32_t div_magic[16];       // floor(x / f) = umulhi(x, magic) >> shift, x < 2^24
+    uint32_t div_shift[16];
+    double recon[16];             // level values (unit RMS)
+    double bounds[16];            // decision boundaries
+};
+
+struct EncArgs {
+    const void* k;
+    const void* v;
+    int dtype, num_tokens, num_kv_heads, page_size;
+    const int32_t* slot_mapping;
+    uint8_t* cache[2];
+    uint16_t* norm[2];
+    uint16_t* drift_stats;
+    uint32_t* err_word;
+    const EncTable* tables;       // device copy: [0] keys, [1] values
+};
+
+struct AttnArgs {
+    const void* q;
+    int q_dtype;
+    const uint8_t* k_cache;
+    const uint8_t* v_cache;
+    const uint16_t* k_norm;
+    const uint16_t* v_norm;
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    int batch, num_q_heads, num_kv_heads, group, max_pages_per_seq, page_size;
+    int num_splits, split_len;          // tokens per split (multiple of the work-group tile)
+    int ck, cv;                         // container bytes
+    int pk, pv;                         // prob bits
+    float step_k, step_v;
+    float softmax_scale;
+    const uint32_t* entries;            // [2][kTableSlots] decode tables (K then V)
+    float* partials;                    // [batch][Hq][splits][kPartStride]
+    float* out;
+    uint32_t* err_word;
+};
+
+constexpr int kPartStride = 132;         // m, l, pad, pad, acc[128]
+
+// Launchers (defined next to their kernels).
+hipError_t launch_encode(const EncArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_symbols(const uint32_t* entries, int prob_bits, int levels, int container,
+                                 const uint8_t* containers, int n, uint8_t* out, uint32_t* err,
+                                 hipStream_t s);
+hipError_t launch_selftest_fp64(const double* a, const double* b, int n, double* sq, double* dv,
+                                uint16_t* f16, hipStream_t s);
+
+// Split rule shared by dq_workspace_size and dq_decode_attention.
+int choose_splits(int batch, int num_kv_heads, int max_context);
+int split_tokens(int max_context, int splits);
+
+}  // namespace dq
+
+struct dq_tables {
+    int device;
+    dq_table_info info[2];
+    dq::EncTable enc[2];
+    uint32_t* d_entries;      // [2][kTableSlots] decode tables, then the two EncTables
+    dq::EncTable* d_enc;
+};

@@ -107,3 +107,27 @@ def ragged_lengths(config: int, batch: int, lo: int, hi: int) -> np.ndarray:
 def page_permutation(config: int, n_pages: int) -> np.ndarray:
     """A seeded permutation of physical page ids, int32."""
     return rng_for(config, T_PAGES).permutation(n_pages).astype(np.int32)
+
+
+def device_gaussian(shape, seed: int, *, device="cuda", dtype=None, outlier_channels=None,
+                    outlier_scale: float = 10.0):
+    """N(0,1) float32 rows drawn on the device by torch's seeded generator.
+
+    For workloads too large to draw on the host. ``outlier_channels`` is an
+    int array [n_kv_heads][count] (axis -2 of ``shape`` is the KV head): those
+    channels are multiplied by ``outlier_scale``. With ``dtype`` the result is
+    cast (rounded to nearest even for bfloat16). Tests that check a slice
+    against the CPU oracle copy that slice of this very tensor to the host.
+    """
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32)
+    if outlier_channels is not None:
+        ch = np.asarray(outlier_channels)
+        for g in range(ch.shape[0]):
+            idx = torch.as_tensor(ch[g], device=device, dtype=torch.long)
+            x[..., g, idx] = x[..., g, idx] * float(outlier_scale)
+    if dtype is not None:
+        x = x.to(dtype)
+    return x

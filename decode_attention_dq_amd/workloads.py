@@ -1,0 +1,136 @@
+"""The benchmark workloads, their seeded inputs and their paged caches.
+
+Shapes follow the model layers D-Quant evaluates (section 5.1: Qwen3-8B and
+Llama-3.1-8B, 32 query heads, 8 KV heads, head_dim 128) at the 2.26-bit
+budget (8 key levels, 6 value levels, 37-byte containers) and a 1.96-bit
+budget (32-byte containers). Inputs are seeded synthetic Gaussian rows
+(optionally with x10 outlier channels), standing in for captured KV; caches
+are filled by the library's own encoder (``dq_encode_kv``).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import synth
+
+
+@dataclass
+class Workload:
+    name: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    context: int                 # uniform context, or the upper bound of a ragged batch
+    k_levels: int = 8
+    v_levels: int = 6
+    container: int = 37
+    page_size: int = 256
+    layers: int = 1
+    q_bf16: bool = True
+    kv_bf16: bool = False
+    outliers: int = 0
+    ragged: tuple | None = None  # (lo, hi) inclusive range of context lengths
+    config_id: int = 0
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 1, 256, page_size=16, q_bf16=False, config_id=1),
+    "encode_llama": Workload("encode_llama", 16, 32, 8, 8192, kv_bf16=True, outliers=4, config_id=2),
+    "decode_qwen3_8b": Workload("decode_qwen3_8b", 128, 32, 8, 8192, layers=36, config_id=3),
+    "long_llama_b4": Workload("long_llama_b4", 4, 32, 8, 65536, config_id=4),
+    "long_llama_b1": Workload("long_llama_b1", 1, 32, 8, 131072, config_id=4, extra={"part": 1}),
+    "ragged_1p96": Workload("ragged_1p96", 64, 32, 8, 16384, container=32, page_size=16,
+                            ragged=(1024, 16384), config_id=5),
+}
+
+
+def context_lengths(w: Workload) -> np.ndarray:
+    if w.ragged is None:
+        return np.full(w.batch, w.context, dtype=np.int32)
+    return synth.ragged_lengths(w.config_id, w.batch, *w.ragged)
+
+
+def page_plan(w: Workload, lens: np.ndarray):
+    """Physical pages per sequence: a seeded permutation for ragged batches,
+    in order otherwise. Returns (block_table [B][max_pages] int32, num_pages)."""
+    P = w.page_size
+    npages = [-(-int(t) // P) for t in lens]
+    total = int(sum(npages))
+    perm = synth.page_permutation(w.config_id, total) if w.ragged is not None else np.arange(total, dtype=np.int32)
+    maxp = max(1, -(-w.context // P))
+    bt = np.zeros((w.batch, maxp), dtype=np.int32)
+    nxt = 0
+    for b, n in enumerate(npages):
+        bt[b, :n] = perm[nxt:nxt + n]
+        nxt += n
+    return bt, total
+
+
+def slot_mapping(block_table: np.ndarray, lens: np.ndarray, page_size: int) -> np.ndarray:
+    """Physical slot of every token of every sequence, sequences concatenated."""
+    out = []
+    for b, T in enumerate(lens):
+        t = np.arange(int(T))
+        out.append(block_table[b, t // page_size] * page_size + (t % page_size))
+    return np.concatenate(out).astype(np.int32)
+
+
+def kv_rows(w: Workload, layer: int, tensor: int, b: int, T: int, device="cuda"):
+    """K (tensor = synth.T_K) or V rows of sequence b: [T][Hkv][128] on the device."""
+    import torch
+    seed = int(np.random.SeedSequence([0, w.config_id, tensor, layer, b]).generate_state(1)[0])
+    ch = None
+    if w.outliers:
+        ch = synth.outlier_channels(w.config_id, synth.T_OUTLIER_K if tensor == synth.T_K else synth.T_OUTLIER_V,
+                                    w.num_kv_heads, w.outliers)
+    return synth.device_gaussian((T, w.num_kv_heads, 128), seed, device=device,
+                                 dtype=torch.bfloat16 if w.kv_bf16 else torch.float32,
+                                 outlier_channels=ch)
+
+
+def query_rows(w: Workload, layer: int = 0, device="cuda"):
+    import torch
+    seed = int(np.random.SeedSequence([0, w.config_id, synth.T_Q, layer]).generate_state(1)[0])
+    return synth.device_gaussian((w.batch, w.num_q_heads, 128), seed, device=device,
+                                 dtype=torch.bfloat16 if w.q_bf16 else torch.float32)
+
+
+@dataclass
+class Cache:
+    k_cache: object
+    v_cache: object
+    k_norm: object
+    v_norm: object
+    block_table: object
+    context_lens: object
+    lens: np.ndarray
+    drift_stats: object | None = None
+
+
+def build_cache(dq, tables, w: Workload, layer: int = 0, keep_stats: bool = False, device="cuda") -> Cache:
+    """Encode every sequence of one layer into a fresh paged cache."""
+    import torch
+    lens = context_lengths(w)
+    bt, total = page_plan(w, lens)
+    P, H, C = w.page_size, w.num_kv_heads, w.container
+    kc = torch.zeros((total, H, P, C), dtype=torch.uint8, device=device)
+    vc = torch.zeros((total, H, P, C), dtype=torch.uint8, device=device)
+    kn = torch.zeros((total, H, P), dtype=torch.int16, device=device)
+    vn = torch.zeros((total, H, P), dtype=torch.int16, device=device)
+    stats = []
+    for b in range(w.batch):
+        T = int(lens[b])
+        slots = torch.as_tensor(slot_mapping(bt[b:b + 1], lens[b:b + 1], P), device=device)
+        k = kv_rows(w, layer, synth.T_K, b, T, device)
+        v = kv_rows(w, layer, synth.T_V, b, T, device)
+        st = torch.zeros((T, H, 2), dtype=torch.int16, device=device) if keep_stats else None
+        dq.dq_encode_kv(tables, k, v, slots, kc, vc, kn, vn, P, drift_stats=st)
+        if keep_stats:
+            stats.append(st)
+        del k, v
+    return Cache(kc, vc, kn, vn, torch.as_tensor(bt, device=device),
+                 torch.as_tensor(lens, device=device), lens,
+                 torch.cat(stats) if keep_stats else None)

@@ -1,0 +1,225 @@
+/*
+ * dq.h - C ABI of the D-Quant KV-cache codec and fused decode attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: "D-Quant: Driftable Entropy Coding for KV Cache Quantization"
+ * (Su, Liu, Yu, Zhu; arXiv 2609.19880). The paper compresses the key (or
+ * value) vector of one token into a fixed-size container (section 4.1), so
+ * that attention kernels can address compressed tokens at a fixed stride and
+ * dequantize them in parallel (abstract; section 4.1). The cache write is:
+ * Hadamard rotation and normalisation (section 3.2, section 4.1), quantisation
+ * on an affine grid (section 4.2, grid equation), rANS coding with a static
+ * table derived from the standard normal and sharpened by p' ~ p^alpha
+ * (section 3.1 Enc/Dec equations; section 4.4 "Distribution sharpening"), and
+ * drift: the length-constrained assignment of section 4.3 that moves a few
+ * expensive symbols to an adjacent cheaper level until sum r(m_i) <= 8C - sigma
+ * (section 4.2 container equation). Decoding feeds the decoded levels straight
+ * into the attention contraction with the affine map folded in (section 4.5
+ * "Decoding").
+ *
+ * Stream format (fixed here; the paper leaves it open):
+ *   - one stream = the 128 channels of one (token, KV head) of K or of V;
+ *   - per-stream scale: rho = sqrt(sum_i y_i^2 / 128) for the rotated row
+ *     y = H x (rho equals the L2 norm of x), stored as fp16 rounded once to
+ *     nearest even from fp64; y / rho (exact rho, fp64) has unit RMS;
+ *   - levels: a symmetric uniform grid, level m at step*(m - (M-1)/2) in
+ *     unit-RMS units; the reconstruction of channel i of the rotated row is
+ *     rho16 * step * (m_i - (M-1)/2), and the original row is H r / 128 with
+ *     H the 128-point Sylvester Hadamard matrix (entries +-1, H H = 128 I);
+ *   - rANS: probability precision 2^p, state interval [2^16, 2^24), byte-wise
+ *     renormalisation (at most one byte per symbol because every frequency is
+ *     at least 2^(p-8)), the final state flushed as 3 little-endian bytes at
+ *     offset 0, then the renormalisation bytes in the order the decoder reads
+ *     them, then zero padding up to C bytes. sigma = 24 bits. The decoder emits
+ *     channel 0 first; after 128 symbols its state is again 2^16.
+ *
+ * Conventions for every call:
+ *   - all array pointers are device memory owned by the caller unless stated;
+ *     the library allocates device memory only in dq_tables_init (freed by
+ *     dq_tables_destroy);
+ *   - calls are asynchronous on the HIP stream passed as `stream` (a
+ *     hipStream_t; NULL means the default stream) and never synchronise;
+ *   - return value 0 (DQ_OK) or one of the DQ_ERR_* codes below; no C++
+ *     exception crosses this interface; dq_strerror() names a code and
+ *     dq_last_hip_error() gives the text of the last HIP failure seen by the
+ *     calling thread;
+ *   - data-dependent device failures (a corrupt container) are not fatal: they
+ *     set bits in *err_word when err_word is not NULL, and the affected
+ *     outputs are then undefined.
+ */
+#ifndef DQ_H
+#define DQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DQ_HEAD_DIM 128
+
+enum {
+    DQ_OK = 0,
+    DQ_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, bad size or shape */
+    DQ_ERR_UNSUPPORTED = 2,  /* a parameter outside what the kernels implement */
+    DQ_ERR_INFEASIBLE = 3,   /* table parameters admit no fitting stream */
+    DQ_ERR_WORKSPACE = 4,    /* workspace too small */
+    DQ_ERR_HIP = 5           /* a HIP runtime call failed */
+};
+
+enum { DQ_DTYPE_F32 = 0, DQ_DTYPE_BF16 = 1 };
+enum { DQ_KEYS = 0, DQ_VALUES = 1 };
+
+/* err_word bits set by the device */
+#define DQ_DEVERR_DECODE 1u   /* a decoded stream did not return to state 2^16 or overran C */
+#define DQ_DEVERR_ENCODE 2u   /* a stream could not be made to fit its container */
+
+/*
+ * Parameters of one static entropy table (keys and values each have one).
+ *   levels     M, number of reconstruction levels, 2..9 (the paper uses 8 for
+ *              keys and 6 for values at 2.26 bits, section 1 and section 5.1)
+ *   container  C, bytes per stream, 8..128
+ *   step       grid step in unit-RMS units; 0 selects the default for (M, C):
+ *              (8,37) 0.92, (6,37) 0.90, (8,32) 1.12, (6,32) 1.09 - the
+ *              steps minimising the mean post-drift NMSE of i.i.d. N(0,1)
+ *              streams; other (M, C) need an explicit step
+ *   alpha      sharpening exponent, p'_m ~ p_m^alpha (section 4.4); 0 selects
+ *              1.4 (section 5.1)
+ *   prob_bits  p, 9..10; 0 selects 10
+ */
+typedef struct dq_table_params {
+    int levels;
+    int container;
+    double step;
+    double alpha;
+    int prob_bits;
+} dq_table_params;
+
+/* Host view of one derived table (filled by dq_table_describe). */
+typedef struct dq_table_info {
+    int levels, container, prob_bits, feasible;
+    double step, alpha;
+    double recon[16];     /* level values, unit-RMS units */
+    double bounds[16];    /* decision boundaries b_1..b_{M-1} (index 0..M-2) */
+    double mass[16];      /* N(0,1) mass of each level's nearest-neighbour cell */
+    uint32_t freq[16];    /* integer frequencies f_m, sum 2^p */
+    uint32_t cum[17];     /* c_m = sum_{j<m} f_j */
+    int64_t cost[16];     /* rint((p - log2 f_m) * 2^16): cost in 2^-16 bit units */
+    int32_t inner[16];    /* drift target: nearest level toward zero with a lower cost, -1 if none */
+    int64_t budget_fx;    /* (8C - 24) * 2^16 */
+} dq_table_info;
+
+typedef struct dq_tables dq_tables;   /* opaque */
+
+/*
+ * Derive one table on the host (no device work): N(0,1) cell masses of the
+ * nearest-level cells (section 1, section 3.2: the model comes straight from
+ * the standard normal), sharpening (section 4.4), integer frequencies (round
+ * half even, floor 2^(p-8), mirrored, residual to the central level(s)), costs
+ * and the feasibility check (the all-central stream must fit with one byte of
+ * slack). Returns DQ_ERR_UNSUPPORTED / DQ_ERR_INFEASIBLE as dq_tables_init.
+ */
+int dq_table_describe(const dq_table_params* params, dq_table_info* out);
+
+/*
+ * Build the key and value tables and upload them to the current HIP device
+ * (synchronously; this is set-up, not a hot-path call). *out receives a
+ * handle owned by the caller and released with dq_tables_destroy. The handle
+ * may be used from any stream on the device it was created on.
+ */
+int dq_tables_init(dq_tables** out, const dq_table_params* keys, const dq_table_params* values);
+int dq_tables_destroy(dq_tables* tables);
+
+/* Host copy of a table held by a handle (which = DQ_KEYS or DQ_VALUES). */
+int dq_tables_info(const dq_tables* tables, int which, dq_table_info* out);
+
+/*
+ * Cache write (sections 4.1-4.3, 4.5 "Encoding"): encode K and V rows of
+ * num_tokens new tokens into the paged compressed cache.
+ *   k, v          [num_tokens][num_kv_heads][128], dtype DQ_DTYPE_F32 or
+ *                 DQ_DTYPE_BF16 (bf16 as raw uint16 bits); finite values
+ *   slot_mapping  int32 [num_tokens]: physical slot page * page_size + offset
+ *                 of each token; a negative slot skips the token
+ *   k_cache       uint8 [num_pages][num_kv_heads][page_size][C_K]
+ *   v_cache       uint8 [num_pages][num_kv_heads][page_size][C_V]
+ *   k_norm,v_norm uint16 (fp16 bits) [num_pages][num_kv_heads][page_size]
+ *   drift_stats   optional (may be NULL) uint16 [num_tokens][num_kv_heads][2]
+ *                 (K then V): low byte = symbols changed by drift, high byte =
+ *                 drift rounds taken (0: none needed, 1: one round, >1: the
+ *                 fallback that may move a symbol by more than one level)
+ *   err_word      optional; DQ_DEVERR_ENCODE is set if a stream cannot fit
+ * page_size must be a multiple of 16. The caller guarantees distinct slots.
+ */
+int dq_encode_kv(const dq_tables* tables, const void* k, const void* v, int dtype,
+                 int num_tokens, int num_kv_heads, int page_size, const int32_t* slot_mapping,
+                 uint8_t* k_cache, uint8_t* v_cache, uint16_t* k_norm, uint16_t* v_norm,
+                 uint16_t* drift_stats, uint32_t* err_word, void* stream);
+
+/*
+ * Workspace bytes dq_decode_attention needs for these sizes; num_splits 0
+ * means the split count the library picks itself (the same rule as
+ * dq_decode_attention). Returns 0 for invalid sizes.
+ */
+size_t dq_workspace_size(int batch, int num_q_heads, int num_kv_heads, int max_context,
+                         int num_splits);
+
+/*
+ * Fused decode attention over the compressed cache (section 4.5 "Decoding"):
+ * for sequence b and query head h with KV head g = h / (Hq / Hkv),
+ *     out[b][h] = sum_t softmax_t(scale * q[b][h] . k_hat_t) v_hat_t,
+ * t over the first context_lens[b] tokens, k_hat / v_hat the reconstructed
+ * rows in the original (unrotated) domain. Work runs in the rotated domain:
+ * the query is rotated once, levels enter the contraction directly and the
+ * output is rotated back.
+ *   q             [batch][num_q_heads][128], DQ_DTYPE_F32 or DQ_DTYPE_BF16
+ *   block_table   int32 [batch][max_pages_per_seq]: physical page of each
+ *                 logical page; entries past the context are not read
+ *   context_lens  int32 [batch], 0 <= len <= max_context (0 gives zeros)
+ *   max_context   host-side upper bound of context_lens (sizes the split)
+ *   softmax_scale <= 0 selects 1/sqrt(128)
+ *   num_splits    0 = chosen by the library; otherwise the number of token
+ *                 ranges each (sequence, KV head) is split into, merged by
+ *                 log-sum-exp (flash-decoding)
+ *   out           fp32 [batch][num_q_heads][128]
+ *   workspace     device buffer of at least dq_workspace_size(...) bytes,
+ *                 16-byte aligned
+ * num_q_heads / num_kv_heads must be 1..4 (query heads per KV head),
+ * page_size a multiple of 16, caches 16-byte aligned.
+ */
+int dq_decode_attention(const dq_tables* tables, const void* q, int q_dtype,
+                        const uint8_t* k_cache, const uint8_t* v_cache,
+                        const uint16_t* k_norm, const uint16_t* v_norm,
+                        const int32_t* block_table, const int32_t* context_lens,
+                        int batch, int num_q_heads, int num_kv_heads, int max_pages_per_seq,
+                        int page_size, int max_context, float softmax_scale, int num_splits,
+                        float* out, void* workspace, size_t workspace_bytes,
+                        uint32_t* err_word, void* stream);
+
+/*
+ * Test hook: decode n_streams contiguous containers ([n_streams][C] bytes of
+ * table `which`) into symbol indices uint8 [n_streams][128] with the same
+ * device decode routine the attention kernel uses. Streams that fail the
+ * integrity check (final state != 2^16 or more than C bytes read) set
+ * DQ_DEVERR_DECODE in *err_word.
+ */
+int dq_decode_symbols(const dq_tables* tables, int which, const uint8_t* containers,
+                      int n_streams, uint8_t* symbols_out, uint32_t* err_word, void* stream);
+
+/*
+ * Test hook for the fp64 primitives the encoder's bit-exactness rests on:
+ * for each of n inputs a (finite, >= 0 for the square root),
+ * sqrt_out = correctly rounded sqrt(a), div_out = correctly rounded a / b,
+ * f16_out = a rounded once (nearest even) to fp16 bits.
+ */
+int dq_selftest_fp64(const double* a, const double* b, int n, double* sqrt_out,
+                     double* div_out, uint16_t* f16_out, void* stream);
+
+const char* dq_strerror(int code);
+const char* dq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DQ_H */

@@ -14,6 +14,16 @@ def pytest_configure(config):
 
 
 @pytest.fixture(scope="session")
+def built_library():
+    """Path of libdq.so, building it in place first if it is missing."""
+    path = os.path.join(ROOT, "decode_attention_dq_amd", "libdq.so")
+    if not os.path.exists(path):
+        from decode_attention_dq_amd import build_lib
+        build_lib.build()
+    return path
+
+
+@pytest.fixture(scope="session")
 def gpu_lib():
     """The HIP library through its Python binding, on cuda:0 (gpu tests only)."""
     import torch

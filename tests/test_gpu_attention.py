@@ -1,0 +1,199 @@
+"""Fused decode attention against the oracle's fp64 attention over its own
+reconstructions of the same seeded K/V: max relative error per (sequence,
+query head) row <= 2e-3. Cases: the tiny check, GQA with ragged lengths and
+shuffled 16-token pages, split-count invariance, an empty context, extreme
+value norms, and sampled rows of the full Qwen3-8B-layer and 128K
+long-context workloads in the benchmark's launch configuration."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_dq_amd import synth, workloads
+from dq_cases import TOL, oracle_encode, paged_layout, row_rel_err, rho16_bits, sequence_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, hkv, P, max_ctx, splits=0):
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    B, hq = q.shape[:2]
+    out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, dq.dq_workspace_size(B, hq, hkv, max_ctx, splits)), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_decode_attention(tabs, q, dev(kc), dev(vc), dev(kn.view(np.int16)), dev(vn.view(np.int16)),
+                           dev(bt), dev(np.asarray(lens, dtype=np.int32)), hkv, P, max_ctx, out, ws,
+                           num_splits=splits, err_word=err)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), int(err.item())
+
+
+def _case(tk, tv, lens, hkv, hq, P, q_bf16, seed, perm_seed=None, v_scale=None):
+    """Oracle containers and expected output for a batch of sequences."""
+    conts_k, conts_v, nk, nv, kh, vh = [], [], [], [], [], []
+    for b, T in enumerate(lens):
+        k = synth.gaussian_kv(100 + seed, synth.T_K, max(T, 1), hkv, part=b)[:T]
+        v = synth.gaussian_kv(100 + seed, synth.T_V, max(T, 1), hkv, part=b)[:T]
+        if v_scale is not None:
+            v = (v * v_scale(T)[:, None, None]).astype(np.float32)
+        if T == 0:
+            C = tk.container
+            conts_k.append(np.zeros((0, hkv, C), np.uint8)); conts_v.append(np.zeros((0, hkv, tv.container), np.uint8))
+            nk.append(np.zeros((0, hkv), np.uint16)); nv.append(np.zeros((0, hkv), np.uint16))
+            kh.append(np.zeros((hkv, 0, 128))); vh.append(np.zeros((hkv, 0, 128)))
+            continue
+        a, bb, c, d, e, f = sequence_case(tk, tv, k, v)
+        conts_k.append(a); conts_v.append(bb); nk.append(c); nv.append(d); kh.append(e); vh.append(f)
+    kc, kn, bt = paged_layout(conts_k, nk, P, perm_seed)
+    vc, vn, bt2 = paged_layout(conts_v, nv, P, perm_seed)
+    assert np.array_equal(bt, bt2)
+    q = synth.queries(100 + seed, len(lens), hq, bf16=q_bf16)
+    ref = np.zeros((len(lens), hq, 128))
+    for b, T in enumerate(lens):
+        if T:
+            ref[b] = oracle.attention(q[b:b + 1], [kh[b]], [vh[b]])[0]
+    qd = torch.from_numpy(q).cuda()
+    if q_bf16:
+        qd = qd.to(torch.bfloat16)   # exact: q already holds bf16 values
+    return qd, kc, vc, kn, vn, bt, ref
+
+
+def _tables(dq, kC=37, vC=37):
+    return (oracle.make_table(8, kC), oracle.make_table(6, vC),
+            dq.dq_tables_init(dq.make_params(8, kC), dq.make_params(6, vC)))
+
+
+def test_attention_tiny_check(gpu_lib):
+    """1 sequence, 1 KV head, 1 query head, 256 tokens, fp32 rows from seed 0."""
+    dq = gpu_lib
+    tk, tv, tabs = _tables(dq)
+    k, v, q = synth.tiny_check_inputs(0)
+    kc_, vc_, kn_, vn_, kh, vh = sequence_case(tk, tv, k, v)
+    kc, kn, bt = paged_layout([kc_], [kn_], 16)
+    vc, vn, _ = paged_layout([vc_], [vn_], 16)
+    ref = oracle.attention(q, [kh], [vh])
+    out, err = _run(dq, tabs, torch.from_numpy(q).cuda(), kc, vc, kn, vn, bt, [256], 1, 16, 256)
+    assert err == 0
+    e = row_rel_err(out, ref)
+    assert e.max() <= TOL, e
+
+
+@pytest.mark.parametrize("C", [37, 32])
+def test_attention_gqa_ragged_paged(gpu_lib, C):
+    dq = gpu_lib
+    tk, tv, tabs = _tables(dq, C, C)
+    lens = [1, 63, 64, 65, 300, 1000]
+    q, kc, vc, kn, vn, bt, ref = _case(tk, tv, lens, 2, 8, 16, True, seed=C, perm_seed=7)
+    out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, 2, 16, max(lens))
+    assert err == 0
+    e = row_rel_err(out, ref)
+    assert e.max() <= TOL, e
+
+
+@pytest.mark.parametrize("G", [1, 2, 3])
+def test_attention_group_sizes(gpu_lib, G):
+    dq = gpu_lib
+    tk, tv, tabs = _tables(dq)
+    lens = [200, 517]
+    q, kc, vc, kn, vn, bt, ref = _case(tk, tv, lens, 2, 2 * G, 32, False, seed=10 + G)
+    out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, 2, 32, 600)
+    assert err == 0
+    assert row_rel_err(out, ref).max() <= TOL
+
+
+def test_split_invariance(gpu_lib):
+    dq = gpu_lib
+    tk, tv, tabs = _tables(dq)
+    lens = [3000, 1700, 256]
+    q, kc, vc, kn, vn, bt, ref = _case(tk, tv, lens, 1, 4, 64, True, seed=3)
+    outs = []
+    for s in (1, 2, 3, 12):
+        out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, 1, 64, 3000, splits=s)
+        assert err == 0
+        assert row_rel_err(out, ref).max() <= TOL, s
+        outs.append(out)
+    for o in outs[1:]:
+        assert row_rel_err(o, outs[0]).max() <= 1e-4
+
+
+def test_empty_context_gives_zeros(gpu_lib):
+    dq = gpu_lib
+    tk, tv, tabs = _tables(dq)
+    lens = [0, 70, 0]
+    q, kc, vc, kn, vn, bt, ref = _case(tk, tv, lens, 1, 2, 16, True, seed=4)
+    out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, 1, 16, 70)
+    assert err == 0
+    assert np.all(out[0] == 0) and np.all(out[2] == 0)
+    assert row_rel_err(out[1:2], ref[1:2]).max() <= TOL
+
+
+def test_extreme_value_norms(gpu_lib):
+    """Value rows whose norms span 1e-5 .. 1e3 inside one sequence."""
+    dq = gpu_lib
+    tk, tv, tabs = _tables(dq)
+    lens = [700]
+    scale = lambda T: 10.0 ** np.random.default_rng(1).uniform(-5, 3, T)
+    q, kc, vc, kn, vn, bt, ref = _case(tk, tv, lens, 1, 4, 16, True, seed=5, v_scale=scale)
+    out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, 1, 16, 700)
+    assert err == 0
+    assert row_rel_err(out, ref).max() <= TOL
+
+
+def test_corrupt_container_sets_error(gpu_lib):
+    dq = gpu_lib
+    tk, tv, tabs = _tables(dq)
+    lens = [128]
+    q, kc, vc, kn, vn, bt, ref = _case(tk, tv, lens, 1, 1, 16, True, seed=6)
+    kc = kc.copy()
+    kc[bt[0, 2], 0, 5, :3] = 0     # state below 2^16
+    _, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, 1, 16, 128)
+    assert err & dq.DQ_DEVERR_DECODE
+
+
+def _full_size_sampled(dq, w, samples):
+    tk, tv = oracle.make_table(w.k_levels, w.container), oracle.make_table(w.v_levels, w.container)
+    tabs = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.container))
+    cache = workloads.build_cache(dq, tabs, w)
+    q = workloads.query_rows(w)
+    B, hq, hkv = w.batch, w.num_q_heads, w.num_kv_heads
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dq.dq_workspace_size(B, hq, hkv, w.context), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_decode_attention(tabs, q, cache.k_cache, cache.v_cache, cache.k_norm, cache.v_norm, cache.block_table,
+                           cache.context_lens, hkv, w.page_size, w.context, out, ws, err_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    out = out.cpu().numpy()
+    qh = q.float().cpu().numpy()
+    bt = cache.block_table.cpu().numpy()
+    G = hq // hkv
+    for b, g in samples:
+        T = int(cache.lens[b])
+        k = workloads.kv_rows(w, 0, synth.T_K, b, T)[:, g:g + 1].float().cpu().numpy()
+        v = workloads.kv_rows(w, 0, synth.T_V, b, T)[:, g:g + 1].float().cpu().numpy()
+        kc_, vc_, kn_, vn_, kh, vh = sequence_case(tk, tv, k, v)
+        slots = workloads.slot_mapping(bt[b:b + 1], cache.lens[b:b + 1], w.page_size)
+        pg = torch.as_tensor(slots // w.page_size, device="cuda", dtype=torch.long)
+        off = torch.as_tensor(slots % w.page_size, device="cuda", dtype=torch.long)
+        assert np.array_equal(cache.k_cache[pg, g, off].cpu().numpy(), kc_[:, 0])
+        assert np.array_equal(cache.v_cache[pg, g, off].cpu().numpy(), vc_[:, 0])
+        ref = oracle.attention(qh[b:b + 1, g * G:(g + 1) * G], [kh], [vh])[0]
+        e = row_rel_err(out[b, g * G:(g + 1) * G], ref)
+        assert e.max() <= TOL, (b, g, e)
+
+
+def test_full_qwen3_layer_sampled(gpu_lib):
+    dq = gpu_lib
+    _full_size_sampled(dq, workloads.WORKLOADS["decode_qwen3_8b"], [(0, 0), (57, 3), (127, 7)])
+
+
+def test_long_context_128k_sampled(gpu_lib):
+    dq = gpu_lib
+    _full_size_sampled(dq, workloads.WORKLOADS["long_llama_b1"], [(0, 5)])
+
+
+def test_ragged_low_budget_sampled(gpu_lib):
+    dq = gpu_lib
+    w = workloads.WORKLOADS["ragged_1p96"]
+    lens = workloads.context_lengths(w)
+    _full_size_sampled(dq, w, [(int(np.argmin(lens)), 1), (int(np.argmax(lens)), 6), (31, 2)])

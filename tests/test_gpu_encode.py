@@ -1,0 +1,167 @@
+"""The device cache write against the oracle: containers, fp16 norms and
+drift statistics byte-identical, on the tiny check, on bf16 rows with
+outlier channels, on degenerate rows, on paged/skipped slots, on a budget
+that forces fallback rounds, and sampled at the full Llama-layer size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_dq_amd import synth, workloads
+from dq_cases import oracle_encode, rho16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _encode(dq, tabs, k, v, page_size=16, slots=None, num_pages=None, C=(37, 37)):
+    """Encode rows k, v [N][H][128] (torch, on device) and return host arrays
+    (containers [N][H][C] for K and V, norm bits [N][H], stats [N][H][2], err)."""
+    N, H = k.shape[:2]
+    if slots is None:
+        slots = torch.arange(N, dtype=torch.int32, device="cuda")
+    pages = num_pages or (N + page_size - 1) // page_size
+    kc = torch.full((pages, H, page_size, C[0]), 0xAB, dtype=torch.uint8, device="cuda")
+    vc = torch.full((pages, H, page_size, C[1]), 0xAB, dtype=torch.uint8, device="cuda")
+    kn = torch.full((pages, H, page_size), 0x5A5A, dtype=torch.int16, device="cuda")
+    vn = torch.full((pages, H, page_size), 0x5A5A, dtype=torch.int16, device="cuda")
+    st = torch.zeros((N, H, 2), dtype=torch.int16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_encode_kv(tabs, k, v, slots, kc, vc, kn, vn, page_size, drift_stats=st, err_word=err)
+    torch.cuda.synchronize()
+    return kc.cpu().numpy(), vc.cpu().numpy(), kn.cpu().numpy().view(np.uint16), \
+        vn.cpu().numpy().view(np.uint16), st.cpu().numpy().view(np.uint16), int(err.item())
+
+
+def _unpage(cache, slots, page_size):
+    """Per token [N][H][...] from a paged [pages][H][P][...] array."""
+    slots = np.asarray(slots)
+    return cache[slots // page_size, :, slots % page_size]
+
+
+def _check(dq, tabs, tk, tv, k_host, v_host, k_dev, v_dev, C=(37, 37)):
+    N, H = k_host.shape[:2]
+    kc, vc, kn, vn, st, err = _encode(dq, tabs, k_dev, v_dev, C=C)
+    assert err == 0
+    slots = np.arange(N)
+    for which, rows, t, cache, norm in ((0, k_host, tk, kc, kn), (1, v_host, tv, vc, vn)):
+        r = oracle_encode(rows, t)
+        got = _unpage(cache, slots, 16).reshape(N * H, -1)
+        bad = np.flatnonzero((got != r.containers).any(axis=1))
+        assert bad.size == 0, f"{'KV'[which]}: {bad.size} containers differ, first stream {bad[:3]}"
+        assert np.array_equal(_unpage(norm, slots, 16).reshape(-1), rho16_bits(r))
+        s = st[:, :, which].reshape(-1)
+        assert np.array_equal(s & 255, r.changed.astype(np.uint16))
+        assert np.array_equal(s >> 8, np.minimum(r.rounds, 255).astype(np.uint16))
+
+
+def test_encode_tiny_check(gpu_lib):
+    dq = gpu_lib
+    tk, tv = oracle.make_table(8, 37), oracle.make_table(6, 37)
+    tabs = dq.dq_tables_init(dq.make_params(8, 37), dq.make_params(6, 37))
+    k, v, _ = synth.tiny_check_inputs(0)
+    _check(dq, tabs, tk, tv, k, v, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+
+
+@pytest.mark.parametrize("C", [37, 32])
+def test_encode_bf16_outliers(gpu_lib, C):
+    dq = gpu_lib
+    tk, tv = oracle.make_table(8, C), oracle.make_table(6, C)
+    tabs = dq.dq_tables_init(dq.make_params(8, C), dq.make_params(6, C))
+    kb = synth.gaussian_kv(2, synth.T_K, 400, 8, outliers=4, bf16=True)
+    vb = synth.gaussian_kv(2, synth.T_V, 400, 8, outliers=4, bf16=True)
+    kd = torch.from_numpy(synth.f32_to_bf16_bits(kb).view(np.int16)).cuda().view(torch.bfloat16)
+    vd = torch.from_numpy(synth.f32_to_bf16_bits(vb).view(np.int16)).cuda().view(torch.bfloat16)
+    _check(dq, tabs, tk, tv, kb, vb, kd, vd, C=(C, C))
+
+
+def _edge_rows():
+    rows = [np.zeros(128), np.ones(128), -np.ones(128), np.eye(128)[0], np.eye(128)[77] * -3.5,
+            np.tile([1.0, -1.0], 64), np.arange(128) - 63.5, np.full(128, 1e-6), np.full(128, 3e-9),
+            np.eye(128)[5] * 1e30, np.full(128, 7.0e3), np.linspace(-1, 1, 128) ** 9,
+            np.r_[np.zeros(127), 2.0 ** -20]]
+    rng = np.random.default_rng(2)
+    for _ in range(19):
+        x = rng.standard_normal(128) * rng.choice([1e-3, 1.0, 1e3])
+        x[rng.integers(0, 128, 3)] *= 100.0
+        rows.append(x)
+    return np.array(rows, dtype=np.float32)
+
+
+def test_encode_edge_rows(gpu_lib):
+    dq = gpu_lib
+    tk, tv = oracle.make_table(8, 37), oracle.make_table(6, 37)
+    tabs = dq.dq_tables_init(dq.make_params(8, 37), dq.make_params(6, 37))
+    e = _edge_rows()
+    k = np.ascontiguousarray(e.reshape(-1, 1, 128))
+    v = np.ascontiguousarray(e[::-1].reshape(-1, 1, 128))
+    _check(dq, tabs, tk, tv, k, v, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+
+
+def test_encode_fallback_rounds(gpu_lib):
+    """A budget so tight that one drift round is not always enough."""
+    dq = gpu_lib
+    M, C, step = 8, 32, 0.7
+    tk = oracle.make_table(M, C, step)
+    assert tk.feasible
+    tabs = dq.dq_tables_init(dq.make_params(M, C, step), dq.make_params(6, 37))
+    k, v, _ = synth.tiny_check_inputs(4, tokens=600)
+    r = oracle_encode(k, tk)
+    assert (r.rounds > 1).any(), "case no longer exercises the fallback"
+    kc, _, kn, _, st, err = _encode(dq, tabs, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), C=(C, 37))
+    assert err == 0
+    got = _unpage(kc, np.arange(600), 16).reshape(600, -1)
+    assert np.array_equal(got, r.containers)
+    assert np.array_equal(_unpage(kn, np.arange(600), 16).reshape(-1), rho16_bits(r))
+    assert np.array_equal(st[:, 0, 0] >> 8, r.rounds.astype(np.uint16))
+
+
+def test_encode_paged_and_skipped_slots(gpu_lib):
+    dq = gpu_lib
+    tk, tv = oracle.make_table(8, 32), oracle.make_table(6, 32)
+    tabs = dq.dq_tables_init(dq.make_params(8, 32), dq.make_params(6, 32))
+    N, H, P, pages = 100, 2, 32, 8
+    k = synth.gaussian_kv(5, synth.T_K, N, H)
+    v = synth.gaussian_kv(5, synth.T_V, N, H)
+    rng = np.random.default_rng(9)
+    slots = rng.permutation(pages * P)[:N].astype(np.int32)
+    slots[::7] = -1
+    kc, vc, kn, vn, st, err = _encode(dq, tabs, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                                      page_size=P, slots=torch.from_numpy(slots).cuda(), num_pages=pages,
+                                      C=(32, 32))
+    assert err == 0
+    live = slots >= 0
+    for rows, t, cache, norm in ((k, tk, kc, kn), (v, tv, vc, vn)):
+        r = oracle_encode(rows[live], t)
+        got = _unpage(cache, slots[live], P).reshape(-1, 32)
+        assert np.array_equal(got, r.containers)
+        assert np.array_equal(_unpage(norm, slots[live], P).reshape(-1), rho16_bits(r))
+        used = np.zeros(pages * P, bool)
+        used[slots[live]] = True
+        untouched = cache.transpose(0, 2, 1, 3).reshape(pages * P, H, 32)[~used]
+        assert (untouched == 0xAB).all()
+
+
+def test_encode_full_llama_layer_sampled(gpu_lib):
+    """Full cache-write workload (16 x 8192 tokens, 8 KV heads, bf16 with
+    outlier channels) in the benchmark's launch configuration; two sampled
+    sequences are checked stream by stream against the oracle."""
+    dq = gpu_lib
+    w = workloads.WORKLOADS["encode_llama"]
+    tk, tv = oracle.make_table(8, w.container), oracle.make_table(6, w.container)
+    tabs = dq.dq_tables_init(dq.make_params(8, w.container), dq.make_params(6, w.container))
+    cache = workloads.build_cache(dq, tabs, w, keep_stats=True)
+    torch.cuda.synchronize()
+    P = w.page_size
+    bt = cache.block_table.cpu().numpy()
+    for b in (3, 14):
+        T = int(cache.lens[b])
+        slots = workloads.slot_mapping(bt[b:b + 1], cache.lens[b:b + 1], P)
+        for tensor, t, cc, nn in ((synth.T_K, tk, cache.k_cache, cache.k_norm),
+                                  (synth.T_V, tv, cache.v_cache, cache.v_norm)):
+            rows = workloads.kv_rows(w, 0, tensor, b, T).float().cpu().numpy()
+            r = oracle_encode(rows, t)
+            got = _unpage(cc.cpu().numpy(), slots, P).reshape(T * w.num_kv_heads, -1)
+            assert np.array_equal(got, r.containers)
+            assert np.array_equal(_unpage(nn.cpu().numpy().view(np.uint16), slots, P).reshape(-1), rho16_bits(r))
+    st = cache.drift_stats.cpu().numpy().view(np.uint16)
+    assert (st >> 8).max() <= 1, "fallback rounds on the benchmark workload"
