@@ -96,7 +96,7 @@ def test_attention_group_sizes(gpu_lib, G):
     tk, tv, tabs = _tables(dq)
     lens = [200, 517]
     q, kc, vc, kn, vn, bt, ref = _case(tk, tv, lens, 2, 2 * G, 32, False, seed=10 + G)
-    out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, 2, 32, 600)
+    out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, 2, 32, max(lens))
     assert err == 0
     assert row_rel_err(out, ref).max() <= TOL
 
@@ -112,8 +112,10 @@ def test_split_invariance(gpu_lib):
         assert err == 0
         assert row_rel_err(out, ref).max() <= TOL, s
         outs.append(out)
+    # split counts change the running maxima the fp16 p.v weights are scaled by, so results
+    # differ at the level of that rounding (2^-11 relative per weight), far inside TOL
     for o in outs[1:]:
-        assert row_rel_err(o, outs[0]).max() <= 1e-4
+        assert row_rel_err(o, outs[0]).max() <= 5e-4
 
 
 def test_empty_context_gives_zeros(gpu_lib):

@@ -39,15 +39,15 @@ def test_fp64_primitives(gpu_lib):
     dq.dq_selftest_fp64(da, db, sq, dv, f16)
     torch.cuda.synchronize()
     with np.errstate(invalid="ignore", over="ignore"):
-        exp_sq = np.where(a >= 0, np.sqrt(np.abs(a)), 0.0)
+        exp_sq = np.sqrt(np.where(a >= 0, a, 0.0))     # IEEE: sqrt(-0) = -0
         exp_dv = a / b
         exp_f16 = a.astype(np.float16).view(np.uint16)
     got_sq = sq.cpu().numpy()
     got_dv = dv.cpu().numpy()
     got_f16 = f16.cpu().numpy().view(np.uint16)
     assert np.array_equal(got_sq.view(np.uint64), exp_sq.view(np.uint64)), \
-        f"sqrt differs at {np.flatnonzero(got_sq != exp_sq)[:5]}"
+        f"sqrt differs at {np.flatnonzero(got_sq.view(np.uint64) != exp_sq.view(np.uint64))[:5]}"
     assert np.array_equal(got_dv.view(np.uint64), exp_dv.view(np.uint64)), \
-        f"division differs at {np.flatnonzero(got_dv != exp_dv)[:5]}"
+        f"division differs at {np.flatnonzero(got_dv.view(np.uint64) != exp_dv.view(np.uint64))[:5]}"
     bad = np.flatnonzero(got_f16 != exp_f16)
     assert bad.size == 0, f"fp16 rounding differs for {a[bad[:5]]}: {got_f16[bad[:5]]} vs {exp_f16[bad[:5]]}"
