@@ -30,19 +30,20 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;
 constexpr int kRowH = 72;                 // fp16 per LDS row of the level / weight tiles
 constexpr int kRowB = kRowH * 2;          // bytes
-constexpr int kPad = 256;                 // bytes after a container tile (a corrupt stream reads < 132 past its start)
+constexpr int kPad = 144;                 // bytes after a container tile: lane 63 of a corrupt tile reads < 63C + 132
+constexpr int kVtRow = 32;                // bytes per token row of the V level tile (16 fp16 channels)
 constexpr uint32_t kOffTabK = 0;
 constexpr uint32_t kOffTabV = 4096;
 constexpr uint32_t kOffQt = 8192;         // [4][128] fp16 rotated queries
-constexpr uint32_t kOffZero = 9216;       // 512 zero bytes: A operand of rows without a head
-constexpr uint32_t kOffKappa = 9728;      // [4] floats
-constexpr uint32_t kOffWaves = 9792;
+constexpr uint32_t kOffZero = 9216;       // 256 zero bytes: A operand of rows without a head
+constexpr uint32_t kOffKappa = 9472;      // [4] floats
+constexpr uint32_t kOffWaves = 9488;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
 
 __host__ __device__ inline uint32_t wave_bytes(int ck, int cv) {
-    return align16(kTile * ck + kPad) + align16(kTile * cv + kPad) + 16 * kRowB + 4 * kRowB;
+    return align16(kTile * ck + kPad) + align16(kTile * cv + kPad) + kTile * kVtRow + 4 * kRowB;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -108,16 +109,21 @@ __device__ __forceinline__ void stage_tile(uint8_t* lds, uint32_t dst, const uin
     }
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
 struct AttnLaunch {
     AttnArgs a;
     int log2p;
 };
 
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch L) {
+__global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const AttnArgs& a = L.a;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __attribute__((address_space(3))) uint8_t* lds_base = (__attribute__((address_space(3))) uint8_t*)lds;
     const int G = a.group;
     const int T = max(0, min(a.context_lens[b], a.max_pages_per_seq * a.page_size));
     const int start = split * a.split_len;
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch L) {
 
     const uint32_t kcB = align16(kTile * a.ck + kPad), vcB = align16(kTile * a.cv + kPad);
     const uint32_t oW = kOffWaves + (uint32_t)wave * wave_bytes(a.ck, a.cv);
-    const uint32_t oKc = oW, oVc = oW + kcB, oVs = oVc + vcB, oWl = oVs + 16 * kRowB;
+    const uint32_t oKc = oW, oVc = oW + kcB, oVt = oVc + vcB, oWl = oVt + kTile * kVtRow;
 
     // ---- prologue: tables, zero regions, rotated queries
     {
@@ -142,9 +148,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch L) {
         uint32_t* tab = (uint32_t*)lds;
         for (int i = tid; i < 2 * kTableSlots; i += kThreads) tab[i] = ent[i];
         uint32_t* z = (uint32_t*)(lds + kOffZero);
-        if (tid < 128) z[tid] = 0u;
-        uint32_t* vs = (uint32_t*)(lds + oVs);
-        for (int i = lane; i < 16 * kRowB / 4; i += 64) vs[i] = 0u;   // low bytes of the level tile stay 0
+        if (tid < 64) z[tid] = 0u;
     }
     if (wave < G) {
         const int h = g * G + wave;
@@ -172,8 +176,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch L) {
     }
     __syncthreads();
 
-    const uint32_t* tabK = (const uint32_t*)(lds + kOffTabK);
-    const uint32_t* tabV = (const uint32_t*)(lds + kOffTabV);
+    const uint32_t lds0 = (uint32_t)(size_t)lds_base;      // absolute LDS address of the dynamic allocation
+    const uint32_t tabK = lds0 + kOffTabK, tabV = lds0 + kOffTabV;
     const uint32_t maskK = (1u << a.pk) - 1u, maskV = (1u << a.pv) - 1u;
     const uint32_t pk = (uint32_t)a.pk, pv = (uint32_t)a.pv;
     float kap[4];
@@ -184,7 +188,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch L) {
     const int r16 = lane & 15, grp = lane >> 4;
     const uint32_t aq_off = (grp == (r16 >> 2) && (r16 & 3) < G) ? kOffQt + (uint32_t)(r16 & 3) * 256u : kOffZero;
     const uint32_t ap_off = r16 < G ? oWl + (uint32_t)r16 * kRowB + (uint32_t)grp * 16u : kOffZero;
-    const uint32_t bp_off = oVs + (uint32_t)r16 * kRowB + (uint32_t)grp * 16u;
 
     const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages_per_seq;
     const int P = a.page_size, log2p = L.log2p, hkv = a.num_kv_heads;
@@ -198,95 +201,154 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnLaunch L) {
     for (int i = 0; i < 8; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
     uint32_t bad = 0;
 
-    for (int t0 = start + wave * kTile; t0 < end; t0 += kWaves * kTile) {
-        stage_tile(lds, oKc, a.k_cache, a.ck, bt_row, log2p, P, hkv, g, t0, T, lane);
-        stage_tile(lds, oVc, a.v_cache, a.cv, bt_row, log2p, P, hkv, g, t0, T, lane);
-        const int tok = t0 + lane;
-        const bool valid = tok < T;
-        float rk = 0.0f, rv = 0.0f;
-        if (valid) {
-            const int page = bt_row[tok >> log2p];
-            const size_t ni = (size_t)(page * hkv + g) * P + (tok & (P - 1));
-            rk = f16_to_f32(a.k_norm[ni]);
-            rv = f16_to_f32(a.v_norm[ni]);
-        }
-        wave_lds_sync();
+    // V level tile: row = token (this lane), 16 channels of fp16 = 32 bytes
+    const uint32_t vt_row = oVt + (uint32_t)lane * kVtRow;
+    // transpose-load sources for the p.v B operand: lane s of a 16-lane group
+    // points at 4 channels (8 bytes) of token 8*group + s/4 (+4 for the
+    // second load), so that result lane n gets channel n of 4 tokens
+    const uint32_t tr0 = oVt + (uint32_t)(8 * grp + (r16 >> 2)) * kVtRow + 8u * (uint32_t)(r16 & 3);
 
-        // ---- keys: decode 128 channels, 16 MFMAs of 8 channels each
-        float4v d = float4v{0.f, 0.f, 0.f, 0.f};
-        {
-            const uint32_t base = oKc + (uint32_t)lane * (uint32_t)a.ck;
-            uint32_t x = (uint32_t)lds[base] | ((uint32_t)lds[base + 1] << 8) | ((uint32_t)lds[base + 2] << 16);
-            uint32_t ptr = base + kStateBytes;
-            bad |= (valid && x < kStateLow) ? 1u : 0u;
+    // One pass over the 128 channels of a key tile (do_k) and/or a value tile
+    // (do_v): two independent decode chains per lane, the q.k MFMA after each
+    // 8 key channels, the p.v MFMAs after each 16 value channels.
+    auto pass = [&](bool do_k, bool do_v, uint32_t& kx, uint32_t& kp, uint32_t& vx, uint32_t& vp, float4v& dk) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                uint32_t e[8];
+        for (int blk = 0; blk < 8; ++blk) {
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) e[jj] = rans_dec_step(x, ptr, tabK, lds, maskK, pk);
-                u32x4 bw;
-                bw[0] = pack_levels(e[0], e[1]);
-                bw[1] = pack_levels(e[2], e[3]);
-                bw[2] = pack_levels(e[4], e[5]);
-                bw[3] = pack_levels(e[6], e[7]);
-                const half8 aq = *(const half8*)(lds + aq_off + 16u * j);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, __builtin_bit_cast(half8, bw), d, 0, 0, 0);
+            for (int hh = 0; hh < 2; ++hh) {
+                uint32_t ek[8], ev[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    if (do_k) ek[jj] = rans_dec_step(kx, kp, tabK, maskK, pk);
+                    if (do_v) ev[jj] = rans_dec_step(vx, vp, tabV, maskV, pv);
+                }
+                if (do_k) {
+                    u32x4 bw;
+                    bw[0] = pack_levels(ek[0], ek[1]);
+                    bw[1] = pack_levels(ek[2], ek[3]);
+                    bw[2] = pack_levels(ek[4], ek[5]);
+                    bw[3] = pack_levels(ek[6], ek[7]);
+                    // pinned here: hoisting all 16 query loads to the top of the pass costs 64 VGPRs
+                    uint32_t qa = aq_off + 16u * (2 * blk + hh);
+                    asm volatile("" : "+v"(qa));
+                    const half8 aq = *(const half8*)(lds + qa);
+                    dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, __builtin_bit_cast(half8, bw), dk, 0, 0, 0);
+                }
+                if (do_v) {
+                    u32x4 vw;
+                    vw[0] = pack_levels(ev[0], ev[1]);
+                    vw[1] = pack_levels(ev[2], ev[3]);
+                    vw[2] = pack_levels(ev[4], ev[5]);
+                    vw[3] = pack_levels(ev[6], ev[7]);
+                    *(u32x4*)(lds + vt_row + 16u * hh) = vw;
+                }
             }
-            bad |= (valid && (x != kStateLow || ptr - base > (uint32_t)a.ck)) ? 1u : 0u;
+            if (do_v) {
+                wave_lds_sync();
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const half8 av = *(const half8*)(lds + ap_off + 64u * hf);
+                    const uint32_t src = tr0 + (uint32_t)hf * 32u * kVtRow;
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_base + src));
+                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_base + src + 4u * kVtRow));
+                    const half8 bv = __builtin_bit_cast(half8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[blk], 0, 0, 0);
+                }
+                wave_lds_sync();
+            }
         }
+    };
 
-        // ---- online softmax (log2 domain); lane = token, d[r] = raw logit of head r
+    // online softmax (log2 domain) of a decoded key tile; lane = token, d[r] = raw logit of head r.
+    // Value norms enter the p.v weights scaled by a running power of two so fp16 keeps them normal.
+    auto softmax = [&](const float4v& d, bool valid, float rk, float rv) {
         float w[4], alpha[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float s = valid ? d[r] * rk * kap[r] : -INFINITY;
-            const float mn = fmaxf(m_run[r], wave_max(s));
+            const float sv = valid ? d[r] * rk * kap[r] : -INFINITY;
+            const float mn = fmaxf(m_run[r], wave_max(sv));
             alpha[r] = exp2f(m_run[r] - mn);
             m_run[r] = mn;
-            w[r] = exp2f(s - mn);
+            w[r] = exp2f(sv - mn);
             l_lane[r] = l_lane[r] * alpha[r] + w[r];
         }
-        // value norms enter the p.v weights scaled by a running power of two so fp16 keeps them normal
         const int e_tile = wave_max_i(valid && rv > 0.0f ? f32_exponent(rv) : -127);
         const int e_new = max(e_run, e_tile);
         const float sc = __builtin_amdgcn_ldexpf(1.0f, e_run - e_new);
         e_run = e_new;
         const float rvs = __builtin_amdgcn_ldexpf(rv, -e_new);
-        {
-            _Float16* wl = (_Float16*)(lds + oWl);
+        _Float16* wl = (_Float16*)(lds + oWl);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (r < G) wl[r * kRowH + lane] = (_Float16)(valid ? w[r] * rvs : 0.0f);
-        }
+        for (int r = 0; r < 4; ++r)
+            if (r < G) wl[r * kRowH + lane] = (_Float16)(valid ? w[r] * rvs : 0.0f);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[i][r] *= alpha[r] * sc;
+    };
 
-        // ---- values: decode 16 channels into the [channel][token] level tile, then 2 MFMAs
-        {
-            const uint32_t base = oVc + (uint32_t)lane * (uint32_t)a.cv;
-            uint32_t x = (uint32_t)lds[base] | ((uint32_t)lds[base + 1] << 8) | ((uint32_t)lds[base + 2] << 16);
-            uint32_t ptr = base + kStateBytes;
-            bad |= (valid && x < kStateLow) ? 1u : 0u;
-            const uint32_t wbase = oVs + (uint32_t)lane * 2u + 1u;
-#pragma unroll
-            for (int blk = 0; blk < 8; ++blk) {
-#pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    const uint32_t e = rans_dec_step(x, ptr, tabV, lds, maskV, pv);
-                    lds[wbase + (uint32_t)c * kRowB] = (uint8_t)e;
-                }
-                wave_lds_sync();
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const half8 av = *(const half8*)(lds + ap_off + 64u * hf);
-                    const half8 bv = *(const half8*)(lds + bp_off + 64u * hf);
-                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[blk], 0, 0, 0);
-                }
-                wave_lds_sync();
-            }
-            bad |= (valid && (x != kStateLow || ptr - base > (uint32_t)a.cv)) ? 1u : 0u;
+    auto load_norms = [&](int t0, float& rk, float& rv) {
+        const int tok = t0 + lane;
+        rk = 0.0f;
+        rv = 0.0f;
+        if (tok < T) {
+            const int page = bt_row[tok >> log2p];
+            const size_t ni = (size_t)(page * hkv + g) * P + (tok & (P - 1));
+            rk = f16_to_f32(a.k_norm[ni]);
+            rv = f16_to_f32(a.v_norm[ni]);
+        }
+    };
+    auto state_at = [&](uint32_t base) {
+        return (uint32_t)lds[base] | ((uint32_t)lds[base + 1] << 8) | ((uint32_t)lds[base + 2] << 16);
+    };
+
+    const int kStep = kWaves * kTile;
+    const uint32_t kbase = oKc + (uint32_t)lane * (uint32_t)a.ck;
+    const uint32_t vbase = oVc + (uint32_t)lane * (uint32_t)a.cv;
+    const uint32_t kabs = lds0 + kbase, vabs = lds0 + vbase;   // absolute addresses for the decode steps
+    int t = start + wave * kTile;
+    if (t < end) {
+        // prologue: keys of the first tile
+        stage_tile(lds, oKc, a.k_cache, a.ck, bt_row, log2p, P, hkv, g, t, T, lane);
+        stage_tile(lds, oVc, a.v_cache, a.cv, bt_row, log2p, P, hkv, g, t, T, lane);
+        float rk, rv;
+        load_norms(t, rk, rv);
+        wave_lds_sync();
+        const bool valid = t + lane < T;
+        uint32_t kx = state_at(kbase), kp = kabs + kStateBytes, vx = 0, vp = 0;
+        bad |= (valid && kx < kStateLow) ? 1u : 0u;
+        float4v dk = float4v{0.f, 0.f, 0.f, 0.f};
+        pass(true, false, kx, kp, vx, vp, dk);
+        bad |= (valid && (kx != kStateLow || kp - kabs > (uint32_t)a.ck)) ? 1u : 0u;
+        softmax(dk, valid, rk, rv);
+    }
+    for (; t < end; t += kStep) {
+        // values of tile t, interleaved with the keys of tile t + kStep
+        const int tn = t + kStep;
+        const bool has_next = tn < end;
+        const bool valid = t + lane < T, valid_n = tn + lane < T;
+        float rk_n = 0.0f, rv_n = 0.0f;
+        if (has_next) {
+            stage_tile(lds, oKc, a.k_cache, a.ck, bt_row, log2p, P, hkv, g, tn, T, lane);
+            load_norms(tn, rk_n, rv_n);
+        }
+        wave_lds_sync();
+        uint32_t vx = state_at(vbase), vp = vabs + kStateBytes;
+        uint32_t kx = has_next ? state_at(kbase) : 0u, kp = kabs + kStateBytes;
+        bad |= (valid && vx < kStateLow) ? 1u : 0u;
+        float4v dk = float4v{0.f, 0.f, 0.f, 0.f};
+        if (has_next) {
+            bad |= (valid_n && kx < kStateLow) ? 1u : 0u;
+            pass(true, true, kx, kp, vx, vp, dk);
+            bad |= (valid_n && (kx != kStateLow || kp - kabs > (uint32_t)a.ck)) ? 1u : 0u;
+        } else {
+            pass(false, true, kx, kp, vx, vp, dk);
+        }
+        bad |= (valid && (vx != kStateLow || vp - vabs > (uint32_t)a.cv)) ? 1u : 0u;
+        if (has_next) {
+            softmax(dk, valid_n, rk_n, rv_n);
+            wave_lds_sync();
+            stage_tile(lds, oVc, a.v_cache, a.cv, bt_row, log2p, P, hkv, g, tn, T, lane);
         }
     }
     if (bad && a.err_word) atomicOr(a.err_word, DQ_DEVERR_DECODE);
@@ -366,6 +428,7 @@ __global__ __launch_bounds__(kThreads) void decode_symbols_kernel(const uint32_t
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t* tab = (uint32_t*)lds;
     for (int i = tid; i < kTableSlots; i += kThreads) tab[i] = ent[i];
+    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)lds;
     const uint32_t oT = 4096u + (uint32_t)wave * align16(kTile * C + kPad);
     const long s0 = ((long)blockIdx.x * kWaves + wave) * kTile;
     const long s1 = (long)n < s0 + kTile ? (long)n : s0 + kTile;
@@ -379,17 +442,17 @@ __global__ __launch_bounds__(kThreads) void decode_symbols_kernel(const uint32_t
     if (s >= n) return;
     const uint32_t base = oT + (uint32_t)lane * (uint32_t)C;
     uint32_t x = (uint32_t)lds[base] | ((uint32_t)lds[base + 1] << 8) | ((uint32_t)lds[base + 2] << 16);
-    uint32_t ptr = base + kStateBytes;
+    uint32_t ptr = lds0 + base + kStateBytes;
     const bool bad_init = x < kStateLow;
     const uint32_t mask = (1u << p) - 1u;
     uint32_t* o = (uint32_t*)(out + s * kHeadDim);
     for (int i = 0; i < kHeadDim / 4; ++i) {
         uint32_t w = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w |= (rans_dec_step(x, ptr, tab, lds, mask, (uint32_t)p) >> 28) << (8 * k);
+        for (int k = 0; k < 4; ++k) w |= (rans_dec_step(x, ptr, lds0, mask, (uint32_t)p) >> 28) << (8 * k);
         o[i] = w;
     }
-    if ((bad_init || x != kStateLow || ptr - base > (uint32_t)C) && err) atomicOr(err, DQ_DEVERR_DECODE);
+    if ((bad_init || x != kStateLow || ptr - (lds0 + base) > (uint32_t)C) && err) atomicOr(err, DQ_DEVERR_DECODE);
 }
 
 }  // namespace

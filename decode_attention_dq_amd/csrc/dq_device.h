@@ -22,18 +22,30 @@ __device__ __forceinline__ void wave_lds_sync() {
 // the table entry of the symbol m that owns it, the state becomes
 // f_m * floor(x / 2^p) + (slot - c_m), and one byte is shifted in when the
 // state drops below 2^16 (at most one, since f_m >= 2^(p-8)). `ptr` is the
-// LDS byte offset of the next container byte; the byte is always read and
-// used only when needed, so the step has no branch. Returns the entry.
-__device__ __forceinline__ uint32_t rans_dec_step(uint32_t& x, uint32_t& ptr, const uint32_t* tab,
-                                                  const uint8_t* bytes, uint32_t mask, uint32_t p) {
-    const uint32_t e = tab[x & mask];
+// LDS address of the next container byte; the byte is always read and used
+// only when needed, so the step has no branch. Returns the entry.
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+
+// `ptr` and `tab` are absolute LDS byte addresses.
+__device__ __forceinline__ uint32_t rans_dec_step(uint32_t& x, uint32_t& ptr, uint32_t tab, uint32_t mask,
+                                                  uint32_t p) {
+    const uint32_t e = *(lds_u32*)(size_t)(tab + ((x & mask) << 2));
+    const uint32_t b = *(lds_u8*)(size_t)ptr;
     const uint32_t f = (e >> 18) & 1023u;
     const uint32_t bias = (e >> 8) & 1023u;
-    x = f * (x >> p) + bias;
-    const uint32_t b = bytes[ptr];
+    x = __umul24(f, x >> p) + bias;       // f < 2^10, x >> p < 2^14
     const bool need = x < kStateLow;
-    x = need ? ((x << 8) | b) : x;
+    // The shifted-in state is formed unconditionally and passed through an
+    // empty asm so that the select stays a v_cndmask: otherwise the byte load
+    // is sunk into a branch and each step pays two dependent LDS trips.
+    uint32_t t = (x << 8) | b;
+    asm volatile("" : "+v"(t));
+    x = need ? t : x;
     ptr += need ? 1u : 0u;
+    // opaque running pointer: otherwise the compiler rewrites it as base + the
+    // sum of all renormalisation flags and keeps every flag live
+    asm volatile("" : "+v"(ptr));
     return e;
 }
 
