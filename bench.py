@@ -44,11 +44,12 @@ def algorithmic_bytes(w, lens) -> int:
     return int(np.sum(lens)) * w.num_kv_heads * per_stream_pair
 
 
-def cpu_baseline(w, tables_host, samples: int, dq_units):
+def cpu_baseline(w, tables_host, samples: int, dq_units, repeats: int):
     """The oracle, untouched, timed on `samples` (sequence, KV head) units of
     the workload: rANS decode of every K and V container, reconstruction and
-    fp64 attention for the query heads of that KV head. The containers are
-    produced beforehand by the oracle's own encoder (not timed)."""
+    fp64 attention for the query heads of that KV head, each unit `repeats`
+    times. The containers are produced beforehand by the oracle's own encoder
+    (not timed)."""
     import oracle
     from threadpoolctl import threadpool_limits
     from decode_attention_dq_amd import synth, workloads
@@ -63,18 +64,35 @@ def cpu_baseline(w, tables_host, samples: int, dq_units):
             v = workloads.kv_rows(w, 0, synth.T_V, b, T)[:, g].float().cpu().numpy().astype(np.float64)
             rk = oracle.encode_streams(k, tk)
             rv = oracle.encode_streams(v, tv)
-            t0 = time.perf_counter()
-            sk, _ = oracle.decode_streams(rk.containers, tk)
-            sv, _ = oracle.decode_streams(rv.containers, tv)
-            kh = oracle.reconstruct(sk, rk.rho16, tk)
-            vh = oracle.reconstruct(sv, rv.rho16, tv)
-            oracle.attention(q[b:b + 1, g * G:(g + 1) * G], [kh[None]], [vh[None]])
-            timed += time.perf_counter() - t0
-            nbytes += T * (w.container + 2) * 2
+            for _ in range(repeats):
+                t0 = time.perf_counter()
+                sk, _ = oracle.decode_streams(rk.containers, tk)
+                sv, _ = oracle.decode_streams(rv.containers, tv)
+                kh = oracle.reconstruct(sk, rk.rho16, tk)
+                vh = oracle.reconstruct(sv, rv.rho16, tv)
+                oracle.attention(q[b:b + 1, g * G:(g + 1) * G], [kh[None]], [vh[None]])
+                timed += time.perf_counter() - t0
+                nbytes += T * (w.container + 2) * 2
     return {"value": round(nbytes / timed / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{samples} (sequence, KV head) units x {T} tokens of {w.name}: decode K and V "
-                      f"containers, reconstruct, fp64 attention for {G} query heads; "
-                      f"{timed:.1f} s timed on {platform.processor() or platform.machine()}"}
+            "sample": f"{samples} (sequence, KV head) units x {T} tokens of {w.name}, each {repeats}x: decode "
+                      f"K and V containers, reconstruct, fp64 attention for {G} query heads; "
+                      f"{timed:.1f} s timed, 1 thread, {platform.machine()}"}
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel sources changed since those counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in ("dq_attn.hip", "dq_device.h"):
+        h.update(open(os.path.join(ROOT, "decode_attention_dq_amd", "csrc", f), "rb").read())
+    if rec.get("source_sha256") != h.hexdigest() or rec.get("workload") != workload:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def main() -> int:
@@ -85,7 +103,12 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_qwen3_8b")
     ap.add_argument("--splits", type=int, default=0, help="token splits per (sequence, KV head); 0 = library rule")
     ap.add_argument("--cpu-samples", type=int, default=8)
+    ap.add_argument("--cpu-repeats", type=int, default=25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="counter collection only: build and run this many layer caches (marked in the output)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one device-to-device copy of BYTES (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode-attention path has no "
@@ -95,7 +118,20 @@ def main() -> int:
     import torch
     from decode_attention_dq_amd import dq, workloads
 
+    if args.calibrate_copy:
+        n = int(args.calibrate_copy)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return 0
+
     w = workloads.WORKLOADS[args.workload]
+    if args.layers:
+        import dataclasses
+        w = dataclasses.replace(w, layers=int(args.layers))
     torch.cuda.set_device(0)
     tables = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.container))
     t_build = time.perf_counter()
@@ -167,12 +203,14 @@ def main() -> int:
         "config": {"workload": w.name, "batch": B, "context": w.context, "q_heads": hq, "kv_heads": hkv,
                    "head_dim": 128, "layers": w.layers, "container_bytes": w.container,
                    "levels": [w.k_levels, w.v_levels], "page_size": w.page_size, "splits": int(splits),
-                   "q_dtype": "bf16" if w.q_bf16 else "f32"},
+                   "q_dtype": "bf16" if w.q_bf16 else "f32",
+                   **({"layers_override": True} if args.layers else {})},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
         "us_per_layer_call": round(per_call_s * 1e6, 2),
         "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
-                     "unit": "Tops/s", "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": None,
+                     "unit": "Tops/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
+                     "traffic": recorded_traffic("attn_kernel", w.name),
                      "algorithmic_bytes_per_call": nbytes, "symbols_per_call": symbols,
                      "hbm_GBps": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
         "cpu_baseline": None,
@@ -184,7 +222,7 @@ def main() -> int:
         units = [(b, g) for b in range(B) for g in range(hkv)]
         rng = np.random.default_rng(0)
         units = [units[i] for i in rng.permutation(len(units))]
-        result["cpu_baseline"] = cpu_baseline(w, (tk, tv), args.cpu_samples, units)
+        result["cpu_baseline"] = cpu_baseline(w, (tk, tv), args.cpu_samples, units, args.cpu_repeats)
     print(json.dumps(result), flush=True)
     return 0
 
