@@ -79,6 +79,50 @@ def cpu_baseline(w, tables_host, samples: int, dq_units, repeats: int):
                       f"{timed:.1f} s timed, 1 thread, {platform.machine()}"}
 
 
+def encode_measurement(dq, torch, workloads, reps: int = 3) -> dict:
+    """Cache write of the Llama-3.1-8B-shaped workload (16 x 8192 tokens, 8 KV
+    heads, bf16 rows with x10 outlier channels, 37-byte containers), inputs
+    resident in HBM, timed with HIP events; drift statistics from the
+    encoder's own per-stream counts."""
+    from decode_attention_dq_amd import synth
+    w = workloads.WORKLOADS["encode_llama"]
+    tables = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.container))
+    lens = workloads.context_lengths(w)
+    bt, total = workloads.page_plan(w, lens)
+    H, P, C = w.num_kv_heads, w.page_size, w.container
+    k = torch.cat([workloads.kv_rows(w, 0, synth.T_K, b, int(lens[b])) for b in range(w.batch)])
+    v = torch.cat([workloads.kv_rows(w, 0, synth.T_V, b, int(lens[b])) for b in range(w.batch)])
+    slots = torch.as_tensor(workloads.slot_mapping(bt, lens, P), device="cuda")
+    kc = torch.zeros((total, H, P, C), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    kn = torch.zeros((total, H, P), dtype=torch.int16, device="cuda")
+    vn = torch.zeros_like(kn)
+    st = torch.zeros((k.shape[0], H, 2), dtype=torch.int16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    dq.dq_encode_kv(tables, k, v, slots, kc, vc, kn, vn, P, drift_stats=st, err_word=err, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dq.dq_encode_kv(tables, k, v, slots, kc, vc, kn, vn, P, drift_stats=st, err_word=err, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps / 1e3
+    s = st.cpu().numpy().view(np.uint16)
+    n_streams = 2 * k.shape[0] * H
+    changed, rounds = s & 255, s >> 8
+    return {"workload": w.name, "streams": n_streams, "ms": round(t * 1e3, 3),
+            "streams_per_s": round(n_streams / t, 1),
+            "input_GBps": round((k.numel() + v.numel()) * k.element_size() / t / 1e9, 2),
+            "output_GBps": round(n_streams * (C + 2) / t / 1e9, 2),
+            "drift_rate_symbols": {"K": round(float(changed[..., 0].sum()) / (k.shape[0] * H * 128), 5),
+                                   "V": round(float(changed[..., 1].sum()) / (k.shape[0] * H * 128), 5)},
+            "drifted_streams": {"K": round(float((changed[..., 0] > 0).mean()), 5),
+                                "V": round(float((changed[..., 1] > 0).mean()), 5)},
+            "fallback_streams": int((rounds > 1).sum()), "device_errors": int(err.item())}
+
+
 def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None when
     the kernel sources changed since those counters were taken."""
@@ -215,6 +259,10 @@ def main() -> int:
                      "hbm_GBps": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
         "cpu_baseline": None,
     }
+    if not args.layers:
+        del caches, qs
+        torch.cuda.empty_cache()
+        result["encode"] = encode_measurement(dq, torch, workloads)
     if not args.no_cpu_baseline:
         import oracle
         tk = oracle.make_table(w.k_levels, w.container)

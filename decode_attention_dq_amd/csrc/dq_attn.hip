@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     // One pass over the 128 channels of a key tile (do_k) and/or a value tile
     // (do_v): two independent decode chains per lane, the q.k MFMA after each
     // 8 key channels, the p.v MFMAs after each 16 value channels.
-    auto pass = [&](bool do_k, bool do_v, uint32_t& kx, uint32_t& kp, uint32_t& vx, uint32_t& vp, float4v& dk) {
+    auto pass = [&](bool do_k, bool do_v, RansLane& kr, RansLane& vr, float4v& dk) {
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
 #pragma unroll
@@ -219,8 +219,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
                 uint32_t ek[8], ev[8];
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
-                    if (do_k) ek[jj] = rans_dec_step(kx, kp, tabK, maskK, pk);
-                    if (do_v) ev[jj] = rans_dec_step(vx, vp, tabV, maskV, pv);
+                    if ((jj & 3) == 0) {
+                        if (do_k) rans_refill(kr);
+                        if (do_v) rans_refill(vr);
+                    }
+                    if (do_k) ek[jj] = rans_dec_step(kr, tabK, maskK, pk);
+                    if (do_v) ev[jj] = rans_dec_step(vr, tabV, maskV, pv);
                 }
                 if (do_k) {
                     u32x4 bw;
@@ -298,9 +302,6 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
             rv = f16_to_f32(a.v_norm[ni]);
         }
     };
-    auto state_at = [&](uint32_t base) {
-        return (uint32_t)lds[base] | ((uint32_t)lds[base + 1] << 8) | ((uint32_t)lds[base + 2] << 16);
-    };
 
     const int kStep = kWaves * kTile;
     const uint32_t kbase = oKc + (uint32_t)lane * (uint32_t)a.ck;
@@ -315,11 +316,13 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         load_norms(t, rk, rv);
         wave_lds_sync();
         const bool valid = t + lane < T;
-        uint32_t kx = state_at(kbase), kp = kabs + kStateBytes, vx = 0, vp = 0;
-        bad |= (valid && kx < kStateLow) ? 1u : 0u;
+        RansLane kr, vr;
+        rans_init(kr, kabs);
+        vr = kr;
+        bad |= (valid && kr.x < kStateLow) ? 1u : 0u;
         float4v dk = float4v{0.f, 0.f, 0.f, 0.f};
-        pass(true, false, kx, kp, vx, vp, dk);
-        bad |= (valid && (kx != kStateLow || kp - kabs > (uint32_t)a.ck)) ? 1u : 0u;
+        pass(true, false, kr, vr, dk);
+        bad |= (valid && (kr.x != kStateLow || rans_consumed(kr, kabs) > (uint32_t)a.ck)) ? 1u : 0u;
         softmax(dk, valid, rk, rv);
     }
     for (; t < end; t += kStep) {
@@ -333,18 +336,20 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
             load_norms(tn, rk_n, rv_n);
         }
         wave_lds_sync();
-        uint32_t vx = state_at(vbase), vp = vabs + kStateBytes;
-        uint32_t kx = has_next ? state_at(kbase) : 0u, kp = kabs + kStateBytes;
-        bad |= (valid && vx < kStateLow) ? 1u : 0u;
+        RansLane vr, kr;
+        rans_init(vr, vabs);
+        kr = vr;
+        bad |= (valid && vr.x < kStateLow) ? 1u : 0u;
         float4v dk = float4v{0.f, 0.f, 0.f, 0.f};
         if (has_next) {
-            bad |= (valid_n && kx < kStateLow) ? 1u : 0u;
-            pass(true, true, kx, kp, vx, vp, dk);
-            bad |= (valid_n && (kx != kStateLow || kp - kabs > (uint32_t)a.ck)) ? 1u : 0u;
+            rans_init(kr, kabs);
+            bad |= (valid_n && kr.x < kStateLow) ? 1u : 0u;
+            pass(true, true, kr, vr, dk);
+            bad |= (valid_n && (kr.x != kStateLow || rans_consumed(kr, kabs) > (uint32_t)a.ck)) ? 1u : 0u;
         } else {
-            pass(false, true, kx, kp, vx, vp, dk);
+            pass(false, true, kr, vr, dk);
         }
-        bad |= (valid && (vx != kStateLow || vp - vabs > (uint32_t)a.cv)) ? 1u : 0u;
+        bad |= (valid && (vr.x != kStateLow || rans_consumed(vr, vabs) > (uint32_t)a.cv)) ? 1u : 0u;
         if (has_next) {
             softmax(dk, valid_n, rk_n, rv_n);
             wave_lds_sync();
@@ -440,19 +445,21 @@ __global__ __launch_bounds__(kThreads) void decode_symbols_kernel(const uint32_t
     __syncthreads();
     const long s = s0 + lane;
     if (s >= n) return;
-    const uint32_t base = oT + (uint32_t)lane * (uint32_t)C;
-    uint32_t x = (uint32_t)lds[base] | ((uint32_t)lds[base + 1] << 8) | ((uint32_t)lds[base + 2] << 16);
-    uint32_t ptr = lds0 + base + kStateBytes;
-    const bool bad_init = x < kStateLow;
+    const uint32_t base = lds0 + oT + (uint32_t)lane * (uint32_t)C;
+    RansLane r;
+    rans_init(r, base);
+    const bool bad_init = r.x < kStateLow;
     const uint32_t mask = (1u << p) - 1u;
     uint32_t* o = (uint32_t*)(out + s * kHeadDim);
     for (int i = 0; i < kHeadDim / 4; ++i) {
+        rans_refill(r);
         uint32_t w = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w |= (rans_dec_step(x, ptr, lds0, mask, (uint32_t)p) >> 28) << (8 * k);
+        for (int k = 0; k < 4; ++k) w |= (rans_dec_step(r, lds0, mask, (uint32_t)p) >> 28) << (8 * k);
         o[i] = w;
     }
-    if ((bad_init || x != kStateLow || ptr - (lds0 + base) > (uint32_t)C) && err) atomicOr(err, DQ_DEVERR_DECODE);
+    if ((bad_init || r.x != kStateLow || rans_consumed(r, base) > (uint32_t)C) && err)
+        atomicOr(err, DQ_DEVERR_DECODE);
 }
 
 }  // namespace

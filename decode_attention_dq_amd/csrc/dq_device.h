@@ -18,34 +18,62 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One rANS decode step (D-Quant section 3.1, Dec): the slot x mod 2^p selects
-// the table entry of the symbol m that owns it, the state becomes
-// f_m * floor(x / 2^p) + (slot - c_m), and one byte is shifted in when the
-// state drops below 2^16 (at most one, since f_m >= 2^(p-8)). `ptr` is the
-// LDS address of the next container byte; the byte is always read and used
-// only when needed, so the step has no branch. Returns the entry.
 typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 
-// `ptr` and `tab` are absolute LDS byte addresses.
-__device__ __forceinline__ uint32_t rans_dec_step(uint32_t& x, uint32_t& ptr, uint32_t tab, uint32_t mask,
-                                                  uint32_t p) {
-    const uint32_t e = *(lds_u32*)(size_t)(tab + ((x & mask) << 2));
-    const uint32_t b = *(lds_u8*)(size_t)ptr;
+// Per-lane rANS decoder state. The container bytes are read through a
+// 4-byte window refilled every 4 steps (at most one byte is consumed per
+// step), so a step needs one LDS access (the table) instead of two.
+struct RansLane {
+    uint32_t x;     // state, in [2^16, 2^24) between steps
+    uint32_t ptr;   // LDS address of the window's first byte
+    uint32_t win;   // the 4 bytes at ptr (first byte in bits 0..7)
+    uint32_t sel;   // v_perm selector kSel0 + bytes consumed from the window
+};
+constexpr uint32_t kSel0 = 0x06050400u;   // result bytes: win[k], x[0], x[1], x[2]
+
+// State from the 3-byte little-endian flush at LDS address `base`.
+__device__ __forceinline__ void rans_init(RansLane& r, uint32_t base) {
+    r.x = (uint32_t)(*(lds_u8*)(size_t)base) | ((uint32_t)(*(lds_u8*)(size_t)(base + 1)) << 8) |
+          ((uint32_t)(*(lds_u8*)(size_t)(base + 2)) << 16);
+    r.ptr = base + kStateBytes;
+    r.win = 0;
+    r.sel = kSel0;
+}
+
+// Advance the window past the bytes consumed since the last refill and load
+// the next 4 bytes (two aligned dwords and a byte-align).
+__device__ __forceinline__ void rans_refill(RansLane& r) {
+    r.ptr += r.sel - kSel0;
+    asm volatile("" : "+v"(r.ptr));
+    const uint32_t a = r.ptr & ~3u;
+    const uint32_t lo = *(lds_u32*)(size_t)a;
+    const uint32_t hi = *(lds_u32*)(size_t)(a + 4);
+    r.win = __builtin_amdgcn_alignbyte(hi, lo, r.ptr);
+    r.sel = kSel0;
+}
+
+// Bytes consumed since rans_init.
+__device__ __forceinline__ uint32_t rans_consumed(const RansLane& r, uint32_t base) {
+    return r.ptr + (r.sel - kSel0) - base;
+}
+
+// One rANS decode step (D-Quant section 3.1, Dec): the slot x mod 2^p selects
+// the table entry of the symbol m that owns it, the state becomes
+// f_m * floor(x / 2^p) + (slot - c_m), and one byte is shifted in when the
+// state drops below 2^16 (at most one, since f_m >= 2^(p-8)). The byte comes
+// from the window; the shift-in is a v_perm whose selector counts the bytes
+// already taken, so the step has no branch. `tab` is the table's absolute
+// LDS address. Returns the entry. At most 4 steps may run between refills.
+__device__ __forceinline__ uint32_t rans_dec_step(RansLane& r, uint32_t tab, uint32_t mask, uint32_t p) {
+    const uint32_t e = *(lds_u32*)(size_t)(tab + ((r.x & mask) << 2));
     const uint32_t f = (e >> 18) & 1023u;
     const uint32_t bias = (e >> 8) & 1023u;
-    x = __umul24(f, x >> p) + bias;       // f < 2^10, x >> p < 2^14
-    const bool need = x < kStateLow;
-    // The shifted-in state is formed unconditionally and passed through an
-    // empty asm so that the select stays a v_cndmask: otherwise the byte load
-    // is sunk into a branch and each step pays two dependent LDS trips.
-    uint32_t t = (x << 8) | b;
-    asm volatile("" : "+v"(t));
-    x = need ? t : x;
-    ptr += need ? 1u : 0u;
-    // opaque running pointer: otherwise the compiler rewrites it as base + the
-    // sum of all renormalisation flags and keeps every flag live
-    asm volatile("" : "+v"(ptr));
+    const uint32_t xn = __umul24(f, r.x >> p) + bias;       // f < 2^10, x >> p < 2^14
+    const uint32_t t = __builtin_amdgcn_perm(xn, r.win, r.sel);
+    const bool need = xn < kStateLow;
+    r.x = need ? t : xn;
+    r.sel += need ? 1u : 0u;
     return e;
 }
 
