@@ -123,6 +123,67 @@ def encode_measurement(dq, torch, workloads, reps: int = 3) -> dict:
             "fallback_streams": int((rounds > 1).sum()), "device_errors": int(err.item())}
 
 
+def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int = 5) -> dict:
+    """One decode-attention call per step on another workload, rotating through
+    `copies` distinct caches (their total above the 256 MB MALL). For a ragged
+    batch the step also re-encodes each sequence's newest token into its slot
+    first (the cache write that precedes attention in a decode step)."""
+    from decode_attention_dq_amd import synth
+    w = workloads.WORKLOADS[name]
+    tables = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.container))
+    caches = [workloads.build_cache(dq, tables, w, layer=l) for l in range(copies)]
+    qs = [workloads.query_rows(w, l) for l in range(copies)]
+    B, hq, hkv, P = w.batch, w.num_q_heads, w.num_kv_heads, w.page_size
+    lens = caches[0].lens
+    append = w.ragged is not None
+    if append:
+        bt = caches[0].block_table.cpu().numpy()
+        last = lens - 1
+        new_slots = torch.as_tensor((bt[np.arange(B), last // P] * P + last % P).astype(np.int32), device="cuda")
+        new_k = [torch.stack([workloads.kv_rows(w, l, synth.T_K, b, int(lens[b]))[-1] for b in range(B)])
+                 for l in range(copies)]
+        new_v = [torch.stack([workloads.kv_rows(w, l, synth.T_V, b, int(lens[b]))[-1] for b in range(B)])
+                 for l in range(copies)]
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dq.dq_workspace_size(B, hq, hkv, w.context), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(l):
+        c = caches[l]
+        if append:
+            a0 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            dq.dq_encode_kv(tables, new_k[l], new_v[l], new_slots, c.k_cache, c.v_cache, c.k_norm, c.v_norm, P,
+                            err_word=err, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dq.dq_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
+                               c.context_lens, hkv, P, w.context, out, ws, err_word=err, stream=stream)
+        e1.record(stream)
+        return (a0 if append else e0, e0, e1)
+
+    for l in range(copies):
+        step(l)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        for l in range(copies):
+            ev.append(step(l))
+    torch.cuda.synchronize()
+    attn = float(np.mean([e0.elapsed_time(e1) for _, e0, e1 in ev])) / 1e3
+    full = float(np.mean([a0.elapsed_time(e1) for a0, _, e1 in ev])) / 1e3
+    nbytes = algorithmic_bytes(w, lens)
+    res = {"batch": B, "context": "ragged %d..%d" % w.ragged if append else w.context,
+           "container_bytes": w.container, "page_size": P, "cache_copies": copies,
+           "us_per_call": round(attn * 1e6, 2), "GBps": round(nbytes / attn / 1e9, 2),
+           "hbm_frac": round(nbytes / attn / 1e9 / HBM_PEAK_GBS, 4), "device_errors": int(err.item())}
+    if append:
+        res["us_per_step_with_append"] = round(full * 1e6, 2)
+        res["appended_streams"] = 2 * B * hkv
+    return res
+
+
 def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None when
     the kernel sources changed since those counters were taken."""
@@ -263,6 +324,11 @@ def main() -> int:
         del caches, qs
         torch.cuda.empty_cache()
         result["encode"] = encode_measurement(dq, torch, workloads)
+        result["other_workloads"] = {
+            "long_llama_b4": config_measurement(dq, torch, workloads, "long_llama_b4", copies=4),
+            "long_llama_b1": config_measurement(dq, torch, workloads, "long_llama_b1", copies=8),
+            "ragged_1p96": config_measurement(dq, torch, workloads, "ragged_1p96", copies=2),
+        }
     if not args.no_cpu_baseline:
         import oracle
         tk = oracle.make_table(w.k_levels, w.container)

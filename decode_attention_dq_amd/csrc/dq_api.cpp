@@ -201,17 +201,19 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 namespace dq {
 
-// Split rule: aim for about 2048 work-groups (8 per CU over 256 CUs) and never
-// split below one work-group tile of 256 tokens.
+// Split rule: token splits of 2048 (8 tiles per wave, and small enough that a
+// ragged batch spreads evenly over the CUs: splits past a sequence's end exit
+// at once); shorter splits, down to one 256-token work-group tile, when that
+// would leave fewer than 1024 work-groups (4 per CU on 256 CUs).
 int choose_splits(int batch, int num_kv_heads, int max_context) {
     const long units = (long)batch * num_kv_heads;
-    const int tile = 256;
+    const int tile = 256, pref = 2048, target = 1024;
     const int max_by_len = (max_context + tile - 1) / tile;
-    long want = (2048 + units - 1) / units;
-    if (want < 1) want = 1;
-    if (want > max_by_len) want = max_by_len;
-    if (want < 1) want = 1;
-    return (int)want;
+    long s = (max_context + pref - 1) / pref;
+    if (units * s < target) s = (target + units - 1) / units;
+    if (s > max_by_len) s = max_by_len;
+    if (s < 1) s = 1;
+    return (int)s;
 }
 
 int split_tokens(int max_context, int splits) {

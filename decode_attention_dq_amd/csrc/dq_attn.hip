@@ -42,8 +42,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
 
+// LDS stride of one token's container: C itself unless C is a multiple of 8,
+// in which case C + 4 keeps the stride an odd number of dwords, so that the
+// lanes' byte-window reads spread over the LDS banks (a stride of 8 dwords
+// would put every fourth lane on the same bank).
+__host__ __device__ inline uint32_t lds_stride(int c) { return (c & 7) ? (uint32_t)c : (uint32_t)c + 4u; }
+
 __host__ __device__ inline uint32_t wave_bytes(int ck, int cv) {
-    return align16(kTile * ck + kPad) + align16(kTile * cv + kPad) + kTile * kVtRow + 4 * kRowB;
+    return align16(kTile * lds_stride(ck) + kPad) + align16(kTile * lds_stride(cv) + kPad) + kTile * kVtRow +
+           4 * kRowB;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -89,12 +96,17 @@ __device__ __forceinline__ int f32_exponent(float v) {   // floor(log2 v) for v 
 }
 
 // Copy the containers of 64 consecutive tokens (4 groups of 16, each group
-// contiguous inside one page) of KV head g into LDS at `dst`, 16 bytes per
-// lane and load. Groups that start at or past T are skipped.
+// contiguous inside one page) of KV head g into LDS at `dst`, token t at
+// dst + t * lds_stride(C), 16 bytes per lane and load. Groups that start at
+// or past T are skipped. With a padded stride (C a multiple of 8) the 16-byte
+// units are scattered as dwords: no dword straddles two containers then.
+template <bool PADDED>
 __device__ __forceinline__ void stage_tile(uint8_t* lds, uint32_t dst, const uint8_t* __restrict__ cache,
-                                           int C, const int32_t* __restrict__ bt_row, int log2p, int P,
-                                           int hkv, int g, int t0, int T, int lane) {
+                                           int C, uint32_t magic, const int32_t* __restrict__ bt_row, int log2p,
+                                           int P, int hkv, int g, int t0, int T, int lane) {
     const int units = 4 * C;
+    const uint32_t S = lds_stride(C);
+    const uint32_t cq = (uint32_t)C >> 2;   // dwords per container when padded; d / cq = (d * magic) >> 16
     for (int u = lane; u < units; u += 64) {
         const int gi = (u >= C) + (u >= 2 * C) + (u >= 3 * C);
         const int off = u - gi * C;
@@ -104,7 +116,17 @@ __device__ __forceinline__ void stage_tile(uint8_t* lds, uint32_t dst, const uin
             const int o = tok & (P - 1);
             const uint8_t* src = cache + ((size_t)(page * hkv + g) * P + o) * C + (size_t)off * 16;
             const u32x4 v = *(const u32x4*)src;
-            *(u32x4*)(lds + dst + (uint32_t)u * 16u) = v;
+            if (!PADDED) {
+                *(u32x4*)(lds + dst + (uint32_t)u * 16u) = v;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t d = (uint32_t)off * 4u + (uint32_t)k;      // dword within the 16-token group
+                    const uint32_t t = (d * magic) >> 16;                     // token within the group
+                    const uint32_t w = d - t * cq;                            // dword within its container
+                    *(uint32_t*)(lds + dst + (uint32_t)(16 * gi + (int)t) * S + 4u * w) = v[k];
+                }
+            }
         }
     }
 }
@@ -116,8 +138,10 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 struct AttnLaunch {
     AttnArgs a;
     int log2p;
+    uint32_t magic_k, magic_v;   // ceil(2^16 / (C/4)) for the padded staging
 };
 
+template <bool PAD_K, bool PAD_V>
 __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const AttnArgs& a = L.a;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -138,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         return;
     }
 
-    const uint32_t kcB = align16(kTile * a.ck + kPad), vcB = align16(kTile * a.cv + kPad);
+    const uint32_t kcB = align16(kTile * lds_stride(a.ck) + kPad), vcB = align16(kTile * lds_stride(a.cv) + kPad);
     const uint32_t oW = kOffWaves + (uint32_t)wave * wave_bytes(a.ck, a.cv);
     const uint32_t oKc = oW, oVc = oW + kcB, oVt = oVc + vcB, oWl = oVt + kTile * kVtRow;
 
@@ -304,24 +328,42 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     };
 
     const int kStep = kWaves * kTile;
-    const uint32_t kbase = oKc + (uint32_t)lane * (uint32_t)a.ck;
-    const uint32_t vbase = oVc + (uint32_t)lane * (uint32_t)a.cv;
+    const uint32_t kbase = oKc + (uint32_t)lane * lds_stride(a.ck);
+    const uint32_t vbase = oVc + (uint32_t)lane * lds_stride(a.cv);
     const uint32_t kabs = lds0 + kbase, vabs = lds0 + vbase;   // absolute addresses for the decode steps
     int t = start + wave * kTile;
     if (t < end) {
         // prologue: keys of the first tile
-        stage_tile(lds, oKc, a.k_cache, a.ck, bt_row, log2p, P, hkv, g, t, T, lane);
-        stage_tile(lds, oVc, a.v_cache, a.cv, bt_row, log2p, P, hkv, g, t, T, lane);
+        stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, bt_row, log2p, P, hkv, g, t, T, lane);
+        stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, bt_row, log2p, P, hkv, g, t, T, lane);
         float rk, rv;
         load_norms(t, rk, rv);
         wave_lds_sync();
         const bool valid = t + lane < T;
-        RansLane kr, vr;
+        RansLane kr;
         rans_init(kr, kabs);
-        vr = kr;
         bad |= (valid && kr.x < kStateLow) ? 1u : 0u;
         float4v dk = float4v{0.f, 0.f, 0.f, 0.f};
-        pass(true, false, kr, vr, dk);
+        // keys only, as a rolled loop: it touches no accumulator array, and keeping
+        // it small keeps the kernel inside the instruction cache
+#pragma unroll 1
+        for (int j = 0; j < 16; ++j) {
+            uint32_t ek[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                if ((jj & 3) == 0) rans_refill(kr);
+                ek[jj] = rans_dec_step(kr, tabK, maskK, pk);
+            }
+            u32x4 bw;
+            bw[0] = pack_levels(ek[0], ek[1]);
+            bw[1] = pack_levels(ek[2], ek[3]);
+            bw[2] = pack_levels(ek[4], ek[5]);
+            bw[3] = pack_levels(ek[6], ek[7]);
+            uint32_t qa = aq_off + 16u * (uint32_t)j;
+            asm volatile("" : "+v"(qa));
+            const half8 aq = *(const half8*)(lds + qa);
+            dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, __builtin_bit_cast(half8, bw), dk, 0, 0, 0);
+        }
         bad |= (valid && (kr.x != kStateLow || rans_consumed(kr, kabs) > (uint32_t)a.ck)) ? 1u : 0u;
         softmax(dk, valid, rk, rv);
     }
@@ -332,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         const bool valid = t + lane < T, valid_n = tn + lane < T;
         float rk_n = 0.0f, rv_n = 0.0f;
         if (has_next) {
-            stage_tile(lds, oKc, a.k_cache, a.ck, bt_row, log2p, P, hkv, g, tn, T, lane);
+            stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, bt_row, log2p, P, hkv, g, tn, T, lane);
             load_norms(tn, rk_n, rv_n);
         }
         wave_lds_sync();
@@ -353,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         if (has_next) {
             softmax(dk, valid_n, rk_n, rv_n);
             wave_lds_sync();
-            stage_tile(lds, oVc, a.v_cache, a.cv, bt_row, log2p, P, hkv, g, tn, T, lane);
+            stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, bt_row, log2p, P, hkv, g, tn, T, lane);
         }
     }
     if (bad && a.err_word) atomicOr(a.err_word, DQ_DEVERR_DECODE);
@@ -399,22 +441,50 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
 
 // Merge the splits of one (sequence, query head) by log-sum-exp and rotate
 // back: out = H (sum_s acc_s 2^(m_s - M)) / (128 * sum_s l_s 2^(m_s - M)).
-__global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ partials, int splits,
-                                                   float* __restrict__ out) {
-    const int bh = blockIdx.x, lane = threadIdx.x;
+// 4 waves share the splits (wave w takes s = w, w + 4, ...), each lane two
+// channels; the loads of different splits are independent, so many are in
+// flight at once.
+constexpr int kMergeWaves = 4;
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __restrict__ partials, int splits,
+                                                                 float* __restrict__ out) {
+    __shared__ float red[kMergeWaves][132];
+    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* p = partials + (size_t)bh * splits * kPartStride;
     float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, p[(size_t)s * kPartStride]);
+    for (int s = tid; s < splits; s += 64 * kMergeWaves) M = fmaxf(M, p[(size_t)s * kPartStride]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (lane == 0) red[wave][0] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, red[w][0]);
+    __syncthreads();
     float L = 0.0f, v0 = 0.0f, v1 = 0.0f;
     if (M != -INFINITY) {
-        for (int s = 0; s < splits; ++s) {
+#pragma unroll 4
+        for (int s = wave; s < splits; s += kMergeWaves) {
             const float* ps = p + (size_t)s * kPartStride;
-            if (ps[0] == -INFINITY) continue;
-            const float f = exp2f(ps[0] - M);
+            const float ms = ps[0];
+            if (ms == -INFINITY) continue;
+            const float f = exp2f(ms - M);
             L += ps[1] * f;
             v0 += ps[4 + lane] * f;
             v1 += ps[4 + 64 + lane] * f;
         }
+    }
+    red[wave][lane] = v0;
+    red[wave][64 + lane] = v1;
+    if (lane == 0) red[wave][128] = L;
+    __syncthreads();
+    if (wave != 0) return;
+    v0 = 0.0f;
+    v1 = 0.0f;
+    L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+        v0 += red[w][lane];
+        v1 += red[w][64 + lane];
+        L += red[w][128];
     }
     const float inv = L > 0.0f ? 1.0f / (L * (float)kHeadDim) : 0.0f;
     v0 *= inv;
@@ -470,19 +540,28 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     L.log2p = 31 - __builtin_clz((unsigned)a.page_size);
     if ((1 << L.log2p) != a.page_size) return hipErrorInvalidValue;
     const size_t lds = kOffWaves + (size_t)kWaves * wave_bytes(a.ck, a.cv);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           160 * 1024);
+    const uint32_t cqk = (uint32_t)a.ck / 4, cqv = (uint32_t)a.cv / 4;
+    L.magic_k = (65536u + cqk - 1u) / cqk;
+    L.magic_v = (65536u + cqv - 1u) / cqv;
+    const bool pk = lds_stride(a.ck) != (uint32_t)a.ck, pv = lds_stride(a.cv) != (uint32_t)a.cv;
+    const void* fn = pk ? (pv ? (const void*)attn_kernel<true, true> : (const void*)attn_kernel<true, false>)
+                        : (pv ? (const void*)attn_kernel<false, true> : (const void*)attn_kernel<false, false>);
+    static bool attr_set[4] = {false, false, false, false};
+    const int which = (pk ? 2 : 0) + (pv ? 1 : 0);
+    if (!attr_set[which]) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set[which] = true;
     }
     dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
-    hipLaunchKernelGGL(attn_kernel, grid, dim3(kThreads), lds, s, L);
+    if (pk && pv) hipLaunchKernelGGL((attn_kernel<true, true>), grid, dim3(kThreads), lds, s, L);
+    else if (pk) hipLaunchKernelGGL((attn_kernel<true, false>), grid, dim3(kThreads), lds, s, L);
+    else if (pv) hipLaunchKernelGGL((attn_kernel<false, true>), grid, dim3(kThreads), lds, s, L);
+    else hipLaunchKernelGGL((attn_kernel<false, false>), grid, dim3(kThreads), lds, s, L);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(merge_kernel, dim3(a.batch * a.num_q_heads), dim3(64), 0, s, a.partials, a.num_splits,
-                       a.out);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.batch * a.num_q_heads), dim3(64 * kMergeWaves), 0, s, a.partials,
+                       a.num_splits, a.out);
     return hipGetLastError();
 }
 

@@ -12,7 +12,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdq.so")
+# DQ_LIBRARY may name another build of the same library (for example a debug build)
+LIB_PATH = os.environ.get("DQ_LIBRARY") or os.path.join(_HERE, "libdq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libdq.so not found at {LIB_PATH}; build it with "

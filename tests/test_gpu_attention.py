@@ -199,3 +199,34 @@ def test_ragged_low_budget_sampled(gpu_lib):
     w = workloads.WORKLOADS["ragged_1p96"]
     lens = workloads.context_lengths(w)
     _full_size_sampled(dq, w, [(int(np.argmin(lens)), 1), (int(np.argmax(lens)), 6), (31, 2)])
+
+
+def test_decode_step_with_append(gpu_lib):
+    """One decode step of a ragged paged batch at the 1.96-bit budget: the device
+    writes each sequence's newest token into its slot (dq_encode_kv), then attends
+    over all tokens including it."""
+    dq = gpu_lib
+    tk, tv, tabs = _tables(dq, 32, 32)
+    lens, hkv, hq, P, seed = [17, 200, 1, 64, 333], 2, 8, 16, 21
+    q, kc, vc, kn, vn, bt, ref = _case(tk, tv, lens, hkv, hq, P, True, seed=seed, perm_seed=3)
+    B = len(lens)
+    last = np.array(lens) - 1
+    slots = (bt[np.arange(B), last // P] * P + last % P).astype(np.int32)
+    new_k = np.stack([synth.gaussian_kv(100 + seed, synth.T_K, T, hkv, part=b)[T - 1] for b, T in enumerate(lens)])
+    new_v = np.stack([synth.gaussian_kv(100 + seed, synth.T_V, T, hkv, part=b)[T - 1] for b, T in enumerate(lens)])
+    kc0, vc0, kn0, vn0 = kc.copy(), vc.copy(), kn.copy(), vn.copy()
+    for arr in (kc0, vc0, kn0, vn0):
+        arr[slots // P, :, slots % P] = 0          # the newest tokens are not in the cache yet
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    dkc, dvc, dkn, dvn = dev(kc0), dev(vc0), dev(kn0.view(np.int16)), dev(vn0.view(np.int16))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_encode_kv(tabs, dev(new_k), dev(new_v), dev(slots), dkc, dvc, dkn, dvn, P, err_word=err)
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dq.dq_workspace_size(B, hq, hkv, max(lens)), dtype=torch.uint8, device="cuda")
+    dq.dq_decode_attention(tabs, q, dkc, dvc, dkn, dvn, dev(bt), dev(np.array(lens, dtype=np.int32)), hkv, P,
+                           max(lens), out, ws, err_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert np.array_equal(dkc.cpu().numpy(), kc) and np.array_equal(dvc.cpu().numpy(), vc)
+    assert np.array_equal(dkn.cpu().numpy().view(np.uint16), kn) and np.array_equal(dvn.cpu().numpy().view(np.uint16), vn)
+    assert row_rel_err(out.cpu().numpy(), ref).max() <= TOL
