@@ -322,15 +322,17 @@ size_t dq_workspace_size(int batch, int num_q_heads, int num_kv_heads, int max_c
     if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context < 0 || num_splits < 0)
         return 0;
     int s = num_splits ? num_splits : dq::choose_splits(batch, num_kv_heads, max_context);
-    return (size_t)batch * num_q_heads * s * dq::kPartStride * sizeof(float);
+    // one partial per split, plus one slot for an optional bf16 window
+    return (size_t)batch * num_q_heads * (s + 1) * dq::kPartStride * sizeof(float);
 }
 
-int dq_decode_attention(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
-                        const uint8_t* v_cache, const uint16_t* k_norm, const uint16_t* v_norm,
-                        const int32_t* block_table, const int32_t* context_lens, int batch,
-                        int num_q_heads, int num_kv_heads, int max_pages_per_seq, int page_size,
-                        int max_context, float softmax_scale, int num_splits, float* out,
-                        void* workspace, size_t workspace_bytes, uint32_t* err_word, void* stream) {
+static int decode_attention_impl(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
+                                 const uint8_t* v_cache, const uint16_t* k_norm, const uint16_t* v_norm,
+                                 const int32_t* block_table, const int32_t* context_lens, int batch,
+                                 int num_q_heads, int num_kv_heads, int max_pages_per_seq, int page_size,
+                                 int max_context, float softmax_scale, int num_splits, const uint16_t* window_k,
+                                 const uint16_t* window_v, const int32_t* window_lens, int window_cap, float* out,
+                                 void* workspace, size_t workspace_bytes, uint32_t* err_word, void* stream) {
     if (!t || !q || !k_cache || !v_cache || !k_norm || !v_norm || !block_table || !context_lens ||
         !out || !workspace)
         return DQ_ERR_INVALID_ARG;
@@ -341,6 +343,12 @@ int dq_decode_attention(const dq_tables* t, const void* q, int q_dtype, const ui
         return DQ_ERR_INVALID_ARG;
     if (num_q_heads / num_kv_heads > 4) return DQ_ERR_UNSUPPORTED;
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace)) return DQ_ERR_INVALID_ARG;
+    const bool win = window_k != nullptr;
+    if (win) {
+        if (!window_v || !window_lens || window_cap <= 0 || !aligned16(window_k) || !aligned16(window_v))
+            return DQ_ERR_INVALID_ARG;
+        if (window_cap > dq::kWindowMax) return DQ_ERR_UNSUPPORTED;
+    }
     int splits = num_splits ? num_splits : dq::choose_splits(batch, num_kv_heads, max_context);
     if (workspace_bytes < dq_workspace_size(batch, num_q_heads, num_kv_heads, max_context, splits))
         return DQ_ERR_WORKSPACE;
@@ -362,6 +370,12 @@ int dq_decode_attention(const dq_tables* t, const void* q, int q_dtype, const ui
     a.page_size = page_size;
     a.num_splits = splits;
     a.split_len = dq::split_tokens(max_context, splits);
+    a.slot_count = splits + 1;
+    a.merge_slots = splits + (win ? 1 : 0);
+    a.win_k = window_k;
+    a.win_v = window_v;
+    a.win_lens = window_lens;
+    a.win_cap = win ? window_cap : 0;
     a.ck = t->info[0].container;
     a.cv = t->info[1].container;
     a.pk = t->info[0].prob_bits;
@@ -375,6 +389,32 @@ int dq_decode_attention(const dq_tables* t, const void* q, int q_dtype, const ui
     a.err_word = err_word;
     hipError_t e = dq::launch_attention(a, (hipStream_t)stream);
     return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
+int dq_decode_attention(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
+                        const uint8_t* v_cache, const uint16_t* k_norm, const uint16_t* v_norm,
+                        const int32_t* block_table, const int32_t* context_lens, int batch,
+                        int num_q_heads, int num_kv_heads, int max_pages_per_seq, int page_size,
+                        int max_context, float softmax_scale, int num_splits, float* out,
+                        void* workspace, size_t workspace_bytes, uint32_t* err_word, void* stream) {
+    return decode_attention_impl(t, q, q_dtype, k_cache, v_cache, k_norm, v_norm, block_table, context_lens,
+                                 batch, num_q_heads, num_kv_heads, max_pages_per_seq, page_size, max_context,
+                                 softmax_scale, num_splits, nullptr, nullptr, nullptr, 0, out, workspace,
+                                 workspace_bytes, err_word, stream);
+}
+
+int dq_decode_attention_window(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
+                               const uint8_t* v_cache, const uint16_t* k_norm, const uint16_t* v_norm,
+                               const int32_t* block_table, const int32_t* context_lens, int batch,
+                               int num_q_heads, int num_kv_heads, int max_pages_per_seq, int page_size,
+                               int max_context, float softmax_scale, int num_splits, const uint16_t* window_k,
+                               const uint16_t* window_v, const int32_t* window_lens, int window_cap, float* out,
+                               void* workspace, size_t workspace_bytes, uint32_t* err_word, void* stream) {
+    if (!window_k) return DQ_ERR_INVALID_ARG;
+    return decode_attention_impl(t, q, q_dtype, k_cache, v_cache, k_norm, v_norm, block_table, context_lens,
+                                 batch, num_q_heads, num_kv_heads, max_pages_per_seq, page_size, max_context,
+                                 softmax_scale, num_splits, window_k, window_v, window_lens, window_cap, out,
+                                 workspace, workspace_bytes, err_word, stream);
 }
 
 int dq_decode_symbols(const dq_tables* t, int which, const uint8_t* containers, int n_streams,

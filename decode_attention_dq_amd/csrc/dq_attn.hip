@@ -152,8 +152,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const int T = max(0, min(a.context_lens[b], a.max_pages_per_seq * a.page_size));
     const int start = split * a.split_len;
     const int end = min(T, start + a.split_len);
-    const size_t head_stride = (size_t)a.num_splits * kPartStride;
-    float* part = a.partials + (((size_t)b * a.num_q_heads + (size_t)g * G) * a.num_splits + split) * kPartStride;
+    const size_t head_stride = (size_t)a.slot_count * kPartStride;
+    float* part = a.partials + (((size_t)b * a.num_q_heads + (size_t)g * G) * a.slot_count + split) * kPartStride;
     if (start >= end) {
         if (tid < G) {
             part[tid * head_stride + 0] = -INFINITY;
@@ -445,11 +445,11 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
 // channels; the loads of different splits are independent, so many are in
 // flight at once.
 constexpr int kMergeWaves = 4;
-__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __restrict__ partials, int splits,
-                                                                 float* __restrict__ out) {
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __restrict__ partials, int slot_count,
+                                                                 int splits, float* __restrict__ out) {
     __shared__ float red[kMergeWaves][132];
     const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float* p = partials + (size_t)bh * splits * kPartStride;
+    const float* p = partials + (size_t)bh * slot_count * kPartStride;
     float M = -INFINITY;
     for (int s = tid; s < splits; s += 64 * kMergeWaves) M = fmaxf(M, p[(size_t)s * kPartStride]);
 #pragma unroll
@@ -492,6 +492,79 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __
     fwht128_f32(v0, v1, lane);
     out[(size_t)bh * kHeadDim + lane] = v0;
     out[(size_t)bh * kHeadDim + 64 + lane] = v1;
+}
+
+// Attention partial of the uncompressed recent-token window (the paper keeps
+// the most recent tokens in BF16, section 5.1). For each query head of KV head
+// g: m = max logit, l = sum_t 2^(s_t - m) and acc = H (sum_t 2^(s_t - m) v_t),
+// in the same log2 logit scale and rotated output domain as the compressed
+// partials, written to slot `slot` so that merge_kernel combines them. Window
+// rows are in the original domain; wave w handles query head g*G + w, lane t
+// the tokens t, t+64, ...; p.v runs with each lane on channels lane, lane+64.
+__global__ __launch_bounds__(kThreads) void window_kernel(AttnArgs a, int slot) {
+    __shared__ float qs[4][kHeadDim];
+    __shared__ float ps[4][kWindowMax];
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = a.group;
+    const int W = max(0, min(a.win_lens[b], a.win_cap));
+    for (int i = tid; i < G * kHeadDim; i += kThreads) {
+        const size_t qo = ((size_t)b * a.num_q_heads + g * G + i / kHeadDim) * kHeadDim + i % kHeadDim;
+        qs[i / kHeadDim][i % kHeadDim] =
+            a.q_dtype == DQ_DTYPE_BF16 ? bf16_to_f32(((const uint16_t*)a.q)[qo]) : ((const float*)a.q)[qo];
+    }
+    __syncthreads();
+    if (wave >= G) return;
+    float* ph = a.partials + (((size_t)b * a.num_q_heads + g * G + wave) * a.slot_count + slot) * kPartStride;
+    if (W == 0) {
+        if (lane == 0) { ph[0] = -INFINITY; ph[1] = 0.0f; }
+        return;
+    }
+    const size_t rows = ((size_t)b * a.num_kv_heads + g) * a.win_cap;
+    const uint16_t* kr = a.win_k + rows * kHeadDim;
+    const uint16_t* vr = a.win_v + rows * kHeadDim;
+    const float sc = a.softmax_scale * kLog2e;
+    float s[kWindowMax / 64];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kWindowMax / 64; ++j) {
+        const int t = lane + 64 * j;
+        s[j] = -INFINITY;
+        if (t < W) {
+            const uint16_t* row = kr + (size_t)t * kHeadDim;
+            float acc = 0.0f;
+            for (int c = 0; c < kHeadDim; c += 8) {
+                const u32x4 w8 = *(const u32x4*)(row + c);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    acc += qs[wave][c + 2 * k] * __uint_as_float(w8[k] << 16);
+                    acc += qs[wave][c + 2 * k + 1] * __uint_as_float(w8[k] & 0xFFFF0000u);
+                }
+            }
+            s[j] = acc * sc;
+        }
+        mx = fmaxf(mx, s[j]);
+    }
+    mx = wave_max(mx);
+    float l = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kWindowMax / 64; ++j) {
+        const int t = lane + 64 * j;
+        const float pj = t < W ? exp2f(s[j] - mx) : 0.0f;
+        ps[wave][t] = pj;
+        l += pj;
+    }
+    l = wave_sum(l);
+    wave_lds_sync();
+    float o0 = 0.0f, o1 = 0.0f;
+    for (int t = 0; t < W; ++t) {
+        const float pt = ps[wave][t];
+        o0 += pt * bf16_to_f32(vr[(size_t)t * kHeadDim + lane]);
+        o1 += pt * bf16_to_f32(vr[(size_t)t * kHeadDim + 64 + lane]);
+    }
+    fwht128_f32(o0, o1, lane);
+    if (lane == 0) { ph[0] = mx; ph[1] = l; }
+    ph[4 + lane] = o0;
+    ph[4 + 64 + lane] = o1;
 }
 
 // Test hook: decode 64 contiguous containers per wave into symbol indices.
@@ -553,6 +626,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set[which] = true;
     }
+    if (a.win_k) {
+        hipLaunchKernelGGL(window_kernel, dim3(a.num_kv_heads, a.batch), dim3(kThreads), 0, s, a, a.num_splits);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
     if (pk && pv) hipLaunchKernelGGL((attn_kernel<true, true>), grid, dim3(kThreads), lds, s, L);
     else if (pk) hipLaunchKernelGGL((attn_kernel<true, false>), grid, dim3(kThreads), lds, s, L);
@@ -561,7 +639,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(merge_kernel, dim3(a.batch * a.num_q_heads), dim3(64 * kMergeWaves), 0, s, a.partials,
-                       a.num_splits, a.out);
+                       a.slot_count, a.merge_slots, a.out);
     return hipGetLastError();
 }
 

@@ -65,17 +65,24 @@ struct AttnArgs {
     const int32_t* context_lens;
     int batch, num_q_heads, num_kv_heads, group, max_pages_per_seq, page_size;
     int num_splits, split_len;          // tokens per split (multiple of the work-group tile)
+    int slot_count;                     // partial slots per (sequence, query head): splits + 1
+    int merge_slots;                    // slots the merge reads: splits, + 1 with a window
+    const uint16_t* win_k;              // optional bf16 window [batch][Hkv][win_cap][128]
+    const uint16_t* win_v;
+    const int32_t* win_lens;            // [batch]
+    int win_cap;
     int ck, cv;                         // container bytes
     int pk, pv;                         // prob bits
     float step_k, step_v;
     float softmax_scale;
     const uint32_t* entries;            // [2][kTableSlots] decode tables (K then V)
-    float* partials;                    // [batch][Hq][splits][kPartStride]
+    float* partials;                    // [batch][Hq][slot_count][kPartStride]
     float* out;
     uint32_t* err_word;
 };
 
 constexpr int kPartStride = 132;         // m, l, pad, pad, acc[128]
+constexpr int kWindowMax = 256;          // largest bf16 window
 
 // Launchers (defined next to their kernels).
 hipError_t launch_encode(const EncArgs& a, hipStream_t s);

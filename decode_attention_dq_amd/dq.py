@@ -72,6 +72,8 @@ _sig = {
     "dq_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "dq_decode_attention": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                  ctypes.c_float, _i, _p, _p, ctypes.c_size_t, _p, _p]),
+    "dq_decode_attention_window": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                        ctypes.c_float, _i, _p, _p, _p, _i, _p, _p, ctypes.c_size_t, _p, _p]),
     "dq_decode_symbols": (_i, [_p, _i, _p, _i, _p, _p, _p]),
     "dq_selftest_fp64": (_i, [_p, _p, _i, _p, _p, _p, _p]),
     "dq_strerror": (ctypes.c_char_p, [_i]),
@@ -226,6 +228,38 @@ def dq_decode_attention(tables: Tables, q, k_cache, v_cache, k_norm, v_norm, blo
                                     int(max_context), float(softmax_scale), int(num_splits), _ptr(out),
                                     _ptr(workspace), nbytes, _ptr(err_word), _stream(stream)),
            "dq_decode_attention")
+
+
+def dq_decode_attention_window(tables: Tables, q, k_cache, v_cache, k_norm, v_norm, block_table, context_lens,
+                               window_k, window_v, window_lens, num_kv_heads: int, page_size: int,
+                               max_context: int, out, workspace, softmax_scale: float = 0.0, num_splits: int = 0,
+                               err_word=None, stream=None) -> None:
+    """As dq_decode_attention, plus a bf16 window of recent tokens:
+    window_k / window_v [B][Hkv][cap][128] bfloat16, window_lens [B] int32."""
+    import torch
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [B][Hq][128]")
+    qd = {torch.float32: DQ_DTYPE_F32, torch.bfloat16: DQ_DTYPE_BF16}.get(q.dtype)
+    if qd is None:
+        raise ValueError("q dtype must be float32 or bfloat16")
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    _need(q, "q")
+    _need(out, "out", torch.float32, (B, hq, HEAD_DIM))
+    _need(block_table, "block_table", torch.int32)
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    _need(window_lens, "window_lens", torch.int32, (B,))
+    for t, nm in ((window_k, "window_k"), (window_v, "window_v")):
+        _need(t, nm, torch.bfloat16)
+        if t.dim() != 4 or t.shape[0] != B or t.shape[1] != num_kv_heads or t.shape[3] != HEAD_DIM:
+            raise ValueError(f"{nm} must be [B][Hkv][cap][128]")
+    cap = int(window_k.shape[2])
+    _need(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.dq_decode_attention_window(
+        tables.handle, _ptr(q), qd, _ptr(k_cache), _ptr(v_cache), _ptr(k_norm), _ptr(v_norm), _ptr(block_table),
+        _ptr(context_lens), B, hq, int(num_kv_heads), int(block_table.shape[1]), int(page_size), int(max_context),
+        float(softmax_scale), int(num_splits), _ptr(window_k), _ptr(window_v), _ptr(window_lens), cap, _ptr(out),
+        _ptr(workspace), nbytes, _ptr(err_word), _stream(stream)), "dq_decode_attention_window")
 
 
 def dq_decode_symbols(tables: Tables, which: int, containers, symbols_out, err_word=None, stream=None) -> None:

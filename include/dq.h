@@ -197,6 +197,31 @@ int dq_decode_attention(const dq_tables* tables, const void* q, int q_dtype,
                         uint32_t* err_word, void* stream);
 
 /*
+ * Decode attention over the compressed cache plus an uncompressed window of
+ * each sequence's most recent tokens (the paper keeps the latest tokens in
+ * BF16 and compresses older ones, section 5.1). The two parts are combined by
+ * log-sum-exp: out[b][h] attends over the context_lens[b] compressed tokens
+ * and the window_lens[b] window tokens together. Arguments as for
+ * dq_decode_attention, plus:
+ *   window_k, window_v  bf16 bits [batch][num_kv_heads][window_cap][128],
+ *                       original (unrotated) domain, 16-byte aligned; rows
+ *                       [0, window_lens[b]) of each sequence are used
+ *   window_lens         int32 [batch], 0 <= len <= window_cap
+ *   window_cap          1..256
+ * The workspace size is the same as for dq_decode_attention.
+ */
+int dq_decode_attention_window(const dq_tables* tables, const void* q, int q_dtype,
+                               const uint8_t* k_cache, const uint8_t* v_cache,
+                               const uint16_t* k_norm, const uint16_t* v_norm,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               int batch, int num_q_heads, int num_kv_heads, int max_pages_per_seq,
+                               int page_size, int max_context, float softmax_scale, int num_splits,
+                               const uint16_t* window_k, const uint16_t* window_v,
+                               const int32_t* window_lens, int window_cap,
+                               float* out, void* workspace, size_t workspace_bytes,
+                               uint32_t* err_word, void* stream);
+
+/*
  * Test hook: decode n_streams contiguous containers ([n_streams][C] bytes of
  * table `which`) into symbol indices uint8 [n_streams][128] with the same
  * device decode routine the attention kernel uses. Streams that fail the

@@ -84,6 +84,9 @@ def test_invalid_arguments_rejected_on_host(dq):
         dq.DQ_ERR_INVALID_ARG
     assert lib.dq_decode_attention(None, fake, 1, fake, fake, fake, fake, fake, fake, 1, 4, 1, 1, 16, 16, 0.0, 0,
                                    fake, fake, 1 << 20, None, None) == dq.DQ_ERR_INVALID_ARG
+    assert lib.dq_decode_attention_window(None, fake, 1, fake, fake, fake, fake, fake, fake, 1, 4, 1, 1, 16, 16, 0.0,
+                                          0, None, None, None, 0, fake, fake, 1 << 20, None, None) == \
+        dq.DQ_ERR_INVALID_ARG
     assert lib.dq_decode_symbols(None, 0, fake, 1, fake, None, None) == dq.DQ_ERR_INVALID_ARG
     assert lib.dq_selftest_fp64(None, None, -1, None, None, None, None) == dq.DQ_ERR_INVALID_ARG
     assert lib.dq_tables_destroy(None) == dq.DQ_OK
@@ -91,7 +94,8 @@ def test_invalid_arguments_rejected_on_host(dq):
 
 def test_workspace_size(dq):
     assert dq.dq_workspace_size(0, 32, 8, 100) == 0
-    assert dq.dq_workspace_size(2, 8, 2, 1000, 3) == 2 * 8 * 3 * 132 * 4
+    # one slot per split plus one for an optional bf16 window
+    assert dq.dq_workspace_size(2, 8, 2, 1000, 3) == 2 * 8 * 4 * 132 * 4
     # the automatic split count never splits below one 256-token tile
-    assert dq.dq_workspace_size(1, 4, 1, 100) == 1 * 4 * 1 * 132 * 4
+    assert dq.dq_workspace_size(1, 4, 1, 100) == 1 * 4 * 2 * 132 * 4
     assert dq.dq_workspace_size(128, 32, 8, 8192) >= 128 * 32 * 132 * 4
