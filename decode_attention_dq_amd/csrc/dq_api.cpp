@@ -56,6 +56,8 @@ double default_step(int levels, int container) {
     if (container == 37 && levels == 6) return 0.90;
     if (container == 32 && levels == 8) return 1.12;
     if (container == 32 && levels == 6) return 1.09;
+    if (container == 41 && levels == 8) return 0.79;
+    if (container == 27 && levels == 6) return 1.34;
     return 0.0;
 }
 

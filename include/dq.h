@@ -81,9 +81,10 @@ enum { DQ_KEYS = 0, DQ_VALUES = 1 };
  *              keys and 6 for values at 2.26 bits, section 1 and section 5.1)
  *   container  C, bytes per stream, 8..128
  *   step       grid step in unit-RMS units; 0 selects the default for (M, C):
- *              (8,37) 0.92, (6,37) 0.90, (8,32) 1.12, (6,32) 1.09 - the
- *              steps minimising the mean post-drift NMSE of i.i.d. N(0,1)
- *              streams; other (M, C) need an explicit step
+ *              (8,37) 0.92, (6,37) 0.90, (8,32) 1.12, (6,32) 1.09,
+ *              (8,41) 0.79, (6,27) 1.34 - the steps minimising the mean
+ *              post-drift NMSE of i.i.d. N(0,1) streams; other (M, C) need
+ *              an explicit step
  *   alpha      sharpening exponent, p'_m ~ p_m^alpha (section 4.4); 0 selects
  *              1.4 (section 5.1)
  *   prob_bits  p, 9..10; 0 selects 10

@@ -48,6 +48,8 @@ DEFAULT_STEP = {
     (6, 37): 0.90,
     (8, 32): 1.12,
     (6, 32): 1.09,
+    (8, 41): 0.79,
+    (6, 27): 1.34,
 }
 
 

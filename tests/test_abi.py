@@ -64,7 +64,7 @@ def test_host_tables_equal_oracle(dq, M, C, p):
 
 
 def test_default_steps_and_unsupported(dq):
-    for (M, C) in [(8, 37), (6, 37), (8, 32), (6, 32)]:
+    for (M, C) in [(8, 37), (6, 37), (8, 32), (6, 32), (8, 41), (6, 27)]:
         assert dq.dq_table_describe(dq.make_params(M, C))["step"] == oracle.default_step(M, C)
     for bad in (dq.make_params(10, 37, 1.0), dq.make_params(1, 37, 1.0), dq.make_params(8, 200, 1.0),
                 dq.make_params(8, 37, 1.0, 0.0, 8), dq.make_params(8, 37, 1.0, 0.0, 11)):
