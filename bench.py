@@ -37,11 +37,15 @@ OPS_PER_SYMBOL = 8                            # lane-ops of one rANS decode step
 METRIC = "decode-attn compressed-KV GB/s (% HBM peak) and tokens/s at B=128, 8K ctx"
 
 
-def algorithmic_bytes(w, lens) -> int:
-    """Compressed bytes one attention call must read: K and V containers plus
-    their fp16 norms for every (token, KV head) of every sequence."""
-    per_stream_pair = (w.container + 2) * 2
-    return int(np.sum(lens)) * w.num_kv_heads * per_stream_pair
+def algorithmic_bytes(w, lens, window_lens=None) -> int:
+    """Bytes one attention call must read: K and V containers plus their fp16
+    norms for every compressed (token, KV head), and 2 x 256 bytes per bf16
+    window token."""
+    per_stream_pair = (w.container + 2) + (w.cv + 2)
+    n = int(np.sum(lens)) * w.num_kv_heads * per_stream_pair
+    if window_lens is not None:
+        n += int(np.sum(window_lens)) * w.num_kv_heads * 2 * 256
+    return n
 
 
 def cpu_baseline(w, tables_host, samples: int, dq_units, repeats: int):
@@ -130,11 +134,12 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
     first (the cache write that precedes attention in a decode step)."""
     from decode_attention_dq_amd import synth
     w = workloads.WORKLOADS[name]
-    tables = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.container))
+    tables = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.cv))
     caches = [workloads.build_cache(dq, tables, w, layer=l) for l in range(copies)]
     qs = [workloads.query_rows(w, l) for l in range(copies)]
     B, hq, hkv, P = w.batch, w.num_q_heads, w.num_kv_heads, w.page_size
     lens = caches[0].lens
+    wl = caches[0].win_lens.cpu().numpy() if w.window else None
     append = w.ragged is not None
     if append:
         bt = caches[0].block_table.cpu().numpy()
@@ -159,8 +164,13 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
                             err_word=err, stream=stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        dq.dq_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
-                               c.context_lens, hkv, P, w.context, out, ws, err_word=err, stream=stream)
+        if w.window:
+            dq.dq_decode_attention_window(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
+                                          c.context_lens, c.win_k, c.win_v, c.win_lens, hkv, P, w.context, out, ws,
+                                          err_word=err, stream=stream)
+        else:
+            dq.dq_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
+                                   c.context_lens, hkv, P, w.context, out, ws, err_word=err, stream=stream)
         e1.record(stream)
         return (a0 if append else e0, e0, e1)
 
@@ -173,9 +183,10 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
     torch.cuda.synchronize()
     attn = float(np.mean([e0.elapsed_time(e1) for _, e0, e1 in ev])) / 1e3
     full = float(np.mean([a0.elapsed_time(e1) for a0, _, e1 in ev])) / 1e3
-    nbytes = algorithmic_bytes(w, lens)
+    nbytes = algorithmic_bytes(w, lens, wl)
     res = {"batch": B, "context": "ragged %d..%d" % w.ragged if append else w.context,
-           "container_bytes": w.container, "page_size": P, "cache_copies": copies,
+           "container_bytes": [w.container, w.cv], "page_size": P, "cache_copies": copies,
+           **({"bf16_window": w.window} if w.window else {}),
            "us_per_call": round(attn * 1e6, 2), "GBps": round(nbytes / attn / 1e9, 2),
            "hbm_frac": round(nbytes / attn / 1e9 / HBM_PEAK_GBS, 4), "device_errors": int(err.item())}
     if append:
@@ -328,6 +339,7 @@ def main() -> int:
             "long_llama_b4": config_measurement(dq, torch, workloads, "long_llama_b4", copies=4),
             "long_llama_b1": config_measurement(dq, torch, workloads, "long_llama_b1", copies=8),
             "ragged_1p96": config_measurement(dq, torch, workloads, "ragged_1p96", copies=2),
+            "window_split_qwen3_8b": config_measurement(dq, torch, workloads, "window_split_qwen3_8b", copies=2),
         }
     if not args.no_cpu_baseline:
         import oracle

@@ -34,6 +34,12 @@ class Workload:
     ragged: tuple | None = None  # (lo, hi) inclusive range of context lengths
     config_id: int = 0
     extra: dict = field(default_factory=dict)
+    container_v: int = 0         # value container bytes (0: same as `container`)
+    window: int = 0              # most recent tokens kept uncompressed in bf16
+
+    @property
+    def cv(self) -> int:
+        return self.container_v or self.container
 
 
 WORKLOADS = {
@@ -44,6 +50,9 @@ WORKLOADS = {
     "long_llama_b1": Workload("long_llama_b1", 1, 32, 8, 131072, config_id=4, extra={"part": 1}),
     "ragged_1p96": Workload("ragged_1p96", 64, 32, 8, 16384, container=32, page_size=16,
                             ragged=(1024, 16384), config_id=5),
+    # the paper's serving layout: last 128 tokens in bf16, keys given more bytes than values
+    "window_split_qwen3_8b": Workload("window_split_qwen3_8b", 128, 32, 8, 8192, container=41, container_v=27,
+                                      window=128, config_id=6),
 }
 
 
@@ -108,29 +117,48 @@ class Cache:
     context_lens: object
     lens: np.ndarray
     drift_stats: object | None = None
+    win_k: object | None = None        # bf16 [B][Hkv][window][128]
+    win_v: object | None = None
+    win_lens: object | None = None
 
 
 def build_cache(dq, tables, w: Workload, layer: int = 0, keep_stats: bool = False, device="cuda") -> Cache:
-    """Encode every sequence of one layer into a fresh paged cache."""
+    """Encode every sequence of one layer into a fresh paged cache. With a
+    window, the last `w.window` tokens of each sequence stay uncompressed (bf16)
+    and only the earlier ones are encoded."""
     import torch
-    lens = context_lengths(w)
+    full = context_lengths(w)
+    lens = np.maximum(full - w.window, 0).astype(np.int32)
     bt, total = page_plan(w, lens)
-    P, H, C = w.page_size, w.num_kv_heads, w.container
-    kc = torch.zeros((total, H, P, C), dtype=torch.uint8, device=device)
-    vc = torch.zeros((total, H, P, C), dtype=torch.uint8, device=device)
+    P, H = w.page_size, w.num_kv_heads
+    kc = torch.zeros((total, H, P, w.container), dtype=torch.uint8, device=device)
+    vc = torch.zeros((total, H, P, w.cv), dtype=torch.uint8, device=device)
     kn = torch.zeros((total, H, P), dtype=torch.int16, device=device)
     vn = torch.zeros((total, H, P), dtype=torch.int16, device=device)
+    if w.window:
+        wk = torch.zeros((w.batch, H, w.window, 128), dtype=torch.bfloat16, device=device)
+        wv = torch.zeros_like(wk)
     stats = []
     for b in range(w.batch):
         T = int(lens[b])
         slots = torch.as_tensor(slot_mapping(bt[b:b + 1], lens[b:b + 1], P), device=device)
-        k = kv_rows(w, layer, synth.T_K, b, T, device)
-        v = kv_rows(w, layer, synth.T_V, b, T, device)
+        k = kv_rows(w, layer, synth.T_K, b, int(full[b]), device)
+        v = kv_rows(w, layer, synth.T_V, b, int(full[b]), device)
+        if w.window:
+            nw = int(full[b]) - T
+            wk[b, :, :nw] = k[T:].transpose(0, 1).to(torch.bfloat16)
+            wv[b, :, :nw] = v[T:].transpose(0, 1).to(torch.bfloat16)
+            k, v = k[:T].contiguous(), v[:T].contiguous()
         st = torch.zeros((T, H, 2), dtype=torch.int16, device=device) if keep_stats else None
-        dq.dq_encode_kv(tables, k, v, slots, kc, vc, kn, vn, P, drift_stats=st)
+        if T:
+            dq.dq_encode_kv(tables, k, v, slots, kc, vc, kn, vn, P, drift_stats=st)
         if keep_stats:
             stats.append(st)
         del k, v
-    return Cache(kc, vc, kn, vn, torch.as_tensor(bt, device=device),
-                 torch.as_tensor(lens, device=device), lens,
-                 torch.cat(stats) if keep_stats else None)
+    c = Cache(kc, vc, kn, vn, torch.as_tensor(bt, device=device),
+              torch.as_tensor(lens, device=device), lens,
+              torch.cat(stats) if keep_stats else None)
+    if w.window:
+        c.win_k, c.win_v = wk, wv
+        c.win_lens = torch.as_tensor((full - lens).astype(np.int32), device=device)
+    return c

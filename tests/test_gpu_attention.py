@@ -153,16 +153,21 @@ def test_corrupt_container_sets_error(gpu_lib):
 
 
 def _full_size_sampled(dq, w, samples):
-    tk, tv = oracle.make_table(w.k_levels, w.container), oracle.make_table(w.v_levels, w.container)
-    tabs = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.container))
+    tk, tv = oracle.make_table(w.k_levels, w.container), oracle.make_table(w.v_levels, w.cv)
+    tabs = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.cv))
     cache = workloads.build_cache(dq, tabs, w)
     q = workloads.query_rows(w)
     B, hq, hkv = w.batch, w.num_q_heads, w.num_kv_heads
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
     ws = torch.empty(dq.dq_workspace_size(B, hq, hkv, w.context), dtype=torch.uint8, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    dq.dq_decode_attention(tabs, q, cache.k_cache, cache.v_cache, cache.k_norm, cache.v_norm, cache.block_table,
-                           cache.context_lens, hkv, w.page_size, w.context, out, ws, err_word=err)
+    if w.window:
+        dq.dq_decode_attention_window(tabs, q, cache.k_cache, cache.v_cache, cache.k_norm, cache.v_norm,
+                                      cache.block_table, cache.context_lens, cache.win_k, cache.win_v,
+                                      cache.win_lens, hkv, w.page_size, w.context, out, ws, err_word=err)
+    else:
+        dq.dq_decode_attention(tabs, q, cache.k_cache, cache.v_cache, cache.k_norm, cache.v_norm, cache.block_table,
+                               cache.context_lens, hkv, w.page_size, w.context, out, ws, err_word=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     out = out.cpu().numpy()
@@ -171,9 +176,13 @@ def _full_size_sampled(dq, w, samples):
     G = hq // hkv
     for b, g in samples:
         T = int(cache.lens[b])
-        k = workloads.kv_rows(w, 0, synth.T_K, b, T)[:, g:g + 1].float().cpu().numpy()
-        v = workloads.kv_rows(w, 0, synth.T_V, b, T)[:, g:g + 1].float().cpu().numpy()
-        kc_, vc_, kn_, vn_, kh, vh = sequence_case(tk, tv, k, v)
+        W = int(cache.win_lens[b]) if w.window else 0
+        k = workloads.kv_rows(w, 0, synth.T_K, b, T + W)[:, g:g + 1].float().cpu().numpy()
+        v = workloads.kv_rows(w, 0, synth.T_V, b, T + W)[:, g:g + 1].float().cpu().numpy()
+        kc_, vc_, kn_, vn_, kh, vh = sequence_case(tk, tv, k[:T], v[:T])
+        if W:   # the window rows enter attention as their bf16 values
+            kh = np.concatenate([kh, synth.round_to_bf16(k[T:]).transpose(1, 0, 2).astype(np.float64)], axis=1)
+            vh = np.concatenate([vh, synth.round_to_bf16(v[T:]).transpose(1, 0, 2).astype(np.float64)], axis=1)
         slots = workloads.slot_mapping(bt[b:b + 1], cache.lens[b:b + 1], w.page_size)
         pg = torch.as_tensor(slots // w.page_size, device="cuda", dtype=torch.long)
         off = torch.as_tensor(slots % w.page_size, device="cuda", dtype=torch.long)
@@ -199,6 +208,13 @@ def test_ragged_low_budget_sampled(gpu_lib):
     w = workloads.WORKLOADS["ragged_1p96"]
     lens = workloads.context_lengths(w)
     _full_size_sampled(dq, w, [(int(np.argmin(lens)), 1), (int(np.argmax(lens)), 6), (31, 2)])
+
+
+def test_window_split_budget_layer_sampled(gpu_lib):
+    """A Qwen3-8B layer at batch 128 with the 128 newest tokens in bf16 and
+    41/27-byte key/value containers."""
+    dq = gpu_lib
+    _full_size_sampled(dq, workloads.WORKLOADS["window_split_qwen3_8b"], [(0, 0), (90, 5), (127, 7)])
 
 
 def test_decode_step_with_append(gpu_lib):
