@@ -63,10 +63,32 @@ __device__ __forceinline__ float wave_sum(float v) {
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     return v;
 }
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
-    return v;
+
+// Wave-wide maxima returned as wave-uniform values, by DPP moves: butterflies
+// inside each 16-lane row (quad swaps, half-row and row mirrors), then row
+// 15 -> row 1/3 and lane 31 -> rows 2/3 broadcasts, after which lane 63 holds
+// the maximum of all 64 lanes. Every lane must be active.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_mov(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ float wave_max_uniform(float v) {
+    v = fmaxf(v, __int_as_float(dpp_mov<0xB1>(__float_as_int(v))));        // quad_perm [1,0,3,2]
+    v = fmaxf(v, __int_as_float(dpp_mov<0x4E>(__float_as_int(v))));        // quad_perm [2,3,0,1]
+    v = fmaxf(v, __int_as_float(dpp_mov<0x141>(__float_as_int(v))));       // row_half_mirror
+    v = fmaxf(v, __int_as_float(dpp_mov<0x140>(__float_as_int(v))));       // row_mirror
+    v = fmaxf(v, __int_as_float(dpp_mov<0x142, 0xA>(__float_as_int(v))));  // row_bcast:15
+    v = fmaxf(v, __int_as_float(dpp_mov<0x143, 0xC>(__float_as_int(v))));  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ int wave_max_uniform_i(int v) {
+    v = max(v, dpp_mov<0xB1>(v));
+    v = max(v, dpp_mov<0x4E>(v));
+    v = max(v, dpp_mov<0x141>(v));
+    v = max(v, dpp_mov<0x140>(v));
+    v = max(v, dpp_mov<0x142, 0xA>(v));
+    v = max(v, dpp_mov<0x143, 0xC>(v));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // In-register 128-point Walsh-Hadamard transform (H x, entries +-1) of a row
@@ -95,40 +117,67 @@ __device__ __forceinline__ int f32_exponent(float v) {   // floor(log2 v) for v 
     return (int)((__float_as_uint(v) >> 23) & 255u) - 127;
 }
 
-// Copy the containers of 64 consecutive tokens (4 groups of 16, each group
-// contiguous inside one page) of KV head g into LDS at `dst`, token t at
-// dst + t * lds_stride(C), 16 bytes per lane and load. Groups that start at
-// or past T are skipped. With a padded stride (C a multiple of 8) the 16-byte
-// units are scattered as dwords: no dword straddles two containers then.
-template <bool PADDED>
-__device__ __forceinline__ void stage_tile(uint8_t* lds, uint32_t dst, const uint8_t* __restrict__ cache,
-                                           int C, uint32_t magic, const int32_t* __restrict__ bt_row, int log2p,
-                                           int P, int hkv, int g, int t0, int T, int lane) {
-    const int units = 4 * C;
-    const uint32_t S = lds_stride(C);
-    const uint32_t cq = (uint32_t)C >> 2;   // dwords per container when padded; d / cq = (d * magic) >> 16
-    for (int u = lane; u < units; u += 64) {
-        const int gi = (u >= C) + (u >= 2 * C) + (u >= 3 * C);
-        const int off = u - gi * C;
-        const int tok = t0 + 16 * gi;
-        if (tok < T) {
-            const int page = bt_row[tok >> log2p];
-            const int o = tok & (P - 1);
-            const uint8_t* src = cache + ((size_t)(page * hkv + g) * P + o) * C + (size_t)off * 16;
-            const u32x4 v = *(const u32x4*)src;
-            if (!PADDED) {
-                *(u32x4*)(lds + dst + (uint32_t)u * 16u) = v;
-            } else {
+// Row index ((page * Hkv + g) * P + slot) of the first token of each 16-token
+// group of the tile starting at t0 (< T); a page holds a multiple of 16
+// tokens, so each group's containers are 16 * C contiguous bytes and its norms
+// 16 contiguous halves. A group that starts at or past T takes group 0's row:
+// its lanes are masked out of the softmax, and the copy stays inside pages of
+// this sequence. Everything here is uniform over the wave.
+__device__ __forceinline__ void tile_rows(size_t* row, const int32_t* __restrict__ bt_row, int log2p, int P,
+                                          int hkv, int g, int t0, int T) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t d = (uint32_t)off * 4u + (uint32_t)k;      // dword within the 16-token group
-                    const uint32_t t = (d * magic) >> 16;                     // token within the group
-                    const uint32_t w = d - t * cq;                            // dword within its container
-                    *(uint32_t*)(lds + dst + (uint32_t)(16 * gi + (int)t) * S + 4u * w) = v[k];
-                }
-            }
+    for (int gi = 0; gi < 4; ++gi) {
+        const int tok = t0 + 16 * gi;
+        if (gi == 0 || tok < T) {
+            const int page = bt_row[tok >> log2p];
+            row[gi] = ((size_t)page * (size_t)hkv + (size_t)g) * (size_t)P + (size_t)(tok & (P - 1));
+        } else {
+            row[gi] = row[0];
         }
     }
+}
+
+// Copy the containers of the tile's 4 token groups into LDS at `dst`, token t
+// at dst + t * lds_stride(C). Lane u (and u + 64 when C > 64) moves 16-byte
+// unit u of every group: a load from the group's uniform base plus 16u, and an
+// LDS store at a per-lane offset. With a padded stride (C a multiple of 8) a
+// unit is stored as two 8-byte halves, each inside one container; the token
+// of byte b of a group is (b * magic) >> 21, exact for b < 2^11 with
+// magic = ceil(2^21 / C).
+template <bool PADDED>
+__device__ __forceinline__ void stage_unit(uint8_t* lds, uint32_t dst, const uint8_t* __restrict__ cache, int C,
+                                           uint32_t magic, const size_t* row, uint32_t u) {
+    const uint32_t S = lds_stride(C);
+    asm volatile("" : "+v"(u));   // recomputed per tile: hoisted, the offsets would stay live through the pass
+    uint32_t o0 = 16u * u, o1 = 0;
+    if (PADDED) {
+        const uint32_t b0 = 16u * u, b1 = b0 + 8u;
+        const uint32_t t0 = __umul24(b0, magic) >> 21, t1 = __umul24(b1, magic) >> 21;
+        o0 = t0 * S + (b0 - t0 * (uint32_t)C);
+        o1 = t1 * S + (b1 - t1 * (uint32_t)C);
+    }
+    u32x4 v[4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) v[gi] = *(const u32x4*)(cache + row[gi] * (size_t)C + 16u * u);
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+        const uint32_t base = dst + (uint32_t)gi * 16u * S;
+        if (!PADDED) {
+            *(u32x4*)(lds + base + o0) = v[gi];
+        } else {
+            *(uint32_t*)(lds + base + o0) = v[gi][0];
+            *(uint32_t*)(lds + base + o0 + 4u) = v[gi][1];
+            *(uint32_t*)(lds + base + o1) = v[gi][2];
+            *(uint32_t*)(lds + base + o1 + 4u) = v[gi][3];
+        }
+    }
+}
+
+template <bool PADDED>
+__device__ __forceinline__ void stage_tile(uint8_t* lds, uint32_t dst, const uint8_t* __restrict__ cache,
+                                           int C, uint32_t magic, const size_t* row, int lane) {
+    if (lane < C) stage_unit<PADDED>(lds, dst, cache, C, magic, row, (uint32_t)lane);
+    if (C > 64 && lane + 64 < C) stage_unit<PADDED>(lds, dst, cache, C, magic, row, (uint32_t)lane + 64u);
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -138,15 +187,97 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 struct AttnLaunch {
     AttnArgs a;
     int log2p;
-    uint32_t magic_k, magic_v;   // ceil(2^16 / (C/4)) for the padded staging
+    uint32_t magic_k, magic_v;   // ceil(2^21 / C) for the padded staging
 };
+
+// Attention partial of the uncompressed recent-token window (the paper keeps
+// the most recent tokens in BF16, section 5.1). For each query head of KV head
+// g: m = max logit, l = sum_t 2^(s_t - m) and acc = H (sum_t 2^(s_t - m) v_t),
+// in the same log2 logit scale and rotated output domain as the compressed
+// partials, written to slot `slot` so that merge_kernel combines them. Window
+// rows are in the original domain; wave w handles query head g*G + w, lane t
+// the tokens t, t+64, ...; p.v runs with each lane on channels lane, lane+64.
+// `smem`: 2 KB of queries and 4 KB of weights in LDS.
+__device__ __forceinline__ void window_partial(const AttnArgs& a, int slot, int g, int b, int tid, uint8_t* smem) {
+    float (*qs)[kHeadDim] = (float (*)[kHeadDim])smem;
+    float (*ps)[kWindowMax] = (float (*)[kWindowMax])(smem + 4 * kHeadDim * sizeof(float));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int G = a.group;
+    const int W = max(0, min(a.win_lens[b], a.win_cap));
+    for (int i = tid; i < G * kHeadDim; i += kThreads) {
+        const size_t qo = ((size_t)b * a.num_q_heads + g * G + i / kHeadDim) * kHeadDim + i % kHeadDim;
+        qs[i / kHeadDim][i % kHeadDim] =
+            a.q_dtype == DQ_DTYPE_BF16 ? bf16_to_f32(((const uint16_t*)a.q)[qo]) : ((const float*)a.q)[qo];
+    }
+    __syncthreads();
+    if (wave >= G) return;
+    float* ph = a.partials + (((size_t)b * a.num_q_heads + g * G + wave) * a.slot_count + slot) * kPartStride;
+    if (W == 0) {
+        if (lane == 0) { ph[0] = -INFINITY; ph[1] = 0.0f; }
+        return;
+    }
+    const size_t rows = ((size_t)b * a.num_kv_heads + g) * a.win_cap;
+    const uint16_t* kr = a.win_k + rows * kHeadDim;
+    const uint16_t* vr = a.win_v + rows * kHeadDim;
+    const float sc = a.softmax_scale * kLog2e;
+    float s[kWindowMax / 64];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kWindowMax / 64; ++j) {
+        const int t = lane + 64 * j;
+        s[j] = -INFINITY;
+        if (t < W) {
+            const uint16_t* row = kr + (size_t)t * kHeadDim;
+            float acc = 0.0f;
+            for (int c = 0; c < kHeadDim; c += 8) {
+                const u32x4 w8 = *(const u32x4*)(row + c);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    acc += qs[wave][c + 2 * k] * __uint_as_float(w8[k] << 16);
+                    acc += qs[wave][c + 2 * k + 1] * __uint_as_float(w8[k] & 0xFFFF0000u);
+                }
+            }
+            s[j] = acc * sc;
+        }
+        mx = fmaxf(mx, s[j]);
+    }
+    mx = wave_max(mx);
+    float l = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kWindowMax / 64; ++j) {
+        const int t = lane + 64 * j;
+        const float pj = t < W ? exp2f(s[j] - mx) : 0.0f;
+        ps[wave][t] = pj;
+        l += pj;
+    }
+    l = wave_sum(l);
+    wave_lds_sync();
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll 8
+    for (int t = 0; t < W; ++t) {
+        const float pt = ps[wave][t];
+        o0 += pt * bf16_to_f32(vr[(size_t)t * kHeadDim + lane]);
+        o1 += pt * bf16_to_f32(vr[(size_t)t * kHeadDim + 64 + lane]);
+    }
+    fwht128_f32(o0, o1, lane);
+    if (lane == 0) { ph[0] = mx; ph[1] = l; }
+    ph[4 + lane] = o0;
+    ph[4 + 64 + lane] = o1;
+}
+
+// One work-group per (KV head, sequence); a kernel of its own, since inlined
+// into the decode kernel it costs that kernel's schedule more than it saves.
+__global__ __launch_bounds__(kThreads) void window_kernel(AttnArgs a, int slot) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kHeadDim * 4 + 4 * kWindowMax * 4];
+    window_partial(a, slot, blockIdx.x, blockIdx.y, threadIdx.x, smem);
+}
 
 template <bool PAD_K, bool PAD_V>
 __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const AttnArgs& a = L.a;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     __attribute__((address_space(3))) uint8_t* lds_base = (__attribute__((address_space(3))) uint8_t*)lds;
     const int G = a.group;
     const int T = max(0, min(a.context_lens[b], a.max_pages_per_seq * a.page_size));
@@ -247,8 +378,17 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
                         if (do_k) rans_refill(kr);
                         if (do_v) rans_refill(vr);
                     }
-                    if (do_k) ek[jj] = rans_dec_step(kr, tabK, maskK, pk);
-                    if (do_v) ev[jj] = rans_dec_step(vr, tabV, maskV, pv);
+                    if (do_k && do_v) {
+                        // both table reads in flight before either chain advances
+                        ek[jj] = rans_lookup(kr, tabK, maskK);
+                        ev[jj] = rans_lookup(vr, tabV, maskV);
+                        __builtin_amdgcn_sched_barrier(0);
+                        rans_advance(kr, ek[jj], pk);
+                        rans_advance(vr, ev[jj], pv);
+                    } else {
+                        if (do_k) ek[jj] = rans_dec_step(kr, tabK, maskK, pk);
+                        if (do_v) ev[jj] = rans_dec_step(vr, tabV, maskV, pv);
+                    }
                 }
                 if (do_k) {
                     u32x4 bw;
@@ -287,43 +427,65 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         }
     };
 
-    // online softmax (log2 domain) of a decoded key tile; lane = token, d[r] = raw logit of head r.
-    // Value norms enter the p.v weights scaled by a running power of two so fp16 keeps them normal.
+    // Online softmax (log2 domain) of a decoded key tile; lane = token, d[r] =
+    // raw logit of head r. The running maximum m_run is only a reference
+    // point: any value works as long as the weights 2^(s - m_run) stay in
+    // range, so it is moved (and the accumulators rescaled) only when some
+    // logit of the tile exceeds it by more than kSlack - after the first
+    // tiles, rarely. Value norms enter the p.v weights scaled by a running
+    // power of two 2^-e_run (moved on the same condition) so that the fp16
+    // weights w * |v| 2^-e_run stay below 2^(kSlack + 1).
     auto softmax = [&](const float4v& d, bool valid, float rk, float rv) {
-        float w[4], alpha[4];
+        constexpr float kSlack = 8.0f;
+        float sv[4];
+        bool up = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float sv = valid ? d[r] * rk * kap[r] : -INFINITY;
-            const float mn = fmaxf(m_run[r], wave_max(sv));
-            alpha[r] = exp2f(m_run[r] - mn);
-            m_run[r] = mn;
-            w[r] = exp2f(sv - mn);
-            l_lane[r] = l_lane[r] * alpha[r] + w[r];
+            sv[r] = valid ? d[r] * rk * kap[r] : -INFINITY;
+            up |= r < G && sv[r] > m_run[r] + kSlack;
         }
-        const int e_tile = wave_max_i(valid && rv > 0.0f ? f32_exponent(rv) : -127);
-        const int e_new = max(e_run, e_tile);
-        const float sc = __builtin_amdgcn_ldexpf(1.0f, e_run - e_new);
-        e_run = e_new;
-        const float rvs = __builtin_amdgcn_ldexpf(rv, -e_new);
+        const int ev = valid && rv > 0.0f ? f32_exponent(rv) : -127;
+        if (__builtin_amdgcn_ballot_w64(up || ev > e_run)) {
+            float alpha[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                alpha[r] = 1.0f;
+                if (r < G) {
+                    const float mn = fmaxf(m_run[r], wave_max_uniform(sv[r]));
+                    alpha[r] = exp2f(m_run[r] - mn);
+                    m_run[r] = mn;
+                    l_lane[r] *= alpha[r];
+                }
+            }
+            const int e_new = max(e_run, wave_max_uniform_i(ev));
+            const float sc = __builtin_amdgcn_ldexpf(1.0f, e_run - e_new);
+            e_run = e_new;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][r] *= alpha[r] * sc;
+        }
+        const float rvs = __builtin_amdgcn_ldexpf(rv, -e_run);
         _Float16* wl = (_Float16*)(lds + oWl);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (r < G) wl[r * kRowH + lane] = (_Float16)(valid ? w[r] * rvs : 0.0f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][r] *= alpha[r] * sc;
+        for (int r = 0; r < 4; ++r) {
+            if (r < G) {
+                const float w = __builtin_amdgcn_exp2f(sv[r] - m_run[r]);   // 0 for a masked token
+                l_lane[r] += w;
+                wl[r * kRowH + lane] = (_Float16)(w * rvs);
+            }
+        }
     };
 
-    auto load_norms = [&](int t0, float& rk, float& rv) {
-        const int tok = t0 + lane;
+    // norms of the lane's token: row of its 16-token group plus its place in the group
+    auto load_norms = [&](int t0, const size_t* row, float& rk, float& rv) {
+        const int gl = lane >> 4;
+        const size_t r = (gl == 0 ? row[0] : gl == 1 ? row[1] : gl == 2 ? row[2] : row[3]) + (size_t)(lane & 15);
         rk = 0.0f;
         rv = 0.0f;
-        if (tok < T) {
-            const int page = bt_row[tok >> log2p];
-            const size_t ni = (size_t)(page * hkv + g) * P + (tok & (P - 1));
-            rk = f16_to_f32(a.k_norm[ni]);
-            rv = f16_to_f32(a.v_norm[ni]);
+        if (t0 + lane < T) {
+            rk = f16_to_f32(a.k_norm[r]);
+            rv = f16_to_f32(a.v_norm[r]);
         }
     };
 
@@ -334,10 +496,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     int t = start + wave * kTile;
     if (t < end) {
         // prologue: keys of the first tile
-        stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, bt_row, log2p, P, hkv, g, t, T, lane);
-        stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, bt_row, log2p, P, hkv, g, t, T, lane);
+        size_t row[4];
+        tile_rows(row, bt_row, log2p, P, hkv, g, t, T);
+        stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
+        stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, row, lane);
         float rk, rv;
-        load_norms(t, rk, rv);
+        load_norms(t, row, rk, rv);
         wave_lds_sync();
         const bool valid = t + lane < T;
         RansLane kr;
@@ -374,8 +538,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         const bool valid = t + lane < T, valid_n = tn + lane < T;
         float rk_n = 0.0f, rv_n = 0.0f;
         if (has_next) {
-            stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, bt_row, log2p, P, hkv, g, tn, T, lane);
-            load_norms(tn, rk_n, rv_n);
+            size_t row[4];
+            tile_rows(row, bt_row, log2p, P, hkv, g, tn, T);
+            stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
+            load_norms(tn, row, rk_n, rv_n);
         }
         wave_lds_sync();
         RansLane vr, kr;
@@ -395,7 +561,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         if (has_next) {
             softmax(dk, valid_n, rk_n, rv_n);
             wave_lds_sync();
-            stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, bt_row, log2p, P, hkv, g, tn, T, lane);
+            size_t row[4];   // recomputed (scalar loads) rather than held through the pass
+            tile_rows(row, bt_row, log2p, P, hkv, g, tn, T);
+            stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, row, lane);
         }
     }
     if (bad && a.err_word) atomicOr(a.err_word, DQ_DEVERR_DECODE);
@@ -494,79 +662,6 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __
     out[(size_t)bh * kHeadDim + 64 + lane] = v1;
 }
 
-// Attention partial of the uncompressed recent-token window (the paper keeps
-// the most recent tokens in BF16, section 5.1). For each query head of KV head
-// g: m = max logit, l = sum_t 2^(s_t - m) and acc = H (sum_t 2^(s_t - m) v_t),
-// in the same log2 logit scale and rotated output domain as the compressed
-// partials, written to slot `slot` so that merge_kernel combines them. Window
-// rows are in the original domain; wave w handles query head g*G + w, lane t
-// the tokens t, t+64, ...; p.v runs with each lane on channels lane, lane+64.
-__global__ __launch_bounds__(kThreads) void window_kernel(AttnArgs a, int slot) {
-    __shared__ float qs[4][kHeadDim];
-    __shared__ float ps[4][kWindowMax];
-    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int G = a.group;
-    const int W = max(0, min(a.win_lens[b], a.win_cap));
-    for (int i = tid; i < G * kHeadDim; i += kThreads) {
-        const size_t qo = ((size_t)b * a.num_q_heads + g * G + i / kHeadDim) * kHeadDim + i % kHeadDim;
-        qs[i / kHeadDim][i % kHeadDim] =
-            a.q_dtype == DQ_DTYPE_BF16 ? bf16_to_f32(((const uint16_t*)a.q)[qo]) : ((const float*)a.q)[qo];
-    }
-    __syncthreads();
-    if (wave >= G) return;
-    float* ph = a.partials + (((size_t)b * a.num_q_heads + g * G + wave) * a.slot_count + slot) * kPartStride;
-    if (W == 0) {
-        if (lane == 0) { ph[0] = -INFINITY; ph[1] = 0.0f; }
-        return;
-    }
-    const size_t rows = ((size_t)b * a.num_kv_heads + g) * a.win_cap;
-    const uint16_t* kr = a.win_k + rows * kHeadDim;
-    const uint16_t* vr = a.win_v + rows * kHeadDim;
-    const float sc = a.softmax_scale * kLog2e;
-    float s[kWindowMax / 64];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kWindowMax / 64; ++j) {
-        const int t = lane + 64 * j;
-        s[j] = -INFINITY;
-        if (t < W) {
-            const uint16_t* row = kr + (size_t)t * kHeadDim;
-            float acc = 0.0f;
-            for (int c = 0; c < kHeadDim; c += 8) {
-                const u32x4 w8 = *(const u32x4*)(row + c);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    acc += qs[wave][c + 2 * k] * __uint_as_float(w8[k] << 16);
-                    acc += qs[wave][c + 2 * k + 1] * __uint_as_float(w8[k] & 0xFFFF0000u);
-                }
-            }
-            s[j] = acc * sc;
-        }
-        mx = fmaxf(mx, s[j]);
-    }
-    mx = wave_max(mx);
-    float l = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kWindowMax / 64; ++j) {
-        const int t = lane + 64 * j;
-        const float pj = t < W ? exp2f(s[j] - mx) : 0.0f;
-        ps[wave][t] = pj;
-        l += pj;
-    }
-    l = wave_sum(l);
-    wave_lds_sync();
-    float o0 = 0.0f, o1 = 0.0f;
-    for (int t = 0; t < W; ++t) {
-        const float pt = ps[wave][t];
-        o0 += pt * bf16_to_f32(vr[(size_t)t * kHeadDim + lane]);
-        o1 += pt * bf16_to_f32(vr[(size_t)t * kHeadDim + 64 + lane]);
-    }
-    fwht128_f32(o0, o1, lane);
-    if (lane == 0) { ph[0] = mx; ph[1] = l; }
-    ph[4 + lane] = o0;
-    ph[4 + 64 + lane] = o1;
-}
-
 // Test hook: decode 64 contiguous containers per wave into symbol indices.
 __global__ __launch_bounds__(kThreads) void decode_symbols_kernel(const uint32_t* __restrict__ ent, int p,
                                                                   int C, const uint8_t* __restrict__ in, int n,
@@ -613,9 +708,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     L.log2p = 31 - __builtin_clz((unsigned)a.page_size);
     if ((1 << L.log2p) != a.page_size) return hipErrorInvalidValue;
     const size_t lds = kOffWaves + (size_t)kWaves * wave_bytes(a.ck, a.cv);
-    const uint32_t cqk = (uint32_t)a.ck / 4, cqv = (uint32_t)a.cv / 4;
-    L.magic_k = (65536u + cqk - 1u) / cqk;
-    L.magic_v = (65536u + cqv - 1u) / cqv;
+    L.magic_k = ((1u << 21) + (uint32_t)a.ck - 1u) / (uint32_t)a.ck;
+    L.magic_v = ((1u << 21) + (uint32_t)a.cv - 1u) / (uint32_t)a.cv;
     const bool pk = lds_stride(a.ck) != (uint32_t)a.ck, pv = lds_stride(a.cv) != (uint32_t)a.cv;
     const void* fn = pk ? (pv ? (const void*)attn_kernel<true, true> : (const void*)attn_kernel<true, false>)
                         : (pv ? (const void*)attn_kernel<false, true> : (const void*)attn_kernel<false, false>);

@@ -65,6 +65,18 @@ __device__ __forceinline__ uint32_t rans_consumed(const RansLane& r, uint32_t ba
 // from the window; the shift-in is a v_perm whose selector counts the bytes
 // already taken, so the step has no branch. `tab` is the table's absolute
 // LDS address. Returns the entry. At most 4 steps may run between refills.
+__device__ __forceinline__ uint32_t rans_lookup(const RansLane& r, uint32_t tab, uint32_t mask) {
+    return *(lds_u32*)(size_t)(tab + ((r.x & mask) << 2));
+}
+__device__ __forceinline__ void rans_advance(RansLane& r, uint32_t e, uint32_t p) {
+    const uint32_t f = (e >> 18) & 1023u;
+    const uint32_t bias = (e >> 8) & 1023u;
+    const uint32_t xn = __umul24(f, r.x >> p) + bias;       // f < 2^10, x >> p < 2^14
+    const uint32_t t = __builtin_amdgcn_perm(xn, r.win, r.sel);
+    const bool need = xn < kStateLow;
+    r.x = need ? t : xn;
+    r.sel += need ? 1u : 0u;
+}
 __device__ __forceinline__ uint32_t rans_dec_step(RansLane& r, uint32_t tab, uint32_t mask, uint32_t p) {
     const uint32_t e = *(lds_u32*)(size_t)(tab + ((r.x & mask) << 2));
     const uint32_t f = (e >> 18) & 1023u;
