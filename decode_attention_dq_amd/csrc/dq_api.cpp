@@ -343,7 +343,7 @@ static int decode_attention_impl(const dq_tables* t, const void* q, int q_dtype,
         max_pages_per_seq <= 0 || page_size <= 0 || page_size % 16 || max_context < 0 ||
         num_splits < 0 || (long)max_pages_per_seq * page_size < max_context)
         return DQ_ERR_INVALID_ARG;
-    if (num_q_heads / num_kv_heads > 4) return DQ_ERR_UNSUPPORTED;
+    if (num_q_heads / num_kv_heads > 4 || (page_size & (page_size - 1))) return DQ_ERR_UNSUPPORTED;
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace)) return DQ_ERR_INVALID_ARG;
     const bool win = window_k != nullptr;
     if (win) {

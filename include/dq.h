@@ -185,8 +185,9 @@ size_t dq_workspace_size(int batch, int num_q_heads, int num_kv_heads, int max_c
  *   out           fp32 [batch][num_q_heads][128]
  *   workspace     device buffer of at least dq_workspace_size(...) bytes,
  *                 16-byte aligned
- * num_q_heads / num_kv_heads must be 1..4 (query heads per KV head),
- * page_size a multiple of 16, caches 16-byte aligned.
+ * num_q_heads / num_kv_heads must be 1..4 (query heads per KV head) and
+ * page_size a power of two of at least 16 (DQ_ERR_UNSUPPORTED otherwise);
+ * caches and workspace 16-byte aligned (DQ_ERR_INVALID_ARG otherwise).
  */
 int dq_decode_attention(const dq_tables* tables, const void* q, int q_dtype,
                         const uint8_t* k_cache, const uint8_t* v_cache,

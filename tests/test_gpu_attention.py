@@ -101,6 +101,22 @@ def test_attention_group_sizes(gpu_lib, G):
     assert row_rel_err(out, ref).max() <= TOL
 
 
+def test_page_size_not_power_of_two_is_unsupported(gpu_lib):
+    """The kernel locates a token's page by shift and mask: a 48-token page is
+    refused on the host before any launch."""
+    dq = gpu_lib
+    _, _, tabs = _tables(dq)
+    z = lambda n, dt=torch.uint8: torch.zeros(n, dtype=dt, device="cuda")
+    q = torch.zeros((1, 4, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((1, 4, 128), dtype=torch.float32, device="cuda")
+    ws = z(dq.dq_workspace_size(1, 4, 1, 48))
+    with pytest.raises(dq.DQError) as ei:
+        dq.dq_decode_attention(tabs, q, z(48 * 37), z(48 * 37), z(48, torch.int16), z(48, torch.int16),
+                               torch.zeros((1, 1), dtype=torch.int32, device="cuda"),
+                               torch.full((1,), 48, dtype=torch.int32, device="cuda"), 1, 48, 48, out, ws)
+    assert ei.value.code == dq.DQ_ERR_UNSUPPORTED
+
+
 def test_split_invariance(gpu_lib):
     dq = gpu_lib
     tk, tv, tabs = _tables(dq)
