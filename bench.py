@@ -195,6 +195,43 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
     return res
 
 
+def bf16_measurement(dq, torch, workloads, name: str, copies: int, dq_us: float, reps: int = 5) -> dict:
+    """The uncompressed bf16 reference kernel on the same shape, rotating
+    through `copies` bf16 caches (each far above the 256 MB MALL)."""
+    w = workloads.WORKLOADS[name]
+    caches = [workloads.build_bf16_cache(w, layer=l) for l in range(copies)]
+    qs = [workloads.query_rows(w, l) for l in range(copies)]
+    B, hq, hkv = w.batch, w.num_q_heads, w.num_kv_heads
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dq.dq_workspace_size(B, hq, hkv, w.context), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(l):
+        kc, vc, bt, cl = caches[l]
+        dq.dq_bf16_decode_attention(qs[l], kc, vc, bt, cl, hkv, w.page_size, w.context, out, ws, stream=stream)
+
+    for l in range(copies):
+        call(l)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        for l in range(copies):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call(l)
+            e1.record(stream)
+            ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    nbytes = int(np.sum(workloads.context_lengths(w))) * hkv * 2 * 256
+    del caches
+    torch.cuda.empty_cache()
+    return {"workload": name, "kv_bytes_per_call": nbytes, "cache_copies": copies, "us_per_call": round(t * 1e6, 2),
+            "GBps": round(nbytes / t / 1e9, 2), "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "kv_bytes_vs_compressed": round(nbytes / algorithmic_bytes(w, workloads.context_lengths(w)), 3),
+            "compressed_time_ratio": round(dq_us / (t * 1e6), 3)}
+
+
 def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None when
     the kernel sources changed since those counters were taken."""
@@ -302,7 +339,8 @@ def main() -> int:
     symbols = int(np.sum(lens)) * hkv * 128 * 2
     gbs = nbytes / per_call_s / 1e9
     tops = symbols * OPS_PER_SYMBOL / per_call_s / 1e12
-    splits = args.splits or dq._lib.dq_workspace_size(B, hq, hkv, w.context, 0) // (B * hq * 132 * 4)
+    # the workspace holds one partial slot per split plus one for a bf16 window
+    splits = args.splits or dq._lib.dq_workspace_size(B, hq, hkv, w.context, 0) // (B * hq * 132 * 4) - 1
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -341,6 +379,8 @@ def main() -> int:
             "ragged_1p96": config_measurement(dq, torch, workloads, "ragged_1p96", copies=2),
             "window_split_qwen3_8b": config_measurement(dq, torch, workloads, "window_split_qwen3_8b", copies=2),
         }
+        result["bf16_reference"] = bf16_measurement(dq, torch, workloads, w.name, copies=2,
+                                                    dq_us=per_call_s * 1e6)
     if not args.no_cpu_baseline:
         import oracle
         tk = oracle.make_table(w.k_levels, w.container)

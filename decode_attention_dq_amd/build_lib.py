@@ -27,6 +27,7 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", "--offload-arch=gfx950", f"-I{INCLUDE}",
 UNITS = {
     "dq_api.cpp": [],
     "dq_attn.hip": [],
+    "dq_bf16.hip": [],
     "dq_encode.hip": ["-ffp-contract=off"],
 }
 

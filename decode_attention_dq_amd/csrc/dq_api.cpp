@@ -405,6 +405,47 @@ int dq_decode_attention(const dq_tables* t, const void* q, int q_dtype, const ui
                                  workspace_bytes, err_word, stream);
 }
 
+int dq_bf16_decode_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                             const int32_t* block_table, const int32_t* context_lens, int batch,
+                             int num_q_heads, int num_kv_heads, int max_pages_per_seq, int page_size,
+                             int max_context, float softmax_scale, int num_splits, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out || !workspace)
+        return DQ_ERR_INVALID_ARG;
+    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+        max_pages_per_seq <= 0 || page_size <= 0 || page_size % 16 || max_context < 0 ||
+        num_splits < 0 || (long)max_pages_per_seq * page_size < max_context)
+        return DQ_ERR_INVALID_ARG;
+    if (num_q_heads / num_kv_heads > 4 || (page_size & (page_size - 1))) return DQ_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+        return DQ_ERR_INVALID_ARG;
+    const int splits = num_splits ? num_splits : dq::choose_splits(batch, num_kv_heads, max_context);
+    if (workspace_bytes < dq_workspace_size(batch, num_q_heads, num_kv_heads, max_context, splits))
+        return DQ_ERR_WORKSPACE;
+    if ((long)batch * num_kv_heads * splits > (long)INT32_MAX / 4) return DQ_ERR_INVALID_ARG;
+    dq::Bf16Args a;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.max_pages_per_seq = max_pages_per_seq;
+    a.page_size = page_size;
+    a.log2p = 31 - __builtin_clz((unsigned)page_size);
+    a.num_splits = splits;
+    a.split_len = dq::split_tokens(max_context, splits);
+    a.slot_count = splits + 1;
+    a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
+    a.partials = (float*)workspace;
+    a.out = out;
+    hipError_t e = dq::launch_bf16_attention(a, (hipStream_t)stream);
+    return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
 int dq_decode_attention_window(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
                                const uint8_t* v_cache, const uint16_t* k_norm, const uint16_t* v_norm,
                                const int32_t* block_table, const int32_t* context_lens, int batch,

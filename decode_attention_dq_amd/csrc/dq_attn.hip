@@ -608,11 +608,13 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
 }
 
 // Merge the splits of one (sequence, query head) by log-sum-exp and rotate
-// back: out = H (sum_s acc_s 2^(m_s - M)) / (128 * sum_s l_s 2^(m_s - M)).
-// 4 waves share the splits (wave w takes s = w, w + 4, ...), each lane two
+// back: out = H (sum_s acc_s 2^(m_s - M)) / (128 * sum_s l_s 2^(m_s - M)),
+// or, for partials in the original domain (ROTATED false),
+// out = (sum_s acc_s 2^(m_s - M)) / (sum_s l_s 2^(m_s - M)). 4 waves share the splits (wave w takes s = w, w + 4, ...), each lane two
 // channels; the loads of different splits are independent, so many are in
 // flight at once.
 constexpr int kMergeWaves = 4;
+template <bool ROTATED>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __restrict__ partials, int slot_count,
                                                                  int splits, float* __restrict__ out) {
     __shared__ float red[kMergeWaves][132];
@@ -654,10 +656,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __
         v1 += red[w][64 + lane];
         L += red[w][128];
     }
-    const float inv = L > 0.0f ? 1.0f / (L * (float)kHeadDim) : 0.0f;
+    const float inv = L > 0.0f ? 1.0f / (ROTATED ? L * (float)kHeadDim : L) : 0.0f;
     v0 *= inv;
     v1 *= inv;
-    fwht128_f32(v0, v1, lane);
+    if (ROTATED) fwht128_f32(v0, v1, lane);
     out[(size_t)bh * kHeadDim + lane] = v0;
     out[(size_t)bh * kHeadDim + 64 + lane] = v1;
 }
@@ -732,8 +734,17 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     else hipLaunchKernelGGL((attn_kernel<false, false>), grid, dim3(kThreads), lds, s, L);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(merge_kernel, dim3(a.batch * a.num_q_heads), dim3(64 * kMergeWaves), 0, s, a.partials,
-                       a.slot_count, a.merge_slots, a.out);
+    return launch_merge(a.partials, a.slot_count, a.merge_slots, a.batch * a.num_q_heads, true, a.out, s);
+}
+
+hipError_t launch_merge(const float* partials, int slot_count, int splits, int rows, bool rotated, float* out,
+                        hipStream_t s) {
+    if (rotated)
+        hipLaunchKernelGGL(merge_kernel<true>, dim3(rows), dim3(64 * kMergeWaves), 0, s, partials, slot_count, splits,
+                           out);
+    else
+        hipLaunchKernelGGL(merge_kernel<false>, dim3(rows), dim3(64 * kMergeWaves), 0, s, partials, slot_count,
+                           splits, out);
     return hipGetLastError();
 }
 

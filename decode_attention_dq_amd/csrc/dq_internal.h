@@ -81,12 +81,32 @@ struct AttnArgs {
     uint32_t* err_word;
 };
 
+// Uncompressed bf16 reference: the same paged layout with 128 bf16 per
+// (token, KV head) row instead of a container and a norm.
+struct Bf16Args {
+    const uint16_t* q;                  // bf16 [batch][Hq][128]
+    const uint16_t* k_cache;            // bf16 [pages][Hkv][page_size][128]
+    const uint16_t* v_cache;
+    const int32_t* block_table;
+    const int32_t* context_lens;
+    int batch, num_q_heads, num_kv_heads, group, max_pages_per_seq, page_size, log2p;
+    int num_splits, split_len, slot_count;
+    float softmax_scale;
+    float* partials;
+    float* out;
+};
+
 constexpr int kPartStride = 132;         // m, l, pad, pad, acc[128]
 constexpr int kWindowMax = 256;          // largest bf16 window
 
 // Launchers (defined next to their kernels).
 hipError_t launch_encode(const EncArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_bf16_attention(const Bf16Args& a, hipStream_t s);
+// Log-sum-exp merge of `splits` partials per (sequence, query head) into out;
+// `rotated`: the partials are in the rotated domain (inverse rotation applied).
+hipError_t launch_merge(const float* partials, int slot_count, int splits, int rows, bool rotated, float* out,
+                        hipStream_t s);
 hipError_t launch_decode_symbols(const uint32_t* entries, int prob_bits, int levels, int container,
                                  const uint8_t* containers, int n, uint8_t* out, uint32_t* err,
                                  hipStream_t s);

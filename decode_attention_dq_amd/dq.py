@@ -74,6 +74,8 @@ _sig = {
                                  ctypes.c_float, _i, _p, _p, ctypes.c_size_t, _p, _p]),
     "dq_decode_attention_window": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                         ctypes.c_float, _i, _p, _p, _p, _i, _p, _p, ctypes.c_size_t, _p, _p]),
+    "dq_bf16_decode_attention": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i, _p, _p,
+                                      ctypes.c_size_t, _p]),
     "dq_decode_symbols": (_i, [_p, _i, _p, _i, _p, _p, _p]),
     "dq_selftest_fp64": (_i, [_p, _p, _i, _p, _p, _p, _p]),
     "dq_strerror": (ctypes.c_char_p, [_i]),
@@ -228,6 +230,34 @@ def dq_decode_attention(tables: Tables, q, k_cache, v_cache, k_norm, v_norm, blo
                                     int(max_context), float(softmax_scale), int(num_splits), _ptr(out),
                                     _ptr(workspace), nbytes, _ptr(err_word), _stream(stream)),
            "dq_decode_attention")
+
+
+def dq_bf16_decode_attention(q, k_cache, v_cache, block_table, context_lens, num_kv_heads: int, page_size: int,
+                             max_context: int, out, workspace, softmax_scale: float = 0.0, num_splits: int = 0,
+                             stream=None) -> None:
+    """Uncompressed reference: q [B][Hq][128] bf16, k_cache / v_cache
+    [pages][Hkv][page_size][128] bf16, out [B][Hq][128] float32."""
+    import torch
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16 [B][Hq][128]")
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    _need(q, "q")
+    _need(out, "out", torch.float32, (B, hq, HEAD_DIM))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages_per_seq]")
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, torch.bfloat16)
+        if t.dim() != 4 or t.shape[1] != num_kv_heads or t.shape[2] != page_size or t.shape[3] != HEAD_DIM:
+            raise ValueError(f"{nm} must be [pages][Hkv][page_size][128]")
+    _need(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.dq_bf16_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                         _ptr(context_lens), B, hq, int(num_kv_heads), int(block_table.shape[1]),
+                                         int(page_size), int(max_context), float(softmax_scale), int(num_splits),
+                                         _ptr(out), _ptr(workspace), nbytes, _stream(stream)),
+           "dq_bf16_decode_attention")
 
 
 def dq_decode_attention_window(tables: Tables, q, k_cache, v_cache, k_norm, v_norm, block_table, context_lens,

@@ -162,3 +162,23 @@ def build_cache(dq, tables, w: Workload, layer: int = 0, keep_stats: bool = Fals
         c.win_k, c.win_v = wk, wv
         c.win_lens = torch.as_tensor((full - lens).astype(np.int32), device=device)
     return c
+
+
+def build_bf16_cache(w: Workload, layer: int = 0, device="cuda"):
+    """The same sequences as build_cache, stored uncompressed: bf16 K and V
+    caches [pages][Hkv][P][128] with the same page plan. Rows past a
+    sequence's end are left unset. Returns (k_cache, v_cache, block_table,
+    context_lens) as device tensors."""
+    import torch
+    lens = context_lengths(w)
+    bt, total = page_plan(w, lens)
+    P, H = w.page_size, w.num_kv_heads
+    kc = torch.empty((total, H, P, 128), dtype=torch.bfloat16, device=device)
+    vc = torch.empty_like(kc)
+    for b in range(w.batch):
+        T = int(lens[b])
+        slots = torch.as_tensor(slot_mapping(bt[b:b + 1], lens[b:b + 1], P), device=device, dtype=torch.long)
+        pg, off = slots // P, slots % P
+        kc[pg, :, off] = kv_rows(w, layer, synth.T_K, b, T, device).to(torch.bfloat16)
+        vc[pg, :, off] = kv_rows(w, layer, synth.T_V, b, T, device).to(torch.bfloat16)
+    return kc, vc, torch.as_tensor(bt, device=device), torch.as_tensor(lens, device=device)

@@ -224,6 +224,27 @@ int dq_decode_attention_window(const dq_tables* tables, const void* q, int q_dty
                                uint32_t* err_word, void* stream);
 
 /*
+ * Uncompressed reference: split-K decode attention over a paged bf16 KV cache
+ * (the paper's full-precision baseline is BF16 attention, section 5.1), with
+ * the same paged layout, GQA map, split rule and workspace as
+ * dq_decode_attention, for timing the two side by side.
+ *   q                bf16 bits [batch][num_q_heads][128]
+ *   k_cache, v_cache bf16 bits [num_pages][num_kv_heads][page_size][128],
+ *                    16-byte aligned
+ *   block_table, context_lens, batch .. num_splits, out, workspace as for
+ *                    dq_decode_attention (workspace of dq_workspace_size(...))
+ * out[b][h] = softmax(q.K^T * scale) V over the context_lens[b] tokens, fp32.
+ * Rows past context_lens[b] inside a page may hold anything; they are ignored.
+ * Returns DQ_ERR_INVALID_ARG / DQ_ERR_UNSUPPORTED / DQ_ERR_WORKSPACE as
+ * dq_decode_attention does.
+ */
+int dq_bf16_decode_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                             const int32_t* block_table, const int32_t* context_lens,
+                             int batch, int num_q_heads, int num_kv_heads, int max_pages_per_seq,
+                             int page_size, int max_context, float softmax_scale, int num_splits,
+                             float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Test hook: decode n_streams contiguous containers ([n_streams][C] bytes of
  * table `which`) into symbol indices uint8 [n_streams][128] with the same
  * device decode routine the attention kernel uses. Streams that fail the
