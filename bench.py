@@ -241,7 +241,7 @@ def recorded_traffic(kernel: str, workload: str):
     except (OSError, KeyError, ValueError):
         return None
     h = hashlib.sha256()
-    for f in ("dq_attn.hip", "dq_device.h"):
+    for f in ("dq_attn.hip", "dq_device.h", "dq_wave.h"):
         h.update(open(os.path.join(ROOT, "decode_attention_dq_amd", "csrc", f), "rb").read())
     if rec.get("source_sha256") != h.hexdigest() or rec.get("workload") != workload:
         return None

@@ -28,6 +28,8 @@ UNITS = {
     "dq_api.cpp": [],
     "dq_attn.hip": [],
     "dq_bf16.hip": [],
+    "dq_merge.hip": [],
+    "dq_window.hip": [],
     "dq_encode.hip": ["-ffp-contract=off"],
 }
 

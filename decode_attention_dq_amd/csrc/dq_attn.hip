@@ -21,6 +21,7 @@
 //     and write one partial (m, l, acc[128]) per query head and split; a
 //     second kernel merges the splits and rotates the result back.
 #include "dq_device.h"
+#include "dq_wave.h"
 
 namespace dq {
 namespace {
@@ -38,7 +39,6 @@ constexpr uint32_t kOffQt = 8192;         // [4][128] fp16 rotated queries
 constexpr uint32_t kOffZero = 9216;       // 256 zero bytes: A operand of rows without a head
 constexpr uint32_t kOffKappa = 9472;      // [4] floats
 constexpr uint32_t kOffWaves = 9488;
-constexpr float kLog2e = 1.4426950408889634f;
 
 __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
 
@@ -51,70 +51,6 @@ __host__ __device__ inline uint32_t lds_stride(int c) { return (c & 7) ? (uint32
 __host__ __device__ inline uint32_t wave_bytes(int ck, int cv) {
     return align16(kTile * lds_stride(ck) + kPad) + align16(kTile * lds_stride(cv) + kPad) + kTile * kVtRow +
            4 * kRowB;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-// Wave-wide maxima returned as wave-uniform values, by DPP moves: butterflies
-// inside each 16-lane row (quad swaps, half-row and row mirrors), then row
-// 15 -> row 1/3 and lane 31 -> rows 2/3 broadcasts, after which lane 63 holds
-// the maximum of all 64 lanes. Every lane must be active.
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ int dpp_mov(int v) {
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xF, false);
-}
-__device__ __forceinline__ float wave_max_uniform(float v) {
-    v = fmaxf(v, __int_as_float(dpp_mov<0xB1>(__float_as_int(v))));        // quad_perm [1,0,3,2]
-    v = fmaxf(v, __int_as_float(dpp_mov<0x4E>(__float_as_int(v))));        // quad_perm [2,3,0,1]
-    v = fmaxf(v, __int_as_float(dpp_mov<0x141>(__float_as_int(v))));       // row_half_mirror
-    v = fmaxf(v, __int_as_float(dpp_mov<0x140>(__float_as_int(v))));       // row_mirror
-    v = fmaxf(v, __int_as_float(dpp_mov<0x142, 0xA>(__float_as_int(v))));  // row_bcast:15
-    v = fmaxf(v, __int_as_float(dpp_mov<0x143, 0xC>(__float_as_int(v))));  // row_bcast:31
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-__device__ __forceinline__ int wave_max_uniform_i(int v) {
-    v = max(v, dpp_mov<0xB1>(v));
-    v = max(v, dpp_mov<0x4E>(v));
-    v = max(v, dpp_mov<0x141>(v));
-    v = max(v, dpp_mov<0x140>(v));
-    v = max(v, dpp_mov<0x142, 0xA>(v));
-    v = max(v, dpp_mov<0x143, 0xC>(v));
-    return __builtin_amdgcn_readlane(v, 63);
-}
-
-// In-register 128-point Walsh-Hadamard transform (H x, entries +-1) of a row
-// held as v0 = x[lane], v1 = x[lane + 64]: butterflies of span 1..32 across
-// lanes, then span 64 inside the lane.
-__device__ __forceinline__ void fwht128_f32(float& v0, float& v1, int lane) {
-#pragma unroll
-    for (int h = 1; h < 64; h <<= 1) {
-        const float p0 = __shfl_xor(v0, h), p1 = __shfl_xor(v1, h);
-        const bool lo = (lane & h) == 0;
-        v0 = lo ? v0 + p0 : p0 - v0;
-        v1 = lo ? v1 + p1 : p1 - v1;
-    }
-    const float a = v0, b = v1;
-    v0 = a + b;
-    v1 = a - b;
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-__device__ __forceinline__ float f16_to_f32(uint16_t h) {
-    _Float16 v;
-    __builtin_memcpy(&v, &h, 2);
-    return (float)v;
-}
-__device__ __forceinline__ int f32_exponent(float v) {   // floor(log2 v) for v > 0 normal
-    return (int)((__float_as_uint(v) >> 23) & 255u) - 127;
 }
 
 // Row index ((page * Hkv + g) * P + slot) of the first token of each 16-token
@@ -189,138 +125,6 @@ struct AttnLaunch {
     int log2p;
     uint32_t magic_k, magic_v;   // ceil(2^21 / C) for the padded staging
 };
-
-// Attention partial of the uncompressed recent-token window (the paper keeps
-// the most recent tokens in BF16, section 5.1). For each query head of KV head
-// g: m = max logit, l = sum_t 2^(s_t - m) and acc = H (sum_t 2^(s_t - m) v_t),
-// in the same log2 logit scale and rotated output domain as the compressed
-// partials, written to slot `slot` so that merge_kernel combines them. Window
-// rows are in the original domain. One work-group per (KV head, sequence); wave
-// w takes window tokens [64w, 64w + 64) for all query heads of the group: lane
-// t computes its token's logits from one K row; for p.v, lane (c, r) takes
-// channels 8c..8c+7 of the wave's tokens r, r + 4, ... (16-byte row loads,
-// all in flight at once). The lane groups are summed by shuffles, the waves'
-// maxima, sums and accumulators in LDS. A kernel of its own: inlined into the decode kernel
-// it costs that kernel's schedule more than it saves.
-static_assert(kWindowMax == 64 * kWaves, "one window token per thread");
-__global__ __launch_bounds__(kThreads) void window_kernel(AttnArgs a, int slot) {
-    __shared__ float qs[4][kHeadDim];
-    __shared__ float ps[4][kWindowMax];          // weights [head][token]
-    __shared__ float wo[kWaves][4][kHeadDim];    // per-wave p.v accumulators
-    __shared__ float wm[kWaves][4], wsum[kWaves][4];
-    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int G = a.group;
-    const int W = max(0, min(a.win_lens[b], a.win_cap));
-    const size_t hs = (size_t)a.slot_count * kPartStride;
-    float* part = a.partials + (((size_t)b * a.num_q_heads + (size_t)g * G) * a.slot_count + slot) * kPartStride;
-    if (W == 0) {
-        if (tid < G) { part[tid * hs] = -INFINITY; part[tid * hs + 1] = 0.0f; }
-        return;
-    }
-    for (int i = tid; i < G * kHeadDim; i += kThreads) {
-        const size_t qo = ((size_t)b * a.num_q_heads + g * G + i / kHeadDim) * kHeadDim + i % kHeadDim;
-        qs[i / kHeadDim][i % kHeadDim] =
-            a.q_dtype == DQ_DTYPE_BF16 ? bf16_to_f32(((const uint16_t*)a.q)[qo]) : ((const float*)a.q)[qo];
-    }
-    __syncthreads();
-    const size_t rows = ((size_t)b * a.num_kv_heads + g) * a.win_cap;
-    const uint16_t* kr = a.win_k + rows * kHeadDim;
-    const uint16_t* vr = a.win_v + rows * kHeadDim;
-    const float sc = a.softmax_scale * kLog2e;
-    const int t = 64 * wave + lane;
-    float s[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (t < W) {
-        const uint16_t* row = kr + (size_t)t * kHeadDim;
-        u32x4 kw[kHeadDim / 8];   // the whole row in flight at once
-#pragma unroll
-        for (int i = 0; i < kHeadDim / 8; ++i) kw[i] = *(const u32x4*)(row + 8 * i);
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < kHeadDim / 8; ++i) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float k0 = __uint_as_float(kw[i][k] << 16), k1 = __uint_as_float(kw[i][k] & 0xFFFF0000u);
-#pragma unroll
-                for (int h = 0; h < 4; ++h)
-                    if (h < G) acc[h] += qs[h][8 * i + 2 * k] * k0 + qs[h][8 * i + 2 * k + 1] * k1;
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < 4; ++h) s[h] = acc[h] * sc;
-    }
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        const float mw = wave_max(s[h]);
-        if (lane == 0) wm[wave][h] = mw;
-    }
-    __syncthreads();
-    float M[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        M[h] = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
-        const float p = (t < W && h < G) ? exp2f(s[h] - M[h]) : 0.0f;
-        ps[h][t] = p;
-        const float lw = wave_sum(p);
-        if (lane == 0) wsum[wave][h] = lw;
-    }
-    wave_lds_sync();
-    // p.v: lane (c, r) takes channels 8c..8c+7 of the wave's tokens 4k + r
-    const int c8 = lane & 15, r = lane >> 4;
-    float o[4][8];
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[h][j] = 0.0f;
-    // tokens at or past W have weight 0; their loads read row W - 1 instead
-    u32x4 w8[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int u = min(64 * wave + 4 * k + r, W - 1);
-        w8[k] = *(const u32x4*)(vr + (size_t)u * kHeadDim + 8 * c8);
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int u = 64 * wave + 4 * k + r;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const float p = ps[h][u];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                o[h][2 * j] += p * __uint_as_float(w8[k][j] << 16);
-                o[h][2 * j + 1] += p * __uint_as_float(w8[k][j] & 0xFFFF0000u);
-            }
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            o[h][j] += __shfl_xor(o[h][j], 16);
-            o[h][j] += __shfl_xor(o[h][j], 32);
-        }
-    if (r == 0) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) wo[wave][h][8 * c8 + j] = o[h][j];
-    }
-    __syncthreads();
-    if (wave < G) {
-        const int h = wave;
-        float o0 = 0.0f, o1 = 0.0f, L = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            o0 += wo[w][h][lane];
-            o1 += wo[w][h][64 + lane];
-            L += wsum[w][h];
-        }
-        fwht128_f32(o0, o1, lane);
-        float* ph = part + (size_t)h * hs;
-        if (lane == 0) { ph[0] = M[h]; ph[1] = L; }
-        ph[4 + lane] = o0;
-        ph[4 + 64 + lane] = o1;
-    }
-}
 
 template <bool PAD_K, bool PAD_V>
 __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
@@ -657,63 +461,6 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     }
 }
 
-// Merge the splits of one (sequence, query head) by log-sum-exp and rotate
-// back: out = H (sum_s acc_s 2^(m_s - M)) / (128 * sum_s l_s 2^(m_s - M)),
-// or, for partials in the original domain (ROTATED false),
-// out = (sum_s acc_s 2^(m_s - M)) / (sum_s l_s 2^(m_s - M)). 4 waves share the splits (wave w takes s = w, w + 4, ...), each lane two
-// channels; the loads of different splits are independent, so many are in
-// flight at once.
-constexpr int kMergeWaves = 4;
-template <bool ROTATED>
-__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __restrict__ partials, int slot_count,
-                                                                 int splits, float* __restrict__ out) {
-    __shared__ float red[kMergeWaves][132];
-    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float* p = partials + (size_t)bh * slot_count * kPartStride;
-    float M = -INFINITY;
-    for (int s = tid; s < splits; s += 64 * kMergeWaves) M = fmaxf(M, p[(size_t)s * kPartStride]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    if (lane == 0) red[wave][0] = M;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, red[w][0]);
-    __syncthreads();
-    float L = 0.0f, v0 = 0.0f, v1 = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll 4
-        for (int s = wave; s < splits; s += kMergeWaves) {
-            const float* ps = p + (size_t)s * kPartStride;
-            const float ms = ps[0];
-            if (ms == -INFINITY) continue;
-            const float f = exp2f(ms - M);
-            L += ps[1] * f;
-            v0 += ps[4 + lane] * f;
-            v1 += ps[4 + 64 + lane] * f;
-        }
-    }
-    red[wave][lane] = v0;
-    red[wave][64 + lane] = v1;
-    if (lane == 0) red[wave][128] = L;
-    __syncthreads();
-    if (wave != 0) return;
-    v0 = 0.0f;
-    v1 = 0.0f;
-    L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) {
-        v0 += red[w][lane];
-        v1 += red[w][64 + lane];
-        L += red[w][128];
-    }
-    const float inv = L > 0.0f ? 1.0f / (ROTATED ? L * (float)kHeadDim : L) : 0.0f;
-    v0 *= inv;
-    v1 *= inv;
-    if (ROTATED) fwht128_f32(v0, v1, lane);
-    out[(size_t)bh * kHeadDim + lane] = v0;
-    out[(size_t)bh * kHeadDim + 64 + lane] = v1;
-}
-
 // Test hook: decode 64 contiguous containers per wave into symbol indices.
 __global__ __launch_bounds__(kThreads) void decode_symbols_kernel(const uint32_t* __restrict__ ent, int p,
                                                                   int C, const uint8_t* __restrict__ in, int n,
@@ -773,8 +520,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
         attr_set[which] = true;
     }
     if (a.win_k) {
-        hipLaunchKernelGGL(window_kernel, dim3(a.num_kv_heads, a.batch), dim3(kThreads), 0, s, a, a.num_splits);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_window(a, a.num_splits, s);
         if (e != hipSuccess) return e;
     }
     dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
@@ -785,17 +531,6 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge(a.partials, a.slot_count, a.merge_slots, a.batch * a.num_q_heads, true, a.out, s);
-}
-
-hipError_t launch_merge(const float* partials, int slot_count, int splits, int rows, bool rotated, float* out,
-                        hipStream_t s) {
-    if (rotated)
-        hipLaunchKernelGGL(merge_kernel<true>, dim3(rows), dim3(64 * kMergeWaves), 0, s, partials, slot_count, splits,
-                           out);
-    else
-        hipLaunchKernelGGL(merge_kernel<false>, dim3(rows), dim3(64 * kMergeWaves), 0, s, partials, slot_count,
-                           splits, out);
-    return hipGetLastError();
 }
 
 hipError_t launch_decode_symbols(const uint32_t* entries, int prob_bits, int levels, int container,

@@ -103,6 +103,8 @@ constexpr int kWindowMax = 256;          // largest bf16 window
 hipError_t launch_encode(const EncArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bf16_attention(const Bf16Args& a, hipStream_t s);
+// Partial of the bf16 window, written to partial slot `slot`.
+hipError_t launch_window(const AttnArgs& a, int slot, hipStream_t s);
 // Log-sum-exp merge of `splits` partials per (sequence, query head) into out;
 // `rotated`: the partials are in the rotated domain (inverse rotation applied).
 hipError_t launch_merge(const float* partials, int slot_count, int splits, int rows, bool rotated, float* out,

@@ -1,0 +1,79 @@
+// Split-K log-sum-exp merge of attention partials (m, l, acc[128]) per
+// (sequence, query head), shared by the compressed and the bf16 kernels.
+#include "dq_internal.h"
+#include "dq_wave.h"
+
+namespace dq {
+namespace {
+
+// Merge the splits of one (sequence, query head) by log-sum-exp and rotate
+// back: out = H (sum_s acc_s 2^(m_s - M)) / (128 * sum_s l_s 2^(m_s - M)),
+// or, for partials in the original domain (ROTATED false),
+// out = (sum_s acc_s 2^(m_s - M)) / (sum_s l_s 2^(m_s - M)). 4 waves share the splits (wave w takes s = w, w + 4, ...), each lane two
+// channels; the loads of different splits are independent, so many are in
+// flight at once.
+constexpr int kMergeWaves = 4;
+template <bool ROTATED>
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __restrict__ partials, int slot_count,
+                                                                 int splits, float* __restrict__ out) {
+    __shared__ float red[kMergeWaves][132];
+    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float* p = partials + (size_t)bh * slot_count * kPartStride;
+    float M = -INFINITY;
+    for (int s = tid; s < splits; s += 64 * kMergeWaves) M = fmaxf(M, p[(size_t)s * kPartStride]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (lane == 0) red[wave][0] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, red[w][0]);
+    __syncthreads();
+    float L = 0.0f, v0 = 0.0f, v1 = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll 4
+        for (int s = wave; s < splits; s += kMergeWaves) {
+            const float* ps = p + (size_t)s * kPartStride;
+            const float ms = ps[0];
+            if (ms == -INFINITY) continue;
+            const float f = exp2f(ms - M);
+            L += ps[1] * f;
+            v0 += ps[4 + lane] * f;
+            v1 += ps[4 + 64 + lane] * f;
+        }
+    }
+    red[wave][lane] = v0;
+    red[wave][64 + lane] = v1;
+    if (lane == 0) red[wave][128] = L;
+    __syncthreads();
+    if (wave != 0) return;
+    v0 = 0.0f;
+    v1 = 0.0f;
+    L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+        v0 += red[w][lane];
+        v1 += red[w][64 + lane];
+        L += red[w][128];
+    }
+    const float inv = L > 0.0f ? 1.0f / (ROTATED ? L * (float)kHeadDim : L) : 0.0f;
+    v0 *= inv;
+    v1 *= inv;
+    if (ROTATED) fwht128_f32(v0, v1, lane);
+    out[(size_t)bh * kHeadDim + lane] = v0;
+    out[(size_t)bh * kHeadDim + 64 + lane] = v1;
+}
+
+}  // namespace
+
+hipError_t launch_merge(const float* partials, int slot_count, int splits, int rows, bool rotated, float* out,
+                        hipStream_t s) {
+    if (rotated)
+        hipLaunchKernelGGL(merge_kernel<true>, dim3(rows), dim3(64 * kMergeWaves), 0, s, partials, slot_count, splits,
+                           out);
+    else
+        hipLaunchKernelGGL(merge_kernel<false>, dim3(rows), dim3(64 * kMergeWaves), 0, s, partials, slot_count,
+                           splits, out);
+    return hipGetLastError();
+}
+
+}  // namespace dq
