@@ -1,9 +1,24 @@
 // Cache write (D-Quant sections 4.1-4.3 and 4.5 "Encoding"): rotation,
-// normalisation, nearest-level quantisation, drift and rANS encoding of one
-// (token, KV head) stream of K or V per wave, bit-exact to the specification:
-// every floating-point decision is an IEEE fp64 operation in a fixed order
-// with no contraction (this file is compiled with -ffp-contract=off).
+// normalisation, nearest-level quantisation, drift and rANS encoding of
+// (token, KV head) streams of K and V, bit-exact to the specification: every
+// floating-point decision is an IEEE fp64 operation in a fixed order with no
+// contraction (this file is compiled with -ffp-contract=off).
+//
+// Work decomposition: a wave takes up to 64 consecutive streams.
+//   1. lane = channel, one stream after another (the next stream's inputs are
+//      already in flight): rotation, norm, nearest level, the drift candidates
+//      and their (key, channel) ranks. What stays in LDS per stream is the
+//      symbol row of the minimal candidate prefix and the channels of the
+//      next candidates in order.
+//   2. lane = stream: the 64 serial rANS encodes run side by side. A stream
+//      whose encoding overflows takes the next candidate and encodes again.
+//   3. lane = stream: a last encode writes each container.
+// A stream that the first drift round cannot fit (no prefix fits, or it needs
+// more extensions than were staged) is redone from scratch by the complete
+// per-stream procedure, which also runs the fallback rounds.
 #include "dq_internal.h"
+
+#include <algorithm>
 
 #pragma clang fp contract(off)
 
@@ -12,6 +27,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kMaxRounds = 64;
+constexpr int kTail = 16;         // candidates staged per stream beyond the minimal prefix
+constexpr int kRow = 132;         // LDS bytes per stream symbol row (an odd number of dwords)
 
 // fp64 -> fp16 bits with a single rounding to nearest even; overflow gives inf.
 __device__ uint16_t f64_to_f16_rne(double d) {
@@ -63,14 +80,24 @@ __device__ __forceinline__ void wave_sync() {
 
 // Per-symbol encode constants of both tables, staged in LDS.
 struct SymConst {
-    uint32_t freq, cum, lim, magic, shift, pad0, pad1, pad2;
+    uint32_t freq, cum, lim, magic, shift, inner, pad0, pad1;
 };
 
-struct WaveLds {
+// One stream's ranking scratch (phase 1 and the per-stream procedure).
+struct Scratch {
     uint64_t key[128];
     int32_t dr[128];
     uint8_t sym[128];
     uint8_t buf[136];
+};
+
+struct WaveLds {
+    Scratch sc;
+    uint8_t sym[64][kRow];        // symbol row of each stream
+    uint8_t ord[64][kTail];       // channels of the staged candidates, in (key, channel) order
+    int32_t kmin[64];             // candidates in the minimal prefix
+    int32_t staged[64];           // staged candidates; -1: redo with the per-stream procedure
+    int32_t meta[64];             // bit 0: over budget before drift; bits 16..31: rho16
 };
 
 // rANS encode of sym[127..0] (section 3.1, Enc) by one lane: before each
@@ -95,54 +122,77 @@ __device__ int rans_encode_lane(const uint8_t* sym, const SymConst* sc, int p, i
     return cnt;
 }
 
-__global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a) {
-    __shared__ WaveLds wl_all[kWaves];
-    __shared__ SymConst sconst[2][16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < 32) {
-        const EncTable* t = a.tables + (tid >> 4);
-        const int m = tid & 15;
-        SymConst c;
-        c.freq = t->freq[m];
-        c.cum = t->cum[m];
-        c.lim = t->renorm_lim[m];
-        c.magic = t->div_magic[m];
-        c.shift = t->div_shift[m];
-        c.pad0 = c.pad1 = c.pad2 = 0;
-        sconst[tid >> 4][m] = c;
+// The same encode, counting bytes only.
+__device__ __forceinline__ int rans_count_lane(const uint8_t* sym, const SymConst* sc, int p, int cap) {
+    uint32_t x = kStateLow;
+    int cnt = 0;
+    for (int i = kHeadDim - 1; i >= 0; --i) {
+        const SymConst c = sc[sym[i]];
+        if (x >= c.lim) {
+            ++cnt;
+            x >>= 8;
+        }
+        const uint32_t q = __umulhi(x, c.magic) >> c.shift;
+        x = x + c.cum + q * ((1u << p) - c.freq);
     }
-    __syncthreads();
+    return cnt <= cap ? cnt : -1;
+}
 
+// The same encode writing the container at dst: the 3-byte state at offset
+// 0, then the cnt emitted bytes in decode order, then zeros up to C.
+__device__ __forceinline__ void rans_write_lane(const uint8_t* sym, const SymConst* sc, int p, int cnt, int C,
+                                                uint8_t* __restrict__ dst) {
+    uint32_t x = kStateLow;
+    int j = kStateBytes + cnt;
+    for (int i = kHeadDim - 1; i >= 0; --i) {
+        const SymConst c = sc[sym[i]];
+        if (x >= c.lim) {
+            dst[--j] = (uint8_t)(x & 255u);
+            x >>= 8;
+        }
+        const uint32_t q = __umulhi(x, c.magic) >> c.shift;
+        x = x + c.cum + q * ((1u << p) - c.freq);
+    }
+    dst[0] = (uint8_t)x;
+    dst[1] = (uint8_t)(x >> 8);
+    dst[2] = (uint8_t)(x >> 16);
+    for (int k = kStateBytes + cnt; k < C; ++k) dst[k] = 0;
+}
+
+struct StreamId {
+    int kv, token, head;
+};
+__device__ __forceinline__ StreamId stream_id(const EncArgs& a, long sid) {
     const long nstreams = (long)a.num_tokens * a.num_kv_heads;
-    const long sid = (long)blockIdx.x * kWaves + wave;
-    if (sid >= 2 * nstreams) return;
-    const int kv = sid >= nstreams ? 1 : 0;
-    const long rem = sid - kv * nstreams;
-    const int token = (int)(rem / a.num_kv_heads), head = (int)(rem % a.num_kv_heads);
-    const int slot = a.slot_mapping[token];
-    if (slot < 0) return;
-    const EncTable* T = a.tables + kv;
-    const SymConst* sc = sconst[kv];
-    WaveLds& W = wl_all[wave];
-    const int M = T->levels, C = T->container, p = T->prob_bits;
-    const int32_t budget = T->budget_fx;
+    StreamId s;
+    s.kv = sid >= nstreams ? 1 : 0;
+    const long rem = sid - s.kv * nstreams;
+    s.token = (int)(rem / a.num_kv_heads);
+    s.head = (int)(rem % a.num_kv_heads);
+    return s;
+}
 
-    // ---- load (exact widening to fp64); lane holds channels lane and lane+64
-    const size_t off = ((size_t)token * a.num_kv_heads + head) * kHeadDim;
-    const void* src = kv ? a.v : a.k;
-    double y0, y1;
+// Inputs of one stream, widened exactly to fp64; lane holds channels lane and lane + 64.
+__device__ __forceinline__ void load_row(const EncArgs& a, const StreamId& s, int lane, double& y0, double& y1) {
+    const size_t off = ((size_t)s.token * a.num_kv_heads + s.head) * kHeadDim;
+    const void* src = s.kv ? a.v : a.k;
     if (a.dtype == DQ_DTYPE_BF16) {
-        const uint16_t* s = (const uint16_t*)src + off;
-        y0 = (double)__uint_as_float((uint32_t)s[lane] << 16);
-        y1 = (double)__uint_as_float((uint32_t)s[lane + 64] << 16);
+        const uint16_t* p = (const uint16_t*)src + off;
+        y0 = (double)__uint_as_float((uint32_t)p[lane] << 16);
+        y1 = (double)__uint_as_float((uint32_t)p[lane + 64] << 16);
     } else {
-        const float* s = (const float*)src + off;
-        y0 = (double)s[lane];
-        y1 = (double)s[lane + 64];
+        const float* p = (const float*)src + off;
+        y0 = (double)p[lane];
+        y1 = (double)p[lane + 64];
     }
+}
 
-    // ---- rotation y = H x (Sylvester, entries +-1): butterflies of span 1, 2, ..., 64,
-    // (a, b) -> (a + b, a - b) for the pair (i, i + h), i mod 2h < h
+// Rotation y = H x (Sylvester, entries +-1): butterflies of span 1, 2, ..., 64,
+// (a, b) -> (a + b, a - b) for the pair (i, i + h), i mod 2h < h; then the norm
+// S by the fixed tree s_j += s_{j+w}, w = 64, 32, ..., 1, rho = sqrt(S / 128),
+// rho16 rounded once, and the unit-RMS values z = y / rho.
+__device__ __forceinline__ void rotate_normalise(double y0, double y1, int lane, double& z0, double& z1,
+                                                 uint16_t& rho16) {
 #pragma unroll
     for (int h = 1; h < 64; h <<= 1) {
         const double p0 = __shfl_xor(y0, h), p1 = __shfl_xor(y1, h);
@@ -155,8 +205,6 @@ __global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a) {
         y0 = u + v;
         y1 = u - v;
     }
-
-    // ---- norm: S by the fixed tree s_j += s_{j+w}, w = 64, 32, ..., 1
     double s = y0 * y0;
     {
         const double s1 = y1 * y1;
@@ -169,29 +217,96 @@ __global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a) {
     }
     const double S = __shfl(s, 0);
     const double rho = dq_sqrt(S / 128.0);
-    const uint16_t rho16 = f64_to_f16_rne(rho);
-    double z0 = 0.0, z1 = 0.0;
+    rho16 = f64_to_f16_rne(rho);
+    z0 = 0.0;
+    z1 = 0.0;
     if (S > 0.0) {
         z0 = y0 / rho;
         z1 = y1 / rho;
     }
+}
 
-    // ---- nearest level; an exact midpoint goes to the inner level
-    int m0 = 0, m1 = 0;
+// Nearest level; an exact midpoint goes to the inner level.
+__device__ __forceinline__ int nearest_level(double z, const EncTable* T, int M) {
+    int m = 0;
     for (int j = 0; j + 1 < M; ++j) {
         const double bj = T->bounds[j];
-        if (bj >= 0.0) {
-            m0 += z0 > bj;
-            m1 += z1 > bj;
-        } else {
-            m0 += z0 >= bj;
-            m1 += z1 >= bj;
-        }
+        if (bj >= 0.0) m += z > bj;
+        else m += z >= bj;
     }
+    return m;
+}
+
+// The drift candidates of the current symbols m0, m1 (one level inward and
+// strictly cheaper, section 4.3) with their keys dd / dr, compacted into W in
+// channel order; then each candidate's rank in (key, channel) order and the
+// rate removed by every candidate ahead of it.
+struct Cands {
+    int i0, i1, dr0, dr1, rank0, rank1, cb0, cb1, pos0, pos1, nc, tot;
+    bool c0, c1;
+};
+__device__ __forceinline__ Cands rank_candidates(const EncTable* T, double z0, double z1, int m0, int m1,
+                                                 int lane, Scratch& W) {
+    Cands r;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    r.i0 = T->inner[m0];
+    r.i1 = T->inner[m1];
+    r.dr0 = r.i0 >= 0 ? T->cost[m0] - T->cost[r.i0] : 0;
+    r.dr1 = r.i1 >= 0 ? T->cost[m1] - T->cost[r.i1] : 0;
+    r.c0 = r.i0 >= 0 && r.dr0 > 0;
+    r.c1 = r.i1 >= 0 && r.dr1 > 0;
+    uint64_t k0 = 0, k1 = 0;
+    if (r.c0) {
+        const double a0 = z0 - T->recon[r.i0], b0 = z0 - T->recon[m0];
+        const double dd = a0 * a0 - b0 * b0;
+        k0 = order_key(dd / (double)r.dr0);
+    }
+    if (r.c1) {
+        const double a1 = z1 - T->recon[r.i1], b1 = z1 - T->recon[m1];
+        const double dd = a1 * a1 - b1 * b1;
+        k1 = order_key(dd / (double)r.dr1);
+    }
+    const uint64_t bal0 = __ballot(r.c0), bal1 = __ballot(r.c1);
+    r.pos0 = __popcll(bal0 & lt_mask);
+    r.pos1 = __popcll(bal0) + __popcll(bal1 & lt_mask);
+    r.nc = __popcll(bal0) + __popcll(bal1);
+    if (r.c0) { W.key[r.pos0] = k0; W.dr[r.pos0] = r.dr0; }
+    if (r.c1) { W.key[r.pos1] = k1; W.dr[r.pos1] = r.dr1; }
+    wave_sync();
+    r.rank0 = 0; r.rank1 = 0; r.cb0 = 0; r.cb1 = 0; r.tot = 0;
+    for (int j = 0; j < r.nc; ++j) {
+        const uint64_t kj = W.key[j];
+        const int dj = W.dr[j];
+        r.tot += dj;
+        const bool a0 = kj < k0 || (kj == k0 && j < r.pos0);
+        const bool a1 = kj < k1 || (kj == k1 && j < r.pos1);
+        r.rank0 += a0;
+        r.cb0 += a0 ? dj : 0;
+        r.rank1 += a1;
+        r.cb1 += a1 ? dj : 0;
+    }
+    wave_sync();
+    return r;
+}
+
+// The complete per-stream procedure (one wave, lane = channel), including the
+// fallback rounds: for the streams the batched path hands back.
+__device__ void encode_one(const EncArgs& a, long sid, int lane, Scratch& W, const SymConst (*sconst)[16]) {
+    const StreamId id = stream_id(a, sid);
+    const int slot = a.slot_mapping[id.token];
+    if (slot < 0) return;
+    const EncTable* T = a.tables + id.kv;
+    const SymConst* sc = sconst[id.kv];
+    const int M = T->levels, C = T->container, p = T->prob_bits;
+    const int32_t budget = T->budget_fx;
+    double y0, y1, z0, z1;
+    uint16_t rho16;
+    load_row(a, id, lane, y0, y1);
+    rotate_normalise(y0, y1, lane, z0, z1, rho16);
+    int m0 = nearest_level(z0, T, M), m1 = nearest_level(z1, T, M);
     const int n0 = m0, n1 = m1;
     int R = wave_sum_i(T->cost[m0] + T->cost[m1]);
 
-    const uint64_t lt_mask = (1ull << lane) - 1ull;
     int rounds = 0;
     bool done = false, failed = false;
     uint32_t state = 0;
@@ -216,51 +331,14 @@ __global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a) {
 
     while (!done) {
         if (++rounds > kMaxRounds) { failed = true; break; }
-        // candidates: one level inward and strictly cheaper (section 4.3)
-        const int i0 = T->inner[m0], i1 = T->inner[m1];
-        const int dr0 = i0 >= 0 ? T->cost[m0] - T->cost[i0] : 0;
-        const int dr1 = i1 >= 0 ? T->cost[m1] - T->cost[i1] : 0;
-        const bool c0 = i0 >= 0 && dr0 > 0, c1 = i1 >= 0 && dr1 > 0;
-        uint64_t k0 = 0, k1 = 0;
-        if (c0) {
-            const double a0 = z0 - T->recon[i0], b0 = z0 - T->recon[m0];
-            const double dd = a0 * a0 - b0 * b0;
-            k0 = order_key(dd / (double)dr0);
-        }
-        if (c1) {
-            const double a1 = z1 - T->recon[i1], b1 = z1 - T->recon[m1];
-            const double dd = a1 * a1 - b1 * b1;
-            k1 = order_key(dd / (double)dr1);
-        }
-        // compact the candidates in channel order
-        const uint64_t bal0 = __ballot(c0), bal1 = __ballot(c1);
-        const int pos0 = __popcll(bal0 & lt_mask);
-        const int pos1 = __popcll(bal0) + __popcll(bal1 & lt_mask);
-        const int nc = __popcll(bal0) + __popcll(bal1);
-        if (c0) { W.key[pos0] = k0; W.dr[pos0] = dr0; }
-        if (c1) { W.key[pos1] = k1; W.dr[pos1] = dr1; }
-        wave_sync();
-        // rank and the rate removed by every candidate ahead of this one in (key, channel) order
-        int rank0 = 0, rank1 = 0, cb0 = 0, cb1 = 0, tot = 0;
-        for (int j = 0; j < nc; ++j) {
-            const uint64_t kj = W.key[j];
-            const int dj = W.dr[j];
-            tot += dj;
-            const bool a0 = kj < k0 || (kj == k0 && j < pos0);
-            const bool a1 = kj < k1 || (kj == k1 && j < pos1);
-            rank0 += a0;
-            cb0 += a0 ? dj : 0;
-            rank1 += a1;
-            cb1 += a1 ? dj : 0;
-        }
-        wave_sync();
+        const Cands c = rank_candidates(T, z0, z1, m0, m1, lane, W);
         const int need = R - budget;
-        if (tot >= need) {
+        if (c.tot >= need) {
             int kmin = 0;
-            if (need > 0) kmin = __popcll(__ballot(c0 && cb0 < need)) + __popcll(__ballot(c1 && cb1 < need));
-            for (int k = kmin; k <= nc; ++k) {
-                const int s0 = (c0 && rank0 < k) ? i0 : m0;
-                const int s1 = (c1 && rank1 < k) ? i1 : m1;
+            if (need > 0) kmin = __popcll(__ballot(c.c0 && c.cb0 < need)) + __popcll(__ballot(c.c1 && c.cb1 < need));
+            for (int k = kmin; k <= c.nc; ++k) {
+                const int s0 = (c.c0 && c.rank0 < k) ? c.i0 : m0;
+                const int s1 = (c.c1 && c.rank1 < k) ? c.i1 : m1;
                 W.sym[lane] = (uint8_t)s0;
                 W.sym[lane + 64] = (uint8_t)s1;
                 wave_sync();
@@ -280,18 +358,18 @@ __global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a) {
             }
         }
         if (!done) {
-            if (nc == 0) { failed = true; break; }
+            if (c.nc == 0) { failed = true; break; }
             // fallback round: every candidate moves, and drift starts again from there
-            m0 = c0 ? i0 : m0;
-            m1 = c1 ? i1 : m1;
+            m0 = c.c0 ? c.i0 : m0;
+            m1 = c.c1 ? c.i1 : m1;
             R = wave_sum_i(T->cost[m0] + T->cost[m1]);
         }
     }
 
     // ---- store: [state, 3 bytes LE][bytes in decode order][zeros]
     const int page = slot / a.page_size, po = slot - page * a.page_size;
-    const size_t idx = ((size_t)page * a.num_kv_heads + head) * a.page_size + po;
-    uint8_t* dst = a.cache[kv] + idx * C;
+    const size_t idx = ((size_t)page * a.num_kv_heads + id.head) * a.page_size + po;
+    uint8_t* dst = a.cache[id.kv] + idx * C;
     for (int j = lane; j < C; j += 64) {
         uint8_t v = 0;
         if (!failed) {
@@ -302,11 +380,122 @@ __global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a) {
     }
     const int changed = wave_sum_i((m0 != n0) + (m1 != n1));
     if (lane == 0) {
-        a.norm[kv][idx] = rho16;
+        a.norm[id.kv][idx] = rho16;
         if (a.drift_stats)
-            a.drift_stats[((size_t)token * a.num_kv_heads + head) * 2 + kv] =
+            a.drift_stats[((size_t)id.token * a.num_kv_heads + id.head) * 2 + id.kv] =
                 (uint16_t)((changed & 255) | ((rounds > 255 ? 255 : rounds) << 8));
         if (failed && a.err_word) atomicOr(a.err_word, DQ_DEVERR_ENCODE);
+    }
+}
+
+__global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a, int per_wave) {
+    __shared__ WaveLds wl_all[kWaves];
+    __shared__ SymConst sconst[2][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < 32) {
+        const EncTable* t = a.tables + (tid >> 4);
+        const int m = tid & 15;
+        SymConst c;
+        c.freq = t->freq[m];
+        c.cum = t->cum[m];
+        c.lim = t->renorm_lim[m];
+        c.magic = t->div_magic[m];
+        c.shift = t->div_shift[m];
+        c.inner = (uint32_t)t->inner[m];
+        c.pad0 = c.pad1 = 0;
+        sconst[tid >> 4][m] = c;
+    }
+    __syncthreads();
+
+    WaveLds& W = wl_all[wave];
+    const long total = 2l * a.num_tokens * a.num_kv_heads;
+    const long sid0 = ((long)blockIdx.x * kWaves + wave) * per_wave;
+    if (sid0 >= total) return;
+    const int nb = (int)min((long)per_wave, total - sid0);   // streams of this wave, <= 64
+
+    // ---- phase 1: lane = channel, one stream at a time
+    int slot_n = -1;
+    double y0n = 0.0, y1n = 0.0;
+    StreamId idn = stream_id(a, sid0);
+    slot_n = a.slot_mapping[idn.token];
+    if (slot_n >= 0) load_row(a, idn, lane, y0n, y1n);
+    for (int s = 0; s < nb; ++s) {
+        const StreamId id = idn;
+        const int slot = slot_n;
+        const double y0 = y0n, y1 = y1n;
+        if (s + 1 < nb) {   // the next stream's inputs go out before this one's work
+            idn = stream_id(a, sid0 + s + 1);
+            slot_n = a.slot_mapping[idn.token];
+            if (slot_n >= 0) load_row(a, idn, lane, y0n, y1n);
+        }
+        if (slot < 0) {
+            if (lane == 0) W.staged[s] = -2;   // no slot: nothing is written
+            continue;
+        }
+        const EncTable* T = a.tables + id.kv;
+        const int M = T->levels;
+        double z0, z1;
+        uint16_t rho16;
+        rotate_normalise(y0, y1, lane, z0, z1, rho16);
+        const int m0 = nearest_level(z0, T, M), m1 = nearest_level(z1, T, M);
+        const int R = wave_sum_i(T->cost[m0] + T->cost[m1]);
+        const Cands c = rank_candidates(T, z0, z1, m0, m1, lane, W.sc);
+        const int need = R - T->budget_fx;
+        int kmin = 0;
+        if (need > 0) kmin = __popcll(__ballot(c.c0 && c.cb0 < need)) + __popcll(__ballot(c.c1 && c.cb1 < need));
+        W.sym[s][lane] = (uint8_t)((c.c0 && c.rank0 < kmin) ? c.i0 : m0);
+        W.sym[s][lane + 64] = (uint8_t)((c.c1 && c.rank1 < kmin) ? c.i1 : m1);
+        if (c.c0 && c.rank0 >= kmin && c.rank0 < kmin + kTail) W.ord[s][c.rank0 - kmin] = (uint8_t)lane;
+        if (c.c1 && c.rank1 >= kmin && c.rank1 < kmin + kTail) W.ord[s][c.rank1 - kmin] = (uint8_t)(lane + 64);
+        if (lane == 0) {
+            // a prefix must remove the excess rate; otherwise the per-stream procedure takes over
+            const bool fits = need <= 0 || c.tot >= need;
+            W.kmin[s] = kmin;
+            W.staged[s] = fits ? min(c.nc - kmin, kTail) : -1;
+            W.meta[s] = (need > 0 ? 1 : 0) | ((int)rho16 << 16) | (c.nc - kmin > kTail ? 2 : 0);
+        }
+    }
+    wave_sync();
+
+    // ---- phases 2 and 3: lane = stream
+    bool slow = false;
+    if (lane < nb && W.staged[lane] >= 0) {
+        const StreamId id = stream_id(a, sid0 + lane);
+        const EncTable* T = a.tables + id.kv;
+        const SymConst* sc = sconst[id.kv];
+        const int C = T->container, p = T->prob_bits;
+        uint8_t* row = W.sym[lane];
+        const int staged = W.staged[lane];
+        int used = 0, cnt;
+        while ((cnt = rans_count_lane(row, sc, p, C - kStateBytes)) < 0 && used < staged) {
+            const int ch = W.ord[lane][used++];   // the next candidate moves one level inward
+            row[ch] = (uint8_t)sc[row[ch]].inner;
+        }
+        if (cnt < 0) {
+            slow = true;   // the staged candidates did not suffice
+        } else {
+            const int slot = a.slot_mapping[id.token];
+            const int page = slot / a.page_size, po = slot - page * a.page_size;
+            const size_t idx = ((size_t)page * a.num_kv_heads + id.head) * a.page_size + po;
+            rans_write_lane(row, sc, p, cnt, C, a.cache[id.kv] + idx * C);
+            const int meta = W.meta[lane];
+            a.norm[id.kv][idx] = (uint16_t)((uint32_t)meta >> 16);
+            if (a.drift_stats) {
+                const int k = W.kmin[lane] + used;
+                const int rounds = ((meta & 1) || k > 0) ? 1 : 0;
+                a.drift_stats[((size_t)id.token * a.num_kv_heads + id.head) * 2 + id.kv] =
+                    (uint16_t)((k & 255) | (rounds << 8));
+            }
+        }
+    } else if (lane < nb && W.staged[lane] == -1) {
+        slow = true;
+    }
+    // streams handed back: the complete per-stream procedure, from scratch
+    uint64_t back = __ballot(slow);
+    while (back) {
+        const int s = __ffsll((long long)back) - 1;
+        back &= back - 1;
+        encode_one(a, sid0 + s, lane, W.sc, sconst);
     }
 }
 
@@ -322,10 +511,16 @@ __global__ void selftest_kernel(const double* __restrict__ a, const double* __re
 
 }  // namespace
 
+// Streams per wave: 64 (one per lane in the serial phase) for large writes;
+// fewer when that would leave the chip short of waves (about 3072 fit at
+// once: 256 CUs x 12), since a wave walks its streams one at a time first.
 hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
     const long streams = 2l * a.num_tokens * a.num_kv_heads;
-    dim3 grid((unsigned)((streams + kWaves - 1) / kWaves));
-    hipLaunchKernelGGL(encode_kernel, grid, dim3(64 * kWaves), 0, s, a);
+    const long waves_wanted = 3072;
+    const int per_wave = (int)std::min(64l, std::max(1l, (streams + waves_wanted - 1) / waves_wanted));
+    const long per_block = (long)per_wave * kWaves;
+    dim3 grid((unsigned)((streams + per_block - 1) / per_block));
+    hipLaunchKernelGGL(encode_kernel, grid, dim3(64 * kWaves), 0, s, a, per_wave);
     return hipGetLastError();
 }
 
