@@ -260,6 +260,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=0,
                     help="counter collection only: build and run this many layer caches (marked in the output)")
+    ap.add_argument("--section", choices=["encode", "bf16"], default=None,
+                    help="profiling only: run just this measurement and print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -279,6 +281,14 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return 0
+
+    if args.section == "encode":
+        print(json.dumps({"encode": encode_measurement(dq, torch, workloads)}), flush=True)
+        return 0
+    if args.section == "bf16":
+        print(json.dumps({"bf16_reference": bf16_measurement(dq, torch, workloads, args.workload, copies=2,
+                                                             dq_us=float("nan"))}), flush=True)
         return 0
 
     w = workloads.WORKLOADS[args.workload]
