@@ -16,6 +16,7 @@ Modules
   codec      O2-O10  rotation, normalisation, quantisation, drift, rANS
              encode/decode, reconstruction (sections 3.1, 4.1-4.3)
   attention  O11  fp64 GQA decode attention over reconstructed K/V
+  means      O12  windowed INT8 channel-mean removal for keys (sections 3.2, 5)
   measures   entropy, cross-entropy, coding gain, normal gap, NMSE (section 3.1/3.2)
 
 Parity status: every function is pinned by the tests in ``tests/`` against
@@ -28,6 +29,7 @@ from .tables import (Table, make_table, default_step, FLUSH_BITS, STATE_LOW, STA
 from .codec import (fwht, normalize, nearest_level, drift_candidates, rans_encode, rans_enc_step, rans_dec_step,
                     rans_decode, encode_streams, decode_streams, reconstruct, EncodeResult)
 from .attention import attention, attention_rotated
+from .means import block_means, dequantize as dequantize_means, BLOCK as MEAN_BLOCK
 from . import measures
 
 __all__ = [
@@ -35,5 +37,5 @@ __all__ = [
     "fwht", "normalize", "nearest_level", "drift_candidates", "rans_encode", "rans_decode",
     "rans_enc_step", "rans_dec_step",
     "encode_streams", "decode_streams", "reconstruct", "EncodeResult",
-    "attention", "attention_rotated", "measures",
+    "attention", "attention_rotated", "measures", "block_means", "dequantize_means", "MEAN_BLOCK",
 ]

@@ -270,9 +270,11 @@ def _apply_prefix(m, order, inner_of_level, k):
     return out
 
 
-def encode_streams(x: np.ndarray, table: Table) -> EncodeResult:
+def encode_streams(x: np.ndarray, table: Table, mean_rot: np.ndarray | None = None) -> EncodeResult:
     """Encode rows x [S, 128] (values exactly representable in fp64) into
-    fixed C-byte containers plus an fp16 norm each.
+    fixed C-byte containers plus an fp16 norm each. With ``mean_rot`` [S, 128]
+    (a key block's dequantised channel mean, O12) the rotated row minus that
+    mean is what gets normalised and coded.
 
     Steps, per stream: y = H x (O2); S, rho, rho16, z (O3); nearest level (O4);
     R = sum of costs and B_fx = (8C - sigma) * 2^16 (O5). Then drift rounds
@@ -287,6 +289,8 @@ def encode_streams(x: np.ndarray, table: Table) -> EncodeResult:
     S, n = x.shape
     C = table.container
     y = fwht(x)
+    if mean_rot is not None:
+        y = y - np.asarray(mean_rot, dtype=np.float64)
     rho, rho16, z = normalize(y)
     nearest = nearest_level(z, table)
 
@@ -359,11 +363,16 @@ def decode_streams(containers: np.ndarray, table: Table, n: int = HEAD_DIM):
     return sym, ok
 
 
-def reconstruct(symbols: np.ndarray, rho16: np.ndarray, table: Table) -> np.ndarray:
-    """O10: x_hat = H (rho16 * level(m)) / 128, back in the original domain.
+def reconstruct(symbols: np.ndarray, rho16: np.ndarray, table: Table,
+                mean_rot: np.ndarray | None = None) -> np.ndarray:
+    """O10: x_hat = H (rho16 * level(m) [+ mean_rot]) / 128, back in the
+    original domain.
 
-    rho16 * level(m) approximates y = H x (the unnormalised rotation); since
+    rho16 * level(m) approximates y = H x (the unnormalised rotation), or
+    y minus a key block's channel mean (O12), which is then added back; since
     H H = 128 I the inverse rotation is H / 128.
     """
     yhat = np.asarray(rho16, dtype=np.float64)[..., None] * table.recon[symbols]
+    if mean_rot is not None:
+        yhat = yhat + np.asarray(mean_rot, dtype=np.float64)
     return fwht(yhat) / yhat.shape[-1]
