@@ -290,10 +290,11 @@ int dq_tables_info(const dq_tables* t, int which, dq_table_info* out) {
     return DQ_OK;
 }
 
-int dq_encode_kv(const dq_tables* t, const void* k, const void* v, int dtype, int num_tokens,
-                 int num_kv_heads, int page_size, const int32_t* slot_mapping, uint8_t* k_cache,
-                 uint8_t* v_cache, uint16_t* k_norm, uint16_t* v_norm, uint16_t* drift_stats,
-                 uint32_t* err_word, void* stream) {
+namespace {
+int encode_impl(const dq_tables* t, const void* k, const void* v, int dtype, int num_tokens, int num_kv_heads,
+                int page_size, const int32_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache, uint16_t* k_norm,
+                uint16_t* v_norm, int8_t* k_mean, uint16_t* k_mean_scale, uint16_t* drift_stats, uint32_t* err_word,
+                void* stream) {
     if (!t || num_tokens < 0 || num_kv_heads <= 0 || page_size <= 0 || page_size % 16)
         return DQ_ERR_INVALID_ARG;
     if (dtype != DQ_DTYPE_F32 && dtype != DQ_DTYPE_BF16) return DQ_ERR_INVALID_ARG;
@@ -316,8 +317,30 @@ int dq_encode_kv(const dq_tables* t, const void* k, const void* v, int dtype, in
     a.drift_stats = drift_stats;
     a.err_word = err_word;
     a.tables = t->d_enc;
+    a.k_mean = k_mean;
+    a.k_mean_scale = k_mean_scale;
     hipError_t e = dq::launch_encode(a, (hipStream_t)stream);
     return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+}  // namespace
+
+int dq_encode_kv(const dq_tables* t, const void* k, const void* v, int dtype, int num_tokens,
+                 int num_kv_heads, int page_size, const int32_t* slot_mapping, uint8_t* k_cache,
+                 uint8_t* v_cache, uint16_t* k_norm, uint16_t* v_norm, uint16_t* drift_stats,
+                 uint32_t* err_word, void* stream) {
+    return encode_impl(t, k, v, dtype, num_tokens, num_kv_heads, page_size, slot_mapping, k_cache, v_cache, k_norm,
+                       v_norm, nullptr, nullptr, drift_stats, err_word, stream);
+}
+
+int dq_encode_kv_blocks(const dq_tables* t, const void* k, const void* v, int dtype, int num_blocks,
+                        int num_kv_heads, int page_size, const int32_t* slot_mapping, uint8_t* k_cache,
+                        uint8_t* v_cache, uint16_t* k_norm, uint16_t* v_norm, int8_t* k_mean,
+                        uint16_t* k_mean_scale, uint16_t* drift_stats, uint32_t* err_word, void* stream) {
+    if (!k_mean || !k_mean_scale || num_blocks < 0 || (long)num_blocks * dq::kMeanBlock > INT32_MAX)
+        return DQ_ERR_INVALID_ARG;
+    if (page_size > 0 && (page_size & (page_size - 1))) return DQ_ERR_UNSUPPORTED;
+    return encode_impl(t, k, v, dtype, num_blocks * dq::kMeanBlock, num_kv_heads, page_size, slot_mapping, k_cache,
+                       v_cache, k_norm, v_norm, k_mean, k_mean_scale, drift_stats, err_word, stream);
 }
 
 size_t dq_workspace_size(int batch, int num_q_heads, int num_kv_heads, int max_context, int num_splits) {
@@ -333,7 +356,8 @@ static int decode_attention_impl(const dq_tables* t, const void* q, int q_dtype,
                                  const int32_t* block_table, const int32_t* context_lens, int batch,
                                  int num_q_heads, int num_kv_heads, int max_pages_per_seq, int page_size,
                                  int max_context, float softmax_scale, int num_splits, const uint16_t* window_k,
-                                 const uint16_t* window_v, const int32_t* window_lens, int window_cap, float* out,
+                                 const uint16_t* window_v, const int32_t* window_lens, int window_cap,
+                                 const int8_t* k_mean, const uint16_t* k_mean_scale, float* out,
                                  void* workspace, size_t workspace_bytes, uint32_t* err_word, void* stream) {
     if (!t || !q || !k_cache || !v_cache || !k_norm || !v_norm || !block_table || !context_lens ||
         !out || !workspace)
@@ -351,6 +375,7 @@ static int decode_attention_impl(const dq_tables* t, const void* q, int q_dtype,
             return DQ_ERR_INVALID_ARG;
         if (window_cap > dq::kWindowMax) return DQ_ERR_UNSUPPORTED;
     }
+    if ((k_mean == nullptr) != (k_mean_scale == nullptr)) return DQ_ERR_INVALID_ARG;
     int splits = num_splits ? num_splits : dq::choose_splits(batch, num_kv_heads, max_context);
     if (workspace_bytes < dq_workspace_size(batch, num_q_heads, num_kv_heads, max_context, splits))
         return DQ_ERR_WORKSPACE;
@@ -378,6 +403,8 @@ static int decode_attention_impl(const dq_tables* t, const void* q, int q_dtype,
     a.win_v = window_v;
     a.win_lens = window_lens;
     a.win_cap = win ? window_cap : 0;
+    a.k_mean = k_mean;
+    a.k_mean_scale = k_mean_scale;
     a.ck = t->info[0].container;
     a.cv = t->info[1].container;
     a.pk = t->info[0].prob_bits;
@@ -401,8 +428,8 @@ int dq_decode_attention(const dq_tables* t, const void* q, int q_dtype, const ui
                         void* workspace, size_t workspace_bytes, uint32_t* err_word, void* stream) {
     return decode_attention_impl(t, q, q_dtype, k_cache, v_cache, k_norm, v_norm, block_table, context_lens,
                                  batch, num_q_heads, num_kv_heads, max_pages_per_seq, page_size, max_context,
-                                 softmax_scale, num_splits, nullptr, nullptr, nullptr, 0, out, workspace,
-                                 workspace_bytes, err_word, stream);
+                                 softmax_scale, num_splits, nullptr, nullptr, nullptr, 0, nullptr, nullptr, out,
+                                 workspace, workspace_bytes, err_word, stream);
 }
 
 int dq_bf16_decode_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
@@ -456,8 +483,26 @@ int dq_decode_attention_window(const dq_tables* t, const void* q, int q_dtype, c
     if (!window_k) return DQ_ERR_INVALID_ARG;
     return decode_attention_impl(t, q, q_dtype, k_cache, v_cache, k_norm, v_norm, block_table, context_lens,
                                  batch, num_q_heads, num_kv_heads, max_pages_per_seq, page_size, max_context,
-                                 softmax_scale, num_splits, window_k, window_v, window_lens, window_cap, out,
-                                 workspace, workspace_bytes, err_word, stream);
+                                 softmax_scale, num_splits, window_k, window_v, window_lens, window_cap, nullptr,
+                                 nullptr, out, workspace, workspace_bytes, err_word, stream);
+}
+
+int dq_decode_attention_ext(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
+                            const uint8_t* v_cache, const uint16_t* k_norm, const uint16_t* v_norm,
+                            const int32_t* block_table, const int32_t* context_lens, int batch,
+                            int num_q_heads, int num_kv_heads, int max_pages_per_seq, int page_size,
+                            int max_context, float softmax_scale, int num_splits, const dq_attention_extras* ex,
+                            float* out, void* workspace, size_t workspace_bytes, uint32_t* err_word,
+                            void* stream) {
+    dq_attention_extras none;
+    memset(&none, 0, sizeof(none));
+    if (!ex) ex = &none;
+    if (ex->window_k && !ex->window_v) return DQ_ERR_INVALID_ARG;
+    return decode_attention_impl(t, q, q_dtype, k_cache, v_cache, k_norm, v_norm, block_table, context_lens,
+                                 batch, num_q_heads, num_kv_heads, max_pages_per_seq, page_size, max_context,
+                                 softmax_scale, num_splits, ex->window_k, ex->window_v, ex->window_lens,
+                                 ex->window_cap, ex->k_mean, ex->k_mean_scale, out, workspace, workspace_bytes,
+                                 err_word, stream);
 }
 
 int dq_decode_symbols(const dq_tables* t, int which, const uint8_t* containers, int n_streams,

@@ -289,13 +289,13 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     // tiles, rarely. Value norms enter the p.v weights scaled by a running
     // power of two 2^-e_run (moved on the same condition) so that the fp16
     // weights w * |v| 2^-e_run stay below 2^(kSlack + 1).
-    auto softmax = [&](const float4v& d, bool valid, float rk, float rv) {
+    auto softmax = [&](const float4v& d, bool valid, float rk, float rv, const float* cm) {
         constexpr float kSlack = 8.0f;
         float sv[4];
         bool up = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            sv[r] = valid ? d[r] * rk * kap[r] : -INFINITY;
+            sv[r] = valid ? d[r] * rk * kap[r] + cm[r] : -INFINITY;
             up |= r < G && sv[r] > m_run[r] + kSlack;
         }
         const int ev = valid && rv > 0.0f ? f32_exponent(rv) : -127;
@@ -331,6 +331,27 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         }
     };
 
+    // The key block mean's share of the tile's logits (sections 3.2, 5): the
+    // block's INT8 channel means times its scale, dotted with the rotated query,
+    // in the log2 logit scale; uniform over the tile (a 64-token tile lies in
+    // one 128-token block).
+    auto mean_terms = [&](int t0, float* cm) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cm[r] = 0.0f;
+        if (!a.k_mean) return;
+        const int tb = t0 & ~(kMeanBlock - 1);
+        const int page = bt_row[tb >> log2p];
+        const size_t mrow = ((size_t)page * hkv + g) * (size_t)mean_rows_per_page(P) + (size_t)((tb & (P - 1)) >> 7);
+        const float s16 = f16_to_f32(a.k_mean_scale[mrow]);
+        const float m0 = (float)a.k_mean[mrow * kHeadDim + lane], m1 = (float)a.k_mean[mrow * kHeadDim + 64 + lane];
+        const _Float16* qt = (const _Float16*)(lds + kOffQt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (r < G)
+                cm[r] = wave_sum_uniform((float)qt[r * kHeadDim + lane] * m0 + (float)qt[r * kHeadDim + 64 + lane] * m1) *
+                        s16 * (kap[r] / a.step_k);
+    };
+
     // norms of the lane's token: row of its 16-token group plus its place in the group
     auto load_norms = [&](int t0, const size_t* row, float& rk, float& rv) {
         const int gl = lane >> 4;
@@ -354,8 +375,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         tile_rows(row, bt_row, log2p, P, hkv, g, t, T);
         stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
         stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, row, lane);
-        float rk, rv;
+        float rk, rv, cm[4];
         load_norms(t, row, rk, rv);
+        mean_terms(t, cm);
         wave_lds_sync();
         const bool valid = t + lane < T;
         RansLane kr;
@@ -383,19 +405,20 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
             dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, __builtin_bit_cast(half8, bw), dk, 0, 0, 0);
         }
         bad |= (valid && (kr.x != kStateLow || rans_consumed(kr, kabs) > (uint32_t)a.ck)) ? 1u : 0u;
-        softmax(dk, valid, rk, rv);
+        softmax(dk, valid, rk, rv, cm);
     }
     for (; t < end; t += kStep) {
         // values of tile t, interleaved with the keys of tile t + kStep
         const int tn = t + kStep;
         const bool has_next = tn < end;
         const bool valid = t + lane < T, valid_n = tn + lane < T;
-        float rk_n = 0.0f, rv_n = 0.0f;
+        float rk_n = 0.0f, rv_n = 0.0f, cm_n[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (has_next) {
             size_t row[4];
             tile_rows(row, bt_row, log2p, P, hkv, g, tn, T);
             stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
             load_norms(tn, row, rk_n, rv_n);
+            mean_terms(tn, cm_n);
         }
         wave_lds_sync();
         RansLane vr, kr;
@@ -413,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         }
         bad |= (valid && (vr.x != kStateLow || rans_consumed(vr, vabs) > (uint32_t)a.cv)) ? 1u : 0u;
         if (has_next) {
-            softmax(dk, valid_n, rk_n, rv_n);
+            softmax(dk, valid_n, rk_n, rv_n, cm_n);
             wave_lds_sync();
             size_t row[4];   // recomputed (scalar loads) rather than held through the pass
             tile_rows(row, bt_row, log2p, P, hkv, g, tn, T);

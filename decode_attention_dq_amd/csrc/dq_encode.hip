@@ -187,12 +187,43 @@ __device__ __forceinline__ void load_row(const EncArgs& a, const StreamId& s, in
     }
 }
 
+// Key channel-mean removal (sections 3.2 and 5): the mean row of the
+// 128-token block that starts at call token `first`, found from that token's
+// slot; false when the slot is missing or not where a block starts.
+__device__ __forceinline__ bool mean_row(const EncArgs& a, int first, int head, size_t& row) {
+    const int slot = a.slot_mapping[first];
+    if (slot < 0) return false;
+    const int P = a.page_size, page = slot / P, off = slot - page * P;
+    if (off % (P < kMeanBlock ? P : kMeanBlock) != 0) return false;
+    row = ((size_t)page * a.num_kv_heads + head) * (size_t)mean_rows_per_page(P) + (size_t)(off / kMeanBlock);
+    return true;
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
+    _Float16 v;
+    __builtin_memcpy(&v, &h, 2);
+    return (double)(float)v;   // both conversions exact
+}
+
+// The dequantised block mean q * s16 a key stream subtracts after the rotation
+// (0 for values and when the removal is off); false when the stream's block has
+// no valid mean row.
+__device__ __forceinline__ bool stream_mean(const EncArgs& a, const StreamId& id, int lane, double& mh0,
+                                            double& mh1) {
+    mh0 = 0.0;
+    mh1 = 0.0;
+    if (!a.k_mean || id.kv != 0) return true;
+    size_t row;
+    if (!mean_row(a, id.token / kMeanBlock * kMeanBlock, id.head, row)) return false;
+    const double sd = f16_bits_to_f64(a.k_mean_scale[row]);
+    mh0 = (double)a.k_mean[row * kHeadDim + lane] * sd;
+    mh1 = (double)a.k_mean[row * kHeadDim + lane + 64] * sd;
+    return true;
+}
+
 // Rotation y = H x (Sylvester, entries +-1): butterflies of span 1, 2, ..., 64,
-// (a, b) -> (a + b, a - b) for the pair (i, i + h), i mod 2h < h; then the norm
-// S by the fixed tree s_j += s_{j+w}, w = 64, 32, ..., 1, rho = sqrt(S / 128),
-// rho16 rounded once, and the unit-RMS values z = y / rho.
-__device__ __forceinline__ void rotate_normalise(double y0, double y1, int lane, double& z0, double& z1,
-                                                 uint16_t& rho16) {
+// (a, b) -> (a + b, a - b) for the pair (i, i + h), i mod 2h < h.
+__device__ __forceinline__ void fwht_f64(double& y0, double& y1, int lane) {
 #pragma unroll
     for (int h = 1; h < 64; h <<= 1) {
         const double p0 = __shfl_xor(y0, h), p1 = __shfl_xor(y1, h);
@@ -200,11 +231,15 @@ __device__ __forceinline__ void rotate_normalise(double y0, double y1, int lane,
         y0 = lo ? y0 + p0 : p0 - y0;
         y1 = lo ? y1 + p1 : p1 - y1;
     }
-    {
-        const double u = y0, v = y1;
-        y0 = u + v;
-        y1 = u - v;
-    }
+    const double u = y0, v = y1;
+    y0 = u + v;
+    y1 = u - v;
+}
+
+// The norm S by the fixed tree s_j += s_{j+w}, w = 64, 32, ..., 1,
+// rho = sqrt(S / 128), rho16 rounded once, and the unit-RMS values z = y / rho.
+__device__ __forceinline__ void normalise(double y0, double y1, int lane, double& z0, double& z1,
+                                          uint16_t& rho16) {
     double s = y0 * y0;
     {
         const double s1 = y1 * y1;
@@ -299,10 +334,14 @@ __device__ void encode_one(const EncArgs& a, long sid, int lane, Scratch& W, con
     const SymConst* sc = sconst[id.kv];
     const int M = T->levels, C = T->container, p = T->prob_bits;
     const int32_t budget = T->budget_fx;
-    double y0, y1, z0, z1;
+    double y0, y1, z0, z1, mh0, mh1;
     uint16_t rho16;
+    if (!stream_mean(a, id, lane, mh0, mh1)) return;   // the mean pass flagged this key block
     load_row(a, id, lane, y0, y1);
-    rotate_normalise(y0, y1, lane, z0, z1, rho16);
+    fwht_f64(y0, y1, lane);
+    y0 = y0 - mh0;
+    y1 = y1 - mh1;
+    normalise(y0, y1, lane, z0, z1, rho16);
     int m0 = nearest_level(z0, T, M), m1 = nearest_level(z1, T, M);
     const int n0 = m0, n1 = m1;
     int R = wave_sum_i(T->cost[m0] + T->cost[m1]);
@@ -388,6 +427,55 @@ __device__ void encode_one(const EncArgs& a, long sid, int lane, Scratch& W, con
     }
 }
 
+// The key channel means of the call's 128-token blocks (sections 3.2, 5): one
+// wave per (block, KV head). The rotated rows are added in token order in
+// fp64 and divided by 128; the INT8 code takes one fp16 scale
+// s16 = fp16(max |mu| / 127) and q = rint(mu / s16) clamped to +-127.
+__global__ __launch_bounds__(64 * kWaves) void mean_kernel(EncArgs a) {
+    const int lane = threadIdx.x & 63;
+    const long w = (long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int nblocks = a.num_tokens / kMeanBlock;
+    if (w >= (long)nblocks * a.num_kv_heads) return;
+    const int blk = (int)(w / a.num_kv_heads), head = (int)(w % a.num_kv_heads);
+    size_t row;
+    if (!mean_row(a, blk * kMeanBlock, head, row)) {
+        if (lane == 0 && a.err_word) atomicOr(a.err_word, DQ_DEVERR_MEAN_SLOT);
+        return;
+    }
+    double acc0 = 0.0, acc1 = 0.0;
+    for (int t0 = 0; t0 < kMeanBlock; t0 += 8) {
+        double y0[8], y1[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            StreamId id;
+            id.kv = 0;
+            id.token = blk * kMeanBlock + t0 + u;
+            id.head = head;
+            load_row(a, id, lane, y0[u], y1[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            fwht_f64(y0[u], y1[u], lane);
+            acc0 = acc0 + y0[u];
+            acc1 = acc1 + y1[u];
+        }
+    }
+    const double mu0 = acc0 / 128.0, mu1 = acc1 / 128.0;
+    double mx = fmax(fabs(mu0), fabs(mu1));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    const uint16_t s16 = f64_to_f16_rne(mx / 127.0);
+    const double sd = f16_bits_to_f64(s16);
+    int q0 = 0, q1 = 0;
+    if (sd > 0.0) {
+        q0 = (int)fmin(fmax(__builtin_rint(mu0 / sd), -127.0), 127.0);
+        q1 = (int)fmin(fmax(__builtin_rint(mu1 / sd), -127.0), 127.0);
+    }
+    a.k_mean[row * kHeadDim + lane] = (int8_t)q0;
+    a.k_mean[row * kHeadDim + lane + 64] = (int8_t)q1;
+    if (lane == 0) a.k_mean_scale[row] = s16;
+}
+
 __global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a, int per_wave) {
     __shared__ WaveLds wl_all[kWaves];
     __shared__ SymConst sconst[2][16];
@@ -415,28 +503,35 @@ __global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a, int per_
 
     // ---- phase 1: lane = channel, one stream at a time
     int slot_n = -1;
-    double y0n = 0.0, y1n = 0.0;
+    double y0n = 0.0, y1n = 0.0, mh0n = 0.0, mh1n = 0.0;
     StreamId idn = stream_id(a, sid0);
     slot_n = a.slot_mapping[idn.token];
-    if (slot_n >= 0) load_row(a, idn, lane, y0n, y1n);
+    bool ok_n = stream_mean(a, idn, lane, mh0n, mh1n);
+    if (slot_n >= 0 && ok_n) load_row(a, idn, lane, y0n, y1n);
     for (int s = 0; s < nb; ++s) {
         const StreamId id = idn;
         const int slot = slot_n;
-        const double y0 = y0n, y1 = y1n;
+        const bool ok = ok_n;
+        double y0 = y0n, y1 = y1n;
+        const double mh0 = mh0n, mh1 = mh1n;
         if (s + 1 < nb) {   // the next stream's inputs go out before this one's work
             idn = stream_id(a, sid0 + s + 1);
             slot_n = a.slot_mapping[idn.token];
-            if (slot_n >= 0) load_row(a, idn, lane, y0n, y1n);
+            ok_n = stream_mean(a, idn, lane, mh0n, mh1n);
+            if (slot_n >= 0 && ok_n) load_row(a, idn, lane, y0n, y1n);
         }
-        if (slot < 0) {
-            if (lane == 0) W.staged[s] = -2;   // no slot: nothing is written
+        if (slot < 0 || !ok) {
+            if (lane == 0) W.staged[s] = -2;   // no slot, or a flagged key block: nothing is written
             continue;
         }
         const EncTable* T = a.tables + id.kv;
         const int M = T->levels;
         double z0, z1;
         uint16_t rho16;
-        rotate_normalise(y0, y1, lane, z0, z1, rho16);
+        fwht_f64(y0, y1, lane);
+        y0 = y0 - mh0;
+        y1 = y1 - mh1;
+        normalise(y0, y1, lane, z0, z1, rho16);
         const int m0 = nearest_level(z0, T, M), m1 = nearest_level(z1, T, M);
         const int R = wave_sum_i(T->cost[m0] + T->cost[m1]);
         const Cands c = rank_candidates(T, z0, z1, m0, m1, lane, W.sc);
@@ -515,6 +610,12 @@ __global__ void selftest_kernel(const double* __restrict__ a, const double* __re
 // fewer when that would leave the chip short of waves (about 3072 fit at
 // once: 256 CUs x 12), since a wave walks its streams one at a time first.
 hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
+    if (a.k_mean) {
+        const long waves = (long)(a.num_tokens / kMeanBlock) * a.num_kv_heads;
+        hipLaunchKernelGGL(mean_kernel, dim3((unsigned)((waves + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const long streams = 2l * a.num_tokens * a.num_kv_heads;
     const long waves_wanted = 3072;
     const int per_wave = (int)std::min(64l, std::max(1l, (streams + waves_wanted - 1) / waves_wanted));

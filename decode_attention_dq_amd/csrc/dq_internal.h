@@ -52,7 +52,18 @@ struct EncArgs {
     uint16_t* drift_stats;
     uint32_t* err_word;
     const EncTable* tables;       // device copy: [0] keys, [1] values
+    // key channel-mean removal: tokens form blocks of 128 (block j = tokens
+    // 128j .. 128j+127 of the call); null when off
+    int8_t* k_mean;               // [pages][Hkv][mean_rows_per_page][128]
+    uint16_t* k_mean_scale;       // [pages][Hkv][mean_rows_per_page], fp16 bits
 };
+
+constexpr int kMeanBlock = 128;   // tokens per key-mean block
+// Mean rows per page: one per 128-token block a page holds, or one (owned by
+// the page a block starts in) when a page holds fewer than 128 tokens.
+__host__ __device__ inline int mean_rows_per_page(int page_size) {
+    return page_size >= kMeanBlock ? page_size / kMeanBlock : 1;
+}
 
 struct AttnArgs {
     const void* q;
@@ -75,6 +86,8 @@ struct AttnArgs {
     int pk, pv;                         // prob bits
     float step_k, step_v;
     float softmax_scale;
+    const int8_t* k_mean;               // optional key block means (see EncArgs)
+    const uint16_t* k_mean_scale;
     const uint32_t* entries;            // [2][kTableSlots] decode tables (K then V)
     float* partials;                    // [batch][Hq][slot_count][kPartStride]
     float* out;
@@ -100,7 +113,7 @@ constexpr int kPartStride = 132;         // m, l, pad, pad, acc[128]
 constexpr int kWindowMax = 256;          // largest bf16 window
 
 // Launchers (defined next to their kernels).
-hipError_t launch_encode(const EncArgs& a, hipStream_t s);
+hipError_t launch_encode(const EncArgs& a, hipStream_t s);   // runs the mean pass first when a.k_mean
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bf16_attention(const Bf16Args& a, hipStream_t s);
 // Partial of the bf16 window, written to partial slot `slot`.

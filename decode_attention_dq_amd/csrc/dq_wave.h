@@ -37,6 +37,17 @@ __device__ __forceinline__ float wave_max_uniform(float v) {
     v = fmaxf(v, __int_as_float(dpp_mov<0x143, 0xC>(__float_as_int(v))));  // row_bcast:31
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// Wave-wide sum returned as a wave-uniform value, by the same DPP pattern
+// (the row broadcasts add zero in the rows they do not write).
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+    v += __int_as_float(dpp_mov<0xB1>(__float_as_int(v)));
+    v += __int_as_float(dpp_mov<0x4E>(__float_as_int(v)));
+    v += __int_as_float(dpp_mov<0x141>(__float_as_int(v)));
+    v += __int_as_float(dpp_mov<0x140>(__float_as_int(v)));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 __device__ __forceinline__ int wave_max_uniform_i(int v) {
     v = max(v, dpp_mov<0xB1>(v));
     v = max(v, dpp_mov<0x4E>(v));

@@ -23,7 +23,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 DQ_OK, DQ_ERR_INVALID_ARG, DQ_ERR_UNSUPPORTED, DQ_ERR_INFEASIBLE, DQ_ERR_WORKSPACE, DQ_ERR_HIP = range(6)
 DQ_DTYPE_F32, DQ_DTYPE_BF16 = 0, 1
 DQ_KEYS, DQ_VALUES = 0, 1
-DQ_DEVERR_DECODE, DQ_DEVERR_ENCODE = 1, 2
+DQ_DEVERR_DECODE, DQ_DEVERR_ENCODE, DQ_DEVERR_MEAN_SLOT = 1, 2, 4
 HEAD_DIM = 128
 
 
@@ -62,6 +62,11 @@ class dq_table_info(ctypes.Structure):
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
+
+
+class dq_attention_extras(ctypes.Structure):
+    _fields_ = [("window_k", ctypes.c_void_p), ("window_v", ctypes.c_void_p), ("window_lens", ctypes.c_void_p),
+                ("window_cap", ctypes.c_int), ("k_mean", ctypes.c_void_p), ("k_mean_scale", ctypes.c_void_p)]
 _sig = {
     "dq_table_describe": (_i, [ctypes.POINTER(dq_table_params), ctypes.POINTER(dq_table_info)]),
     "dq_tables_init": (_i, [ctypes.POINTER(_p), ctypes.POINTER(dq_table_params),
@@ -69,11 +74,15 @@ _sig = {
     "dq_tables_destroy": (_i, [_p]),
     "dq_tables_info": (_i, [_p, _i, ctypes.POINTER(dq_table_info)]),
     "dq_encode_kv": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "dq_encode_kv_blocks": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "dq_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "dq_decode_attention": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                  ctypes.c_float, _i, _p, _p, ctypes.c_size_t, _p, _p]),
     "dq_decode_attention_window": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                         ctypes.c_float, _i, _p, _p, _p, _i, _p, _p, ctypes.c_size_t, _p, _p]),
+    "dq_decode_attention_ext": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                     ctypes.c_float, _i, ctypes.POINTER(dq_attention_extras), _p, _p,
+                                     ctypes.c_size_t, _p, _p]),
     "dq_bf16_decode_attention": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, ctypes.c_float, _i, _p, _p,
                                       ctypes.c_size_t, _p]),
     "dq_decode_symbols": (_i, [_p, _i, _p, _i, _p, _p, _p]),
@@ -193,6 +202,86 @@ def dq_encode_kv(tables: Tables, k, v, slot_mapping, k_cache, v_cache, k_norm, v
     _check(_lib.dq_encode_kv(tables.handle, _ptr(k), _ptr(v), dtype, n, hkv, int(page_size),
                              _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _ptr(k_norm), _ptr(v_norm),
                              _ptr(drift_stats), _ptr(err_word), _stream(stream)), "dq_encode_kv")
+
+
+MEAN_BLOCK = 128
+
+
+def mean_rows_per_page(page_size: int) -> int:
+    """Key-mean rows each page owns: one per 128-token block it holds, or one."""
+    return page_size // MEAN_BLOCK if page_size >= MEAN_BLOCK else 1
+
+
+def dq_encode_kv_blocks(tables: Tables, k, v, slot_mapping, k_cache, v_cache, k_norm, v_norm, k_mean, k_mean_scale,
+                        page_size: int, drift_stats=None, err_word=None, stream=None) -> None:
+    """Cache write with key channel-mean removal: k, v [128 * blocks][Hkv][128]
+    (block j = rows 128j .. 128j+127), k_mean int8 [pages][Hkv][R][128],
+    k_mean_scale 16-bit [pages][Hkv][R] with R = mean_rows_per_page(page_size)."""
+    import torch
+    if k.dtype != v.dtype or k.shape != v.shape or k.dim() != 3 or k.shape[2] != HEAD_DIM:
+        raise ValueError("k and v must both be [num_tokens][Hkv][128] of one dtype")
+    if k.shape[0] % MEAN_BLOCK:
+        raise ValueError("the token count must be a multiple of 128")
+    dtype = {torch.float32: DQ_DTYPE_F32, torch.bfloat16: DQ_DTYPE_BF16}.get(k.dtype)
+    if dtype is None:
+        raise ValueError("k/v dtype must be float32 or bfloat16")
+    n, hkv = int(k.shape[0]), int(k.shape[1])
+    _need(k, "k"); _need(v, "v")
+    _need(slot_mapping, "slot_mapping", torch.int32, (n,))
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, torch.uint8)
+    for t, nm in ((k_norm, "k_norm"), (v_norm, "v_norm"), (k_mean_scale, "k_mean_scale")):
+        _need(t, nm)
+        if t.element_size() != 2:
+            raise ValueError(f"{nm} must hold 16-bit elements")
+    _need(k_mean, "k_mean", torch.int8)
+    if drift_stats is not None:
+        _need(drift_stats, "drift_stats", shape=(n, hkv, 2))
+    if err_word is not None:
+        _need(err_word, "err_word")
+    _check(_lib.dq_encode_kv_blocks(tables.handle, _ptr(k), _ptr(v), dtype, n // MEAN_BLOCK, hkv, int(page_size),
+                                    _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _ptr(k_norm), _ptr(v_norm),
+                                    _ptr(k_mean), _ptr(k_mean_scale), _ptr(drift_stats), _ptr(err_word),
+                                    _stream(stream)), "dq_encode_kv_blocks")
+
+
+def dq_decode_attention_ext(tables: Tables, q, k_cache, v_cache, k_norm, v_norm, block_table, context_lens,
+                            num_kv_heads: int, page_size: int, max_context: int, out, workspace,
+                            window_k=None, window_v=None, window_lens=None, k_mean=None, k_mean_scale=None,
+                            softmax_scale: float = 0.0, num_splits: int = 0, err_word=None, stream=None) -> None:
+    """dq_decode_attention with the optional bf16 window and key block means."""
+    import torch
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [B][Hq][128]")
+    qd = {torch.float32: DQ_DTYPE_F32, torch.bfloat16: DQ_DTYPE_BF16}.get(q.dtype)
+    if qd is None:
+        raise ValueError("q dtype must be float32 or bfloat16")
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    _need(q, "q")
+    _need(out, "out", torch.float32, (B, hq, HEAD_DIM))
+    _need(block_table, "block_table", torch.int32)
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    _need(workspace, "workspace")
+    ex = dq_attention_extras()
+    if window_k is not None:
+        for t, nm in ((window_k, "window_k"), (window_v, "window_v")):
+            _need(t, nm, torch.bfloat16)
+            if t.dim() != 4 or t.shape[0] != B or t.shape[1] != num_kv_heads or t.shape[3] != HEAD_DIM:
+                raise ValueError(f"{nm} must be [B][Hkv][cap][128]")
+        _need(window_lens, "window_lens", torch.int32, (B,))
+        ex.window_k, ex.window_v, ex.window_lens = _ptr(window_k), _ptr(window_v), _ptr(window_lens)
+        ex.window_cap = int(window_k.shape[2])
+    if k_mean is not None:
+        _need(k_mean, "k_mean", torch.int8)
+        _need(k_mean_scale, "k_mean_scale")
+        ex.k_mean, ex.k_mean_scale = _ptr(k_mean), _ptr(k_mean_scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.dq_decode_attention_ext(tables.handle, _ptr(q), qd, _ptr(k_cache), _ptr(v_cache), _ptr(k_norm),
+                                        _ptr(v_norm), _ptr(block_table), _ptr(context_lens), B, hq,
+                                        int(num_kv_heads), int(block_table.shape[1]), int(page_size),
+                                        int(max_context), float(softmax_scale), int(num_splits),
+                                        ctypes.byref(ex), _ptr(out), _ptr(workspace), nbytes, _ptr(err_word),
+                                        _stream(stream)), "dq_decode_attention_ext")
 
 
 def dq_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_context: int,

@@ -74,6 +74,7 @@ enum { DQ_KEYS = 0, DQ_VALUES = 1 };
 /* err_word bits set by the device */
 #define DQ_DEVERR_DECODE 1u   /* a decoded stream did not return to state 2^16 or overran C */
 #define DQ_DEVERR_ENCODE 2u   /* a stream could not be made to fit its container */
+#define DQ_DEVERR_MEAN_SLOT 4u /* a key block's first slot is not where a 128-token block starts */
 
 /*
  * Parameters of one static entropy table (keys and values each have one).
@@ -156,6 +157,30 @@ int dq_encode_kv(const dq_tables* tables, const void* k, const void* v, int dtyp
                  int num_tokens, int num_kv_heads, int page_size, const int32_t* slot_mapping,
                  uint8_t* k_cache, uint8_t* v_cache, uint16_t* k_norm, uint16_t* v_norm,
                  uint16_t* drift_stats, uint32_t* err_word, void* stream);
+
+/*
+ * Cache write with windowed key channel-mean removal (the paper removes the
+ * channel-wise mean of the rotated keys, section 3.2 Table 1, with windowed
+ * INT8 channel means, section 5): the call's tokens form num_blocks blocks of
+ * 128 (block j = rows 128j .. 128j+127 of k and v, 128 consecutive positions
+ * of one sequence starting at a multiple of 128). For every block and KV head
+ * the rotated key rows' mean mu (token-order fp64 sum / 128) is stored as
+ * INT8 with one fp16 scale s16 = fp16(max|mu| / 127), q = rint(mu / s16)
+ * clamped to +-127; each key stream then codes its rotated row minus q * s16.
+ * Values are coded as by dq_encode_kv. Arguments as for dq_encode_kv, plus:
+ *   k_mean        int8 [num_pages][num_kv_heads][R][128], R = page_size / 128
+ *                 when page_size >= 128, else 1: a block's row lives in the
+ *                 page its first token occupies, at index (offset / 128)
+ *   k_mean_scale  uint16 (fp16 bits) [num_pages][num_kv_heads][R]
+ * page_size must be a power of two (DQ_ERR_UNSUPPORTED). A block whose first
+ * slot is negative or not at offset 0 mod min(page_size, 128) of its page sets
+ * DQ_DEVERR_MEAN_SLOT and its key streams are not written.
+ */
+int dq_encode_kv_blocks(const dq_tables* tables, const void* k, const void* v, int dtype,
+                        int num_blocks, int num_kv_heads, int page_size, const int32_t* slot_mapping,
+                        uint8_t* k_cache, uint8_t* v_cache, uint16_t* k_norm, uint16_t* v_norm,
+                        int8_t* k_mean, uint16_t* k_mean_scale, uint16_t* drift_stats,
+                        uint32_t* err_word, void* stream);
 
 /*
  * Workspace bytes dq_decode_attention needs for these sizes; num_splits 0
@@ -243,6 +268,40 @@ int dq_bf16_decode_attention(const uint16_t* q, const uint16_t* k_cache, const u
                              int batch, int num_q_heads, int num_kv_heads, int max_pages_per_seq,
                              int page_size, int max_context, float softmax_scale, int num_splits,
                              float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Optional inputs of dq_decode_attention_ext; a NULL pointer leaves a part out.
+ *   window_k, window_v, window_lens, window_cap   a bf16 window of recent
+ *                 tokens, as for dq_decode_attention_window
+ *   k_mean, k_mean_scale   the key block means written by dq_encode_kv_blocks
+ *                 for every compressed token (context_lens counts whole
+ *                 blocks then, except for a sequence's unfinished last block,
+ *                 whose tokens use that block's row all the same)
+ */
+typedef struct {
+    const uint16_t* window_k;
+    const uint16_t* window_v;
+    const int32_t* window_lens;
+    int window_cap;
+    const int8_t* k_mean;
+    const uint16_t* k_mean_scale;
+} dq_attention_extras;
+
+/*
+ * Decode attention with any of the optional parts of dq_attention_extras: a
+ * bf16 window merged by log-sum-exp, and key block means (their share
+ * q~ . (q * s16) / 128 is added to every logit of the block, sections 3.2 and
+ * 5). extras may be NULL (then it is dq_decode_attention). Other arguments,
+ * errors and workspace as for dq_decode_attention.
+ */
+int dq_decode_attention_ext(const dq_tables* tables, const void* q, int q_dtype,
+                            const uint8_t* k_cache, const uint8_t* v_cache,
+                            const uint16_t* k_norm, const uint16_t* v_norm,
+                            const int32_t* block_table, const int32_t* context_lens,
+                            int batch, int num_q_heads, int num_kv_heads, int max_pages_per_seq,
+                            int page_size, int max_context, float softmax_scale, int num_splits,
+                            const dq_attention_extras* extras, float* out, void* workspace,
+                            size_t workspace_bytes, uint32_t* err_word, void* stream);
 
 /*
  * Test hook: decode n_streams contiguous containers ([n_streams][C] bytes of
