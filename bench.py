@@ -39,10 +39,13 @@ METRIC = "decode-attn compressed-KV GB/s (% HBM peak) and tokens/s at B=128, 8K 
 
 def algorithmic_bytes(w, lens, window_lens=None) -> int:
     """Bytes one attention call must read: K and V containers plus their fp16
-    norms for every compressed (token, KV head), and 2 x 256 bytes per bf16
+    norms for every compressed (token, KV head), 128 INT8 means and a scale per
+    128-token key block when the workload has them, and 2 x 256 bytes per bf16
     window token."""
     per_stream_pair = (w.container + 2) + (w.cv + 2)
     n = int(np.sum(lens)) * w.num_kv_heads * per_stream_pair
+    if getattr(w, "means", False):
+        n += int(np.sum(-(-np.asarray(lens) // 128))) * w.num_kv_heads * (128 + 2)
     if window_lens is not None:
         n += int(np.sum(window_lens)) * w.num_kv_heads * 2 * 256
     return n
@@ -164,7 +167,11 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
                             err_word=err, stream=stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        if w.window:
+        if w.means:
+            dq.dq_decode_attention_ext(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
+                                       c.context_lens, hkv, P, w.context, out, ws, k_mean=c.k_mean,
+                                       k_mean_scale=c.k_mean_scale, err_word=err, stream=stream)
+        elif w.window:
             dq.dq_decode_attention_window(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
                                           c.context_lens, c.win_k, c.win_v, c.win_lens, hkv, P, w.context, out, ws,
                                           err_word=err, stream=stream)
@@ -187,6 +194,7 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
     res = {"batch": B, "context": "ragged %d..%d" % w.ragged if append else w.context,
            "container_bytes": [w.container, w.cv], "page_size": P, "cache_copies": copies,
            **({"bf16_window": w.window} if w.window else {}),
+           **({"key_block_means": True} if w.means else {}),
            "us_per_call": round(attn * 1e6, 2), "GBps": round(nbytes / attn / 1e9, 2),
            "hbm_frac": round(nbytes / attn / 1e9 / HBM_PEAK_GBS, 4), "device_errors": int(err.item())}
     if append:
@@ -388,6 +396,7 @@ def main() -> int:
             "long_llama_b1": config_measurement(dq, torch, workloads, "long_llama_b1", copies=8),
             "ragged_1p96": config_measurement(dq, torch, workloads, "ragged_1p96", copies=2),
             "window_split_qwen3_8b": config_measurement(dq, torch, workloads, "window_split_qwen3_8b", copies=2),
+            "mean_qwen3_8b": config_measurement(dq, torch, workloads, "mean_qwen3_8b", copies=2),
         }
         result["bf16_reference"] = bf16_measurement(dq, torch, workloads, w.name, copies=2,
                                                     dq_us=per_call_s * 1e6)

@@ -126,7 +126,10 @@ struct AttnLaunch {
     uint32_t magic_k, magic_v;   // ceil(2^21 / C) for the padded staging
 };
 
-template <bool PAD_K, bool PAD_V>
+// PAD_K / PAD_V: containers laid out at the padded LDS stride; MEANS: key
+// block means are added to the logits (a separate instantiation, so that the
+// kernels without them keep their own register allocation).
+template <bool PAD_K, bool PAD_V, bool MEANS>
 __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const AttnArgs& a = L.a;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         bool up = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            sv[r] = valid ? d[r] * rk * kap[r] + cm[r] : -INFINITY;
+            sv[r] = valid ? (MEANS ? d[r] * rk * kap[r] + cm[r] : d[r] * rk * kap[r]) : -INFINITY;
             up |= r < G && sv[r] > m_run[r] + kSlack;
         }
         const int ev = valid && rv > 0.0f ? f32_exponent(rv) : -127;
@@ -335,15 +338,24 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     // block's INT8 channel means times its scale, dotted with the rotated query,
     // in the log2 logit scale; uniform over the tile (a 64-token tile lies in
     // one 128-token block).
-    auto mean_terms = [&](int t0, float* cm) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) cm[r] = 0.0f;
-        if (!a.k_mean) return;
+    // mean_load issues the loads (the lane's two INT8 means packed in one
+    // register, and the block's scale) well before mean_finish uses them.
+    auto mean_load = [&](int t0, uint32_t& mq, float& s16) {
+        mq = 0;
+        s16 = 0.0f;
+        if (!MEANS) return;
         const int tb = t0 & ~(kMeanBlock - 1);
         const int page = bt_row[tb >> log2p];
         const size_t mrow = ((size_t)page * hkv + g) * (size_t)mean_rows_per_page(P) + (size_t)((tb & (P - 1)) >> 7);
-        const float s16 = f16_to_f32(a.k_mean_scale[mrow]);
-        const float m0 = (float)a.k_mean[mrow * kHeadDim + lane], m1 = (float)a.k_mean[mrow * kHeadDim + 64 + lane];
+        s16 = f16_to_f32(a.k_mean_scale[mrow]);
+        const uint8_t* mb = (const uint8_t*)a.k_mean + mrow * kHeadDim;
+        mq = (uint32_t)mb[lane] | ((uint32_t)mb[64 + lane] << 8);
+    };
+    auto mean_finish = [&](uint32_t mq, float s16, float* cm) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cm[r] = 0.0f;
+        if (!MEANS) return;
+        const float m0 = (float)(int8_t)(mq & 255u), m1 = (float)(int8_t)(mq >> 8);
         const _Float16* qt = (const _Float16*)(lds + kOffQt);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -375,9 +387,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         tile_rows(row, bt_row, log2p, P, hkv, g, t, T);
         stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
         stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, row, lane);
-        float rk, rv, cm[4];
+        float rk, rv, cm[4], ms;
+        uint32_t mq;
+        mean_load(t, mq, ms);
         load_norms(t, row, rk, rv);
-        mean_terms(t, cm);
         wave_lds_sync();
         const bool valid = t + lane < T;
         RansLane kr;
@@ -405,6 +418,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
             dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, __builtin_bit_cast(half8, bw), dk, 0, 0, 0);
         }
         bad |= (valid && (kr.x != kStateLow || rans_consumed(kr, kabs) > (uint32_t)a.ck)) ? 1u : 0u;
+        mean_finish(mq, ms, cm);
         softmax(dk, valid, rk, rv, cm);
     }
     for (; t < end; t += kStep) {
@@ -412,13 +426,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         const int tn = t + kStep;
         const bool has_next = tn < end;
         const bool valid = t + lane < T, valid_n = tn + lane < T;
-        float rk_n = 0.0f, rv_n = 0.0f, cm_n[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float rk_n = 0.0f, rv_n = 0.0f, cm_n[4], ms_n = 0.0f;
+        uint32_t mq_n = 0;
         if (has_next) {
+            mean_load(tn, mq_n, ms_n);
             size_t row[4];
             tile_rows(row, bt_row, log2p, P, hkv, g, tn, T);
             stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
             load_norms(tn, row, rk_n, rv_n);
-            mean_terms(tn, cm_n);
         }
         wave_lds_sync();
         RansLane vr, kr;
@@ -436,6 +451,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         }
         bad |= (valid && (vr.x != kStateLow || rans_consumed(vr, vabs) > (uint32_t)a.cv)) ? 1u : 0u;
         if (has_next) {
+            mean_finish(mq_n, ms_n, cm_n);
             softmax(dk, valid_n, rk_n, rv_n, cm_n);
             wave_lds_sync();
             size_t row[4];   // recomputed (scalar loads) rather than held through the pass
@@ -533,12 +549,17 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     L.magic_k = ((1u << 21) + (uint32_t)a.ck - 1u) / (uint32_t)a.ck;
     L.magic_v = ((1u << 21) + (uint32_t)a.cv - 1u) / (uint32_t)a.cv;
     const bool pk = lds_stride(a.ck) != (uint32_t)a.ck, pv = lds_stride(a.cv) != (uint32_t)a.cv;
-    const void* fn = pk ? (pv ? (const void*)attn_kernel<true, true> : (const void*)attn_kernel<true, false>)
-                        : (pv ? (const void*)attn_kernel<false, true> : (const void*)attn_kernel<false, false>);
-    static bool attr_set[4] = {false, false, false, false};
-    const int which = (pk ? 2 : 0) + (pv ? 1 : 0);
+    const bool mk = a.k_mean != nullptr;
+    typedef void (*Kernel)(AttnLaunch);
+    static const Kernel kernels[8] = {
+        attn_kernel<false, false, false>, attn_kernel<false, true, false>, attn_kernel<true, false, false>,
+        attn_kernel<true, true, false>,   attn_kernel<false, false, true>, attn_kernel<false, true, true>,
+        attn_kernel<true, false, true>,   attn_kernel<true, true, true>};
+    const int which = (mk ? 4 : 0) + (pk ? 2 : 0) + (pv ? 1 : 0);
+    const Kernel fn = kernels[which];
+    static bool attr_set[8] = {false, false, false, false, false, false, false, false};
     if (!attr_set[which]) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set[which] = true;
     }
@@ -547,10 +568,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
-    if (pk && pv) hipLaunchKernelGGL((attn_kernel<true, true>), grid, dim3(kThreads), lds, s, L);
-    else if (pk) hipLaunchKernelGGL((attn_kernel<true, false>), grid, dim3(kThreads), lds, s, L);
-    else if (pv) hipLaunchKernelGGL((attn_kernel<false, true>), grid, dim3(kThreads), lds, s, L);
-    else hipLaunchKernelGGL((attn_kernel<false, false>), grid, dim3(kThreads), lds, s, L);
+    hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, s, L);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge(a.partials, a.slot_count, a.merge_slots, a.batch * a.num_q_heads, true, a.out, s);

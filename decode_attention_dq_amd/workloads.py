@@ -36,6 +36,8 @@ class Workload:
     extra: dict = field(default_factory=dict)
     container_v: int = 0         # value container bytes (0: same as `container`)
     window: int = 0              # most recent tokens kept uncompressed in bf16
+    key_offset: float = 0.0      # std of a per-(layer, KV head, channel) offset added to the keys
+    means: bool = False          # keys written in 128-token blocks with their channel means
 
     @property
     def cv(self) -> int:
@@ -53,6 +55,8 @@ WORKLOADS = {
     # the paper's serving layout: last 128 tokens in bf16, keys given more bytes than values
     "window_split_qwen3_8b": Workload("window_split_qwen3_8b", 128, 32, 8, 8192, container=41, container_v=27,
                                       window=128, config_id=6),
+    # keys with a strong channel mean, removed per 128-token block (the paper's key preprocessing)
+    "mean_qwen3_8b": Workload("mean_qwen3_8b", 128, 32, 8, 8192, key_offset=2.0, means=True, config_id=7),
 }
 
 
@@ -95,9 +99,14 @@ def kv_rows(w: Workload, layer: int, tensor: int, b: int, T: int, device="cuda")
     if w.outliers:
         ch = synth.outlier_channels(w.config_id, synth.T_OUTLIER_K if tensor == synth.T_K else synth.T_OUTLIER_V,
                                     w.num_kv_heads, w.outliers)
-    return synth.device_gaussian((T, w.num_kv_heads, 128), seed, device=device,
-                                 dtype=torch.bfloat16 if w.kv_bf16 else torch.float32,
-                                 outlier_channels=ch)
+    x = synth.device_gaussian((T, w.num_kv_heads, 128), seed, device=device,
+                              dtype=torch.bfloat16 if w.kv_bf16 else torch.float32,
+                              outlier_channels=ch)
+    if w.key_offset and tensor == synth.T_K:
+        oseed = int(np.random.SeedSequence([0, w.config_id, synth.T_K, layer, 999]).generate_state(1)[0])
+        off = synth.device_gaussian((w.num_kv_heads, 128), oseed, device=device, dtype=torch.float32) * w.key_offset
+        x = (x.float() + off[None]).to(x.dtype)
+    return x
 
 
 def query_rows(w: Workload, layer: int = 0, device="cuda"):
@@ -117,6 +126,8 @@ class Cache:
     context_lens: object
     lens: np.ndarray
     drift_stats: object | None = None
+    k_mean: object | None = None       # int8 [pages][Hkv][R][128] with the block means
+    k_mean_scale: object | None = None
     win_k: object | None = None        # bf16 [B][Hkv][window][128]
     win_v: object | None = None
     win_lens: object | None = None
@@ -138,6 +149,10 @@ def build_cache(dq, tables, w: Workload, layer: int = 0, keep_stats: bool = Fals
     if w.window:
         wk = torch.zeros((w.batch, H, w.window, 128), dtype=torch.bfloat16, device=device)
         wv = torch.zeros_like(wk)
+    if w.means:
+        R = dq.mean_rows_per_page(P)
+        km = torch.zeros((total, H, R, 128), dtype=torch.int8, device=device)
+        ks = torch.zeros((total, H, R), dtype=torch.int16, device=device)
     stats = []
     for b in range(w.batch):
         T = int(lens[b])
@@ -150,7 +165,11 @@ def build_cache(dq, tables, w: Workload, layer: int = 0, keep_stats: bool = Fals
             wv[b, :, :nw] = v[T:].transpose(0, 1).to(torch.bfloat16)
             k, v = k[:T].contiguous(), v[:T].contiguous()
         st = torch.zeros((T, H, 2), dtype=torch.int16, device=device) if keep_stats else None
-        if T:
+        if T and w.means:
+            if T % 128:
+                raise ValueError("block writes need whole 128-token blocks")
+            dq.dq_encode_kv_blocks(tables, k, v, slots, kc, vc, kn, vn, km, ks, P, drift_stats=st)
+        elif T:
             dq.dq_encode_kv(tables, k, v, slots, kc, vc, kn, vn, P, drift_stats=st)
         if keep_stats:
             stats.append(st)
@@ -158,6 +177,8 @@ def build_cache(dq, tables, w: Workload, layer: int = 0, keep_stats: bool = Fals
     c = Cache(kc, vc, kn, vn, torch.as_tensor(bt, device=device),
               torch.as_tensor(lens, device=device), lens,
               torch.cat(stats) if keep_stats else None)
+    if w.means:
+        c.k_mean, c.k_mean_scale = km, ks
     if w.window:
         c.win_k, c.win_v = wk, wv
         c.win_lens = torch.as_tensor((full - lens).astype(np.int32), device=device)
