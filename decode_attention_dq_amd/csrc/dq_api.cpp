@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <string>
 
@@ -203,19 +204,30 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 namespace dq {
 
-// Split rule: token splits of 2048 (8 tiles per wave, and small enough that a
-// ragged batch spreads evenly over the CUs: splits past a sequence's end exit
-// at once); shorter splits, down to one 256-token work-group tile, when that
-// would leave fewer than 1024 work-groups (4 per CU on 256 CUs).
+// Split rule. Work-groups are taken longest job first, so a launch ends well
+// when its last jobs are short ones: 1536-token splits (whose last split per
+// sequence is shorter) when they give at least four work-groups per slot (4
+// resident work-groups on each of 256 CUs); otherwise 2048-token splits, so
+// that a launch of about one round still fills every slot with equal jobs;
+// and shorter splits, down to one 256-token tile, when even that would leave
+// fewer than 1024 work-groups.
 int choose_splits(int batch, int num_kv_heads, int max_context) {
     const long units = (long)batch * num_kv_heads;
-    const int tile = 256, pref = 2048, target = 1024;
+    const int tile = 256, slots = 1024;
     const int max_by_len = (max_context + tile - 1) / tile;
-    long s = (max_context + pref - 1) / pref;
-    if (units * s < target) s = (target + units - 1) / units;
+    long s = (max_context + 1535) / 1536;
+    if (units * s < 4L * slots) {
+        s = (max_context + 2047) / 2048;
+        if (units * s < slots) s = (slots + units - 1) / units;
+    }
     if (s > max_by_len) s = max_by_len;
     if (s < 1) s = 1;
     return (int)s;
+}
+
+int token_cap(int max_pages_per_seq, int page_size, int splits, int split_len) {
+    long cap = std::min((long)max_pages_per_seq * page_size, (long)splits * split_len);
+    return (int)std::min(cap, (long)INT32_MAX);
 }
 
 int split_tokens(int max_context, int splits) {
@@ -398,7 +410,7 @@ static int decode_attention_impl(const dq_tables* t, const void* q, int q_dtype,
     a.num_splits = splits;
     a.split_len = dq::split_tokens(max_context, splits);
     a.slot_count = splits + 1;
-    a.merge_slots = splits + (win ? 1 : 0);
+    a.token_cap = dq::token_cap(max_pages_per_seq, page_size, splits, a.split_len);
     a.win_k = window_k;
     a.win_v = window_v;
     a.win_lens = window_lens;
@@ -466,6 +478,7 @@ int dq_bf16_decode_attention(const uint16_t* q, const uint16_t* k_cache, const u
     a.num_splits = splits;
     a.split_len = dq::split_tokens(max_context, splits);
     a.slot_count = splits + 1;
+    a.token_cap = dq::token_cap(max_pages_per_seq, page_size, splits, a.split_len);
     a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
     a.partials = (float*)workspace;
     a.out = out;

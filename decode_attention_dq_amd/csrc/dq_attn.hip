@@ -21,6 +21,7 @@
 //     and write one partial (m, l, acc[128]) per query head and split; a
 //     second kernel merges the splits and rotates the result back.
 #include "dq_device.h"
+#include "dq_sched.h"
 #include "dq_wave.h"
 
 namespace dq {
@@ -133,22 +134,21 @@ template <bool PAD_K, bool PAD_V, bool MEANS>
 __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const AttnArgs& a = L.a;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // Work-groups reach the eight XCDs round-robin by linear index; with the KV
+    // head fastest every XCD gets an even share of each job class. Jobs go
+    // longest first (pick_job); work-groups past the last job exit.
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = blockIdx.x % a.num_kv_heads;
+    int b, split;
+    if (!pick_job(a.context_lens, a.batch, a.token_cap, a.split_len, blockIdx.x / a.num_kv_heads, lane, b, split))
+        return;
     __attribute__((address_space(3))) uint8_t* lds_base = (__attribute__((address_space(3))) uint8_t*)lds;
     const int G = a.group;
-    const int T = max(0, min(a.context_lens[b], a.max_pages_per_seq * a.page_size));
+    const int T = covered_tokens(a.context_lens[b], a.token_cap);
     const int start = split * a.split_len;
     const int end = min(T, start + a.split_len);
     const size_t head_stride = (size_t)a.slot_count * kPartStride;
     float* part = a.partials + (((size_t)b * a.num_q_heads + (size_t)g * G) * a.slot_count + split) * kPartStride;
-    if (start >= end) {
-        if (tid < G) {
-            part[tid * head_stride + 0] = -INFINITY;
-            part[tid * head_stride + 1] = 0.0f;
-        }
-        return;
-    }
 
     const uint32_t kcB = align16(kTile * lds_stride(a.ck) + kPad), vcB = align16(kTile * lds_stride(a.cv) + kPad);
     const uint32_t oW = kOffWaves + (uint32_t)wave * wave_bytes(a.ck, a.cv);
@@ -567,11 +567,13 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
         hipError_t e = launch_window(a, a.num_splits, s);
         if (e != hipSuccess) return e;
     }
-    dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
+    dim3 grid((unsigned)(a.num_splits * a.num_kv_heads * a.batch));
     hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, s, L);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_merge(a.partials, a.slot_count, a.merge_slots, a.batch * a.num_q_heads, true, a.out, s);
+    MergeArgs m = {a.partials, a.slot_count, a.context_lens, a.token_cap, a.split_len, a.num_q_heads,
+                   a.win_k ? a.num_splits : -1, a.out};
+    return launch_merge(m, a.batch * a.num_q_heads, true, s);
 }
 
 hipError_t launch_decode_symbols(const uint32_t* entries, int prob_bits, int levels, int container,

@@ -16,6 +16,7 @@
 //     r, r+4, ...; the weights come from LDS, and the 4 lane groups and then
 //     the 4 waves are summed at the end.
 #include "dq_internal.h"
+#include "dq_sched.h"
 
 namespace dq {
 namespace {
@@ -35,21 +36,19 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 __global__ __launch_bounds__(kThreads, 4) void bf16_attn_kernel(Bf16Args a) {
     __shared__ __attribute__((aligned(16))) float pl[kWaves][kTile][4];   // weights [token][head]
     __shared__ float red[kWaves][4 * kHeadDim + 8];                       // acc[4][128], m[4], l[4]
-    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // KV head fastest (an even share of every job class per XCD, as work-groups
+    // reach the XCDs round-robin by linear index), jobs longest first.
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = blockIdx.x % a.num_kv_heads;
+    int b, split;
+    if (!pick_job(a.context_lens, a.batch, a.token_cap, a.split_len, blockIdx.x / a.num_kv_heads, lane, b, split))
+        return;
     const int G = a.group;
-    const int T = max(0, min(a.context_lens[b], a.max_pages_per_seq * a.page_size));
+    const int T = covered_tokens(a.context_lens[b], a.token_cap);
     const int start = split * a.split_len;
     const int end = min(T, start + a.split_len);
     const size_t head_stride = (size_t)a.slot_count * kPartStride;
     float* part = a.partials + (((size_t)b * a.num_q_heads + (size_t)g * G) * a.slot_count + split) * kPartStride;
-    if (start >= end) {
-        if (tid < G) {
-            part[tid * head_stride + 0] = -INFINITY;
-            part[tid * head_stride + 1] = 0.0f;
-        }
-        return;
-    }
     const int col = lane & 15, r = lane >> 4;   // MFMA column / lane group
     const int P = a.page_size, hkv = a.num_kv_heads;
     const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages_per_seq;
@@ -197,11 +196,12 @@ __global__ __launch_bounds__(kThreads, 4) void bf16_attn_kernel(Bf16Args a) {
 }  // namespace
 
 hipError_t launch_bf16_attention(const Bf16Args& a, hipStream_t s) {
-    dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
+    dim3 grid((unsigned)(a.num_splits * a.num_kv_heads * a.batch));
     hipLaunchKernelGGL(bf16_attn_kernel, grid, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_merge(a.partials, a.slot_count, a.num_splits, a.batch * a.num_q_heads, false, a.out, s);
+    MergeArgs m = {a.partials, a.slot_count, a.context_lens, a.token_cap, a.split_len, a.num_q_heads, -1, a.out};
+    return launch_merge(m, a.batch * a.num_q_heads, false, s);
 }
 
 }  // namespace dq

@@ -77,7 +77,7 @@ struct AttnArgs {
     int batch, num_q_heads, num_kv_heads, group, max_pages_per_seq, page_size;
     int num_splits, split_len;          // tokens per split (multiple of the work-group tile)
     int slot_count;                     // partial slots per (sequence, query head): splits + 1
-    int merge_slots;                    // slots the merge reads: splits, + 1 with a window
+    int token_cap;                      // tokens a sequence can cover: min(pages * page_size, splits * split_len)
     const uint16_t* win_k;              // optional bf16 window [batch][Hkv][win_cap][128]
     const uint16_t* win_v;
     const int32_t* win_lens;            // [batch]
@@ -103,7 +103,7 @@ struct Bf16Args {
     const int32_t* block_table;
     const int32_t* context_lens;
     int batch, num_q_heads, num_kv_heads, group, max_pages_per_seq, page_size, log2p;
-    int num_splits, split_len, slot_count;
+    int num_splits, split_len, slot_count, token_cap;
     float softmax_scale;
     float* partials;
     float* out;
@@ -118,10 +118,19 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_bf16_attention(const Bf16Args& a, hipStream_t s);
 // Partial of the bf16 window, written to partial slot `slot`.
 hipError_t launch_window(const AttnArgs& a, int slot, hipStream_t s);
-// Log-sum-exp merge of `splits` partials per (sequence, query head) into out;
+// Log-sum-exp merge of the partials of each (sequence, query head) into out:
+// the splits that hold tokens of the sequence, and the window slot if any.
+struct MergeArgs {
+    const float* partials;              // [batch][Hq][slot_count][kPartStride]
+    int slot_count;
+    const int32_t* context_lens;
+    int cap;                            // tokens a sequence can cover (see covered_tokens)
+    int split_len, num_q_heads;
+    int window_slot;                    // slot of the bf16 window partial, or -1
+    float* out;
+};
 // `rotated`: the partials are in the rotated domain (inverse rotation applied).
-hipError_t launch_merge(const float* partials, int slot_count, int splits, int rows, bool rotated, float* out,
-                        hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, int rows, bool rotated, hipStream_t s);
 hipError_t launch_decode_symbols(const uint32_t* entries, int prob_bits, int levels, int container,
                                  const uint8_t* containers, int n, uint8_t* out, uint32_t* err,
                                  hipStream_t s);
@@ -131,6 +140,7 @@ hipError_t launch_selftest_fp64(const double* a, const double* b, int n, double*
 // Split rule shared by dq_workspace_size and dq_decode_attention.
 int choose_splits(int batch, int num_kv_heads, int max_context);
 int split_tokens(int max_context, int splits);
+int token_cap(int max_pages_per_seq, int page_size, int splits, int split_len);
 
 }  // namespace dq
 

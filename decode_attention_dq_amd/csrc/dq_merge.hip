@@ -1,6 +1,7 @@
 // Split-K log-sum-exp merge of attention partials (m, l, acc[128]) per
 // (sequence, query head), shared by the compressed and the bf16 kernels.
 #include "dq_internal.h"
+#include "dq_sched.h"
 #include "dq_wave.h"
 
 namespace dq {
@@ -9,18 +10,23 @@ namespace {
 // Merge the splits of one (sequence, query head) by log-sum-exp and rotate
 // back: out = H (sum_s acc_s 2^(m_s - M)) / (128 * sum_s l_s 2^(m_s - M)),
 // or, for partials in the original domain (ROTATED false),
-// out = (sum_s acc_s 2^(m_s - M)) / (sum_s l_s 2^(m_s - M)). 4 waves share the splits (wave w takes s = w, w + 4, ...), each lane two
-// channels; the loads of different splits are independent, so many are in
-// flight at once.
+// out = (sum_s acc_s 2^(m_s - M)) / (sum_s l_s 2^(m_s - M)). The splits are
+// the ceil(T_b / split_len) that hold tokens of sequence b, plus the window
+// slot when there is one. 4 waves share them (wave w takes the w-th, the
+// (w + 4)-th, ...), each lane two channels; the loads of different splits are
+// independent, so many are in flight at once.
 constexpr int kMergeWaves = 4;
 template <bool ROTATED>
-__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __restrict__ partials, int slot_count,
-                                                                 int splits, float* __restrict__ out) {
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
     __shared__ float red[kMergeWaves][132];
     const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float* p = partials + (size_t)bh * slot_count * kPartStride;
+    const float* p = a.partials + (size_t)bh * a.slot_count * kPartStride;
+    const int T = covered_tokens(a.context_lens[bh / a.num_q_heads], a.cap);
+    const int n = (T + a.split_len - 1) / a.split_len;
+    const int slots = n + (a.window_slot >= 0 ? 1 : 0);
+    auto slot = [&](int i) { return i < n ? i : a.window_slot; };
     float M = -INFINITY;
-    for (int s = tid; s < splits; s += 64 * kMergeWaves) M = fmaxf(M, p[(size_t)s * kPartStride]);
+    for (int i = tid; i < slots; i += 64 * kMergeWaves) M = fmaxf(M, p[(size_t)slot(i) * kPartStride]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     if (lane == 0) red[wave][0] = M;
@@ -31,8 +37,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __
     float L = 0.0f, v0 = 0.0f, v1 = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll 4
-        for (int s = wave; s < splits; s += kMergeWaves) {
-            const float* ps = p + (size_t)s * kPartStride;
+        for (int i = wave; i < slots; i += kMergeWaves) {
+            const float* ps = p + (size_t)slot(i) * kPartStride;
             const float ms = ps[0];
             if (ms == -INFINITY) continue;
             const float f = exp2f(ms - M);
@@ -59,20 +65,17 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const float* __
     v0 *= inv;
     v1 *= inv;
     if (ROTATED) fwht128_f32(v0, v1, lane);
-    out[(size_t)bh * kHeadDim + lane] = v0;
-    out[(size_t)bh * kHeadDim + 64 + lane] = v1;
+    a.out[(size_t)bh * kHeadDim + lane] = v0;
+    a.out[(size_t)bh * kHeadDim + 64 + lane] = v1;
 }
 
 }  // namespace
 
-hipError_t launch_merge(const float* partials, int slot_count, int splits, int rows, bool rotated, float* out,
-                        hipStream_t s) {
+hipError_t launch_merge(const MergeArgs& a, int rows, bool rotated, hipStream_t s) {
     if (rotated)
-        hipLaunchKernelGGL(merge_kernel<true>, dim3(rows), dim3(64 * kMergeWaves), 0, s, partials, slot_count, splits,
-                           out);
+        hipLaunchKernelGGL(merge_kernel<true>, dim3(rows), dim3(64 * kMergeWaves), 0, s, a);
     else
-        hipLaunchKernelGGL(merge_kernel<false>, dim3(rows), dim3(64 * kMergeWaves), 0, s, partials, slot_count,
-                           splits, out);
+        hipLaunchKernelGGL(merge_kernel<false>, dim3(rows), dim3(64 * kMergeWaves), 0, s, a);
     return hipGetLastError();
 }
 

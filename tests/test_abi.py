@@ -99,3 +99,16 @@ def test_workspace_size(dq):
     # the automatic split count never splits below one 256-token tile
     assert dq.dq_workspace_size(1, 4, 1, 100) == 1 * 4 * 2 * 132 * 4
     assert dq.dq_workspace_size(128, 32, 8, 8192) >= 128 * 32 * 132 * 4
+
+
+@pytest.mark.parametrize("B,hkv,ctx,splits", [
+    (128, 8, 8192, 6),      # >= 4 work-groups per slot: 1536-token splits
+    (64, 8, 16384, 11),
+    (4, 8, 65536, 32),      # about one round: 2048-token splits, 1024 work-groups
+    (1, 8, 131072, 128),    # fewer: shorter splits up to 1024 work-groups
+    (1, 1, 300, 2),         # never below one 256-token tile
+])
+def test_split_rule(dq, B, hkv, ctx, splits):
+    """The automatic split count, read back from the workspace size (one
+    partial slot per split plus one for a window)."""
+    assert dq.dq_workspace_size(B, 4 * hkv, hkv, ctx) == B * 4 * hkv * (splits + 1) * 132 * 4

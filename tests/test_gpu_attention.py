@@ -19,7 +19,9 @@ def _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, hkv, P, max_ctx, splits=0):
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     B, hq = q.shape[:2]
     out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, dq.dq_workspace_size(B, hq, hkv, max_ctx, splits)), dtype=torch.uint8, device="cuda")
+    # NaN bytes: a partial the kernels leave unwritten reaches the merge as NaN
+    ws = torch.full((max(1, dq.dq_workspace_size(B, hq, hkv, max_ctx, splits)),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     dq.dq_decode_attention(tabs, q, dev(kc), dev(vc), dev(kn.view(np.int16)), dev(vn.view(np.int16)),
                            dev(bt), dev(np.asarray(lens, dtype=np.int32)), hkv, P, max_ctx, out, ws,
@@ -132,6 +134,22 @@ def test_split_invariance(gpu_lib):
     # differ at the level of that rounding (2^-11 relative per weight), far inside TOL
     for o in outs[1:]:
         assert row_rel_err(o, outs[0]).max() <= 5e-4
+
+
+@pytest.mark.parametrize("splits", [0, 2, 3, 7, 13])
+def test_every_job_class(gpu_lib, splits):
+    """Lengths on both sides of every 256-token tile and split boundary, so
+    that the longest-first job order draws jobs from every tile class (full
+    splits, last splits of 1 .. K tiles, empty sequences) at several split
+    lengths; every partial the merge reads must have been written."""
+    dq = gpu_lib
+    tk, tv, tabs = _tables(dq)
+    lens = [0, 1, 255, 256, 257, 511, 769, 1024, 1535, 1536, 1537, 2047, 3072, 3300]
+    q, kc, vc, kn, vn, bt, ref = _case(tk, tv, lens, 2, 4, 16, True, seed=8, perm_seed=8)
+    out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, lens, 2, 16, max(lens), splits=splits)
+    assert err == 0
+    assert np.all(out[0] == 0)
+    assert row_rel_err(out[1:], ref[1:]).max() <= TOL
 
 
 def test_empty_context_gives_zeros(gpu_lib):

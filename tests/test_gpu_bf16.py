@@ -41,7 +41,8 @@ def _case(dq, lens, hkv, hq, P, seed, perm_seed=None, splits=0):
     vcd = bf(vc).view(vc.shape[0], hkv, P, 128)
     max_ctx = max(1, max(lens))
     out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(dq.dq_workspace_size(B, hq, hkv, max_ctx, splits), dtype=torch.uint8, device="cuda")
+    # NaN bytes: a partial the kernel leaves unwritten reaches the merge as NaN
+    ws = torch.full((dq.dq_workspace_size(B, hq, hkv, max_ctx, splits),), 0xFF, dtype=torch.uint8, device="cuda")
     dq.dq_bf16_decode_attention(bf(synth.f32_to_bf16_bits(q)), kcd, vcd, dev(bt),
                                 dev(np.asarray(lens, dtype=np.int32)), hkv, P, max_ctx, out, ws,
                                 num_splits=splits)
@@ -62,6 +63,16 @@ def test_bf16_splits_and_empty(gpu_lib):
         out, ref = _case(gpu_lib, lens, 1, 4, 64, seed=7, splits=splits)
         assert np.all(out[0] == 0)
         assert row_rel_err(out[1:], ref[1:]).max() <= TOL_BF16, splits
+
+
+@pytest.mark.parametrize("splits", [0, 3, 7])
+def test_bf16_every_job_class(gpu_lib, splits):
+    """Lengths around every tile and split boundary (see the compressed path's
+    test of the same name): each job class taken once, every partial written."""
+    lens = [0, 1, 255, 257, 511, 1024, 1537, 2047, 3300]
+    out, ref = _case(gpu_lib, lens, 2, 4, 16, seed=9, perm_seed=3, splits=splits)
+    assert np.all(out[0] == 0)
+    assert row_rel_err(out[1:], ref[1:]).max() <= TOL_BF16
 
 
 def test_bf16_full_qwen3_layer_sampled(gpu_lib):
