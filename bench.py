@@ -240,20 +240,59 @@ def bf16_measurement(dq, torch, workloads, name: str, copies: int, dq_us: float,
             "compressed_time_ratio": round(dq_us / (t * 1e6), 3)}
 
 
+# the sources attn_kernel is built from: counters taken on other sources are stale
+ATTN_SOURCES = ("dq_attn.hip", "dq_device.h", "dq_wave.h", "dq_sched.h", "dq_internal.h")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, "decode_attention_dq_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None when
     the kernel sources changed since those counters were taken."""
-    import hashlib
     try:
-        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kernel]
+        rec = json.load(open(TRAFFIC_JSON))[kernel]
     except (OSError, KeyError, ValueError):
         return None
-    h = hashlib.sha256()
-    for f in ("dq_attn.hip", "dq_device.h", "dq_wave.h"):
-        h.update(open(os.path.join(ROOT, "decode_attention_dq_amd", "csrc", f), "rb").read())
-    if rec.get("source_sha256") != h.hexdigest() or rec.get("workload") != workload:
+    if rec.get("source_sha256") != attn_source_hash() or rec.get("workload") != workload:
         return None
     return int(rec["traffic_bytes_per_launch"])
+
+
+def record_traffic(fetch_csv: str, write_csv: str, workload: str = "decode_qwen3_8b") -> dict:
+    """Host only: HBM bytes per attn_kernel launch from two rocprofv3 --pmc
+    counter CSVs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch, mean over the
+    headline kernel's dispatches), scaled by what the same counters read for
+    a plain device copy of known size (kept in the record), written to
+    profiles/traffic.json with the hash of the current kernel sources."""
+    import csv
+
+    def mean_kib(path, counter):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if r["Counter_Name"] == counter and "attn_kernel<false, false, false>" in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"no {counter} rows for attn_kernel<false, false, false> in {path}")
+        return sum(vals) / len(vals), len(vals)
+
+    allrec = json.load(open(TRAFFIC_JSON))
+    rec = allrec["attn_kernel"]
+    fk, nf = mean_kib(fetch_csv, "FETCH_SIZE")
+    wk, nw = mean_kib(write_csv, "WRITE_SIZE")
+    copy = rec["copy_bytes"]
+    fs, ws_ = copy / (rec["copy_fetch_kib"] * 1024), copy / (rec["copy_write_kib"] * 1024)
+    rec.update({"workload": workload, "source_sha256": attn_source_hash(), "fetch_size_kib": fk,
+                "write_size_kib": wk, "fetch_scale": fs, "write_scale": ws_, "dispatches": [nf, nw],
+                "traffic_bytes_per_launch": fk * 1024 * fs + wk * 1024 * ws_})
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(allrec, f, indent=1)
+        f.write("\n")
+    return rec
 
 
 def main() -> int:
@@ -272,7 +311,12 @@ def main() -> int:
                     help="profiling only: run just this measurement and print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (reference for HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: write profiles/traffic.json from two rocprofv3 --pmc counter CSVs")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(*args.record_traffic)), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode-attention path has no "
               f"multi-GPU mode in this build.", file=sys.stderr)
