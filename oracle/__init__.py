@@ -17,6 +17,9 @@ Modules
              encode/decode, reconstruction (sections 3.1, 4.1-4.3)
   attention  O11  fp64 GQA decode attention over reconstructed K/V
   means      O12  windowed INT8 channel-mean removal for keys (sections 3.2, 5)
+  token      O13-O17  the per-token format: one 1024-value stream per token over
+             all 8 KV heads, min-max affine grid, drift, rANS, least-squares
+             refit with fp16 (o, s) (sections 4.2-4.5, 5.1, 5.5)
   measures   entropy, cross-entropy, coding gain, normal gap, NMSE (section 3.1/3.2)
 
 Parity status: every function is pinned by the tests in ``tests/`` against
@@ -30,6 +33,8 @@ from .codec import (fwht, normalize, nearest_level, drift_candidates, rans_encod
                     rans_decode, encode_streams, decode_streams, reconstruct, EncodeResult)
 from .attention import attention, attention_rotated
 from .means import block_means, dequantize as dequantize_means, BLOCK as MEAN_BLOCK
+from .token import (make_token_table, encode_tokens, decode_tokens, reconstruct_tokens, TokenEncodeResult,
+                    TOKEN_N, TOKEN_HEADS)
 from . import measures
 
 __all__ = [
@@ -38,4 +43,6 @@ __all__ = [
     "rans_enc_step", "rans_dec_step",
     "encode_streams", "decode_streams", "reconstruct", "EncodeResult",
     "attention", "attention_rotated", "measures", "block_means", "dequantize_means", "MEAN_BLOCK",
+    "make_token_table", "encode_tokens", "decode_tokens", "reconstruct_tokens", "TokenEncodeResult", "TOKEN_N",
+    "TOKEN_HEADS",
 ]
