@@ -30,6 +30,7 @@ UNITS = {
     "dq_bf16.hip": [],
     "dq_merge.hip": [],
     "dq_window.hip": [],
+    "dq_token_attn.hip": [],
     "dq_encode.hip": ["-ffp-contract=off"],
 }
 

@@ -62,20 +62,44 @@ double default_step(int levels, int container) {
     return 0.0;
 }
 
+// E[max of n i.i.d. N(0,1)] = integral of x n phi(x) Phi(x)^(n-1) dx by the
+// composite Simpson rule on [-12, 12] with 40000 intervals.
+double expected_max(int n) {
+    const int steps = 40000;
+    const double lo = -12.0, hi = 12.0, h = (hi - lo) / steps;
+    double total = 0.0;
+    for (int i = 0; i <= steps; ++i) {
+        const double x = lo + i * h;
+        const double phi = exp(-0.5 * x * x) / sqrt(2.0 * M_PI);
+        const double cdf = 0.5 * erfc(-x / sqrt(2.0));
+        const double f = x * n * phi * pow(cdf, n - 1);
+        const double w = (i == 0 || i == steps) ? 1.0 : (i % 2 ? 4.0 : 2.0);
+        total += w * f;
+    }
+    return total * h / 3.0;
+}
+
+// Default grid step of the per-token format: the min-max grid of an average
+// stream of 1024 N(0,1) values, 2 E[max] / (M - 1), in N(0,1) units.
+double token_step(int levels) { return 2.0 * expected_max(dq::kTokN) / (levels - 1); }
+
 // Table derivation. The probability model is the N(0,1) mass of each
 // level's nearest-neighbour cell (the paper derives its model directly from
 // the standard normal: section 1, section 3.2), sharpened by p^alpha and
 // renormalised (section 4.4), then quantised to integer frequencies summing
 // to 2^p for the rANS pair of section 3.1.
-int describe(const dq_table_params* in, dq_table_info* t) {
+// `token`: a table of the per-token format (1024 symbols per stream).
+int describe(const dq_table_params* in, dq_table_info* t, bool token = false) {
     if (!in || !t) return DQ_ERR_INVALID_ARG;
     memset(t, 0, sizeof(*t));
     const int M = in->levels, C = in->container;
     const int p = in->prob_bits ? in->prob_bits : 10;
     const double alpha = in->alpha > 0 ? in->alpha : 1.4;
-    double step = in->step > 0 ? in->step : default_step(M, C);
-    if (M < 2 || M > dq::kMaxLevels || p < 9 || p > dq::kMaxProbBits || C < 8 || C > 128)
+    const int n = token ? dq::kTokN : dq::kHeadDim;
+    const int c_lo = token ? dq::kTokMinC : 8, c_hi = token ? dq::kTokMaxC : 128;
+    if (M < 2 || M > dq::kMaxLevels || p < 9 || p > dq::kMaxProbBits || C < c_lo || C > c_hi)
         return DQ_ERR_UNSUPPORTED;
+    double step = in->step > 0 ? in->step : (token ? token_step(M) : default_step(M, C));
     if (!(step > 0) || !(alpha > 0) || !isfinite(step) || !isfinite(alpha)) return DQ_ERR_INVALID_ARG;
     t->levels = M;
     t->container = C;
@@ -157,7 +181,7 @@ int describe(const dq_table_params* in, dq_table_info* t) {
         while (t->inner[cur] >= 0) cur = t->inner[cur];
         if (t->cost[cur] > worst) worst = t->cost[cur];
     }
-    if (ok && (int64_t)dq::kHeadDim * worst + (8ll << dq::kCostFracBits) > t->budget_fx) ok = false;
+    if (ok && (int64_t)n * worst + (8ll << dq::kCostFracBits) > t->budget_fx) ok = false;
     t->feasible = ok ? 1 : 0;
     return ok ? DQ_OK : DQ_ERR_INFEASIBLE;
 }
@@ -225,6 +249,19 @@ int choose_splits(int batch, int num_kv_heads, int max_context) {
     return (int)s;
 }
 
+// Per-token split rule: 2048-token splits, or shorter ones (down to one
+// 256-token tile) until there are 2048 work-groups, four rounds of the 512 that
+// are resident at once (2 per CU).
+int token_choose_splits(int batch, int max_context) {
+    const int tile = 256, target = 2048;
+    const int max_by_len = (max_context + tile - 1) / tile;
+    long s = (max_context + 2047) / 2048;
+    if ((long)batch * s < target) s = (target + batch - 1) / batch;
+    if (s > max_by_len) s = max_by_len;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
 int token_cap(int max_pages_per_seq, int page_size, int splits, int split_len) {
     long cap = std::min((long)max_pages_per_seq * page_size, (long)splits * split_len);
     return (int)std::min(cap, (long)INT32_MAX);
@@ -259,13 +296,14 @@ int dq_table_describe(const dq_table_params* params, dq_table_info* out) {
     return describe(params, out);
 }
 
-int dq_tables_init(dq_tables** out, const dq_table_params* keys, const dq_table_params* values) {
+static int tables_init(dq_tables** out, const dq_table_params* keys, const dq_table_params* values, bool token) {
     if (!out || !keys || !values) return DQ_ERR_INVALID_ARG;
     *out = nullptr;
     dq_tables* t = new (std::nothrow) dq_tables();
     if (!t) return DQ_ERR_INVALID_ARG;
-    int rc = describe(keys, &t->info[0]);
-    if (rc == DQ_OK) rc = describe(values, &t->info[1]);
+    t->format = token ? 1 : 0;
+    int rc = describe(keys, &t->info[0], token);
+    if (rc == DQ_OK) rc = describe(values, &t->info[1], token);
     if (rc != DQ_OK) { delete t; return rc; }
     fill_enc_table(t->info[0], &t->enc[0]);
     fill_enc_table(t->info[1], &t->enc[1]);
@@ -288,6 +326,18 @@ int dq_tables_init(dq_tables** out, const dq_table_params* keys, const dq_table_
     return DQ_OK;
 }
 
+int dq_tables_init(dq_tables** out, const dq_table_params* keys, const dq_table_params* values) {
+    return tables_init(out, keys, values, false);
+}
+
+int dq_token_tables_init(dq_tables** out, const dq_table_params* keys, const dq_table_params* values) {
+    return tables_init(out, keys, values, true);
+}
+
+int dq_token_table_describe(const dq_table_params* params, dq_table_info* out) {
+    return describe(params, out, true);
+}
+
 int dq_tables_destroy(dq_tables* t) {
     if (!t) return DQ_OK;
     hipError_t e = hipSuccess;
@@ -307,7 +357,7 @@ int encode_impl(const dq_tables* t, const void* k, const void* v, int dtype, int
                 int page_size, const int32_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache, uint16_t* k_norm,
                 uint16_t* v_norm, int8_t* k_mean, uint16_t* k_mean_scale, uint16_t* drift_stats, uint32_t* err_word,
                 void* stream) {
-    if (!t || num_tokens < 0 || num_kv_heads <= 0 || page_size <= 0 || page_size % 16)
+    if (!t || t->format != 0 || num_tokens < 0 || num_kv_heads <= 0 || page_size <= 0 || page_size % 16)
         return DQ_ERR_INVALID_ARG;
     if (dtype != DQ_DTYPE_F32 && dtype != DQ_DTYPE_BF16) return DQ_ERR_INVALID_ARG;
     if (num_tokens == 0) return DQ_OK;
@@ -371,7 +421,7 @@ static int decode_attention_impl(const dq_tables* t, const void* q, int q_dtype,
                                  const uint16_t* window_v, const int32_t* window_lens, int window_cap,
                                  const int8_t* k_mean, const uint16_t* k_mean_scale, float* out,
                                  void* workspace, size_t workspace_bytes, uint32_t* err_word, void* stream) {
-    if (!t || !q || !k_cache || !v_cache || !k_norm || !v_norm || !block_table || !context_lens ||
+    if (!t || t->format != 0 || !q || !k_cache || !v_cache || !k_norm || !v_norm || !block_table || !context_lens ||
         !out || !workspace)
         return DQ_ERR_INVALID_ARG;
     if (q_dtype != DQ_DTYPE_F32 && q_dtype != DQ_DTYPE_BF16) return DQ_ERR_INVALID_ARG;
@@ -520,7 +570,8 @@ int dq_decode_attention_ext(const dq_tables* t, const void* q, int q_dtype, cons
 
 int dq_decode_symbols(const dq_tables* t, int which, const uint8_t* containers, int n_streams,
                       uint8_t* symbols_out, uint32_t* err_word, void* stream) {
-    if (!t || (which != DQ_KEYS && which != DQ_VALUES) || n_streams < 0) return DQ_ERR_INVALID_ARG;
+    if (!t || t->format != 0 || (which != DQ_KEYS && which != DQ_VALUES) || n_streams < 0)
+        return DQ_ERR_INVALID_ARG;
     if (n_streams == 0) return DQ_OK;
     if (!containers || !symbols_out || !aligned16(containers) || !aligned16(symbols_out))
         return DQ_ERR_INVALID_ARG;
@@ -528,6 +579,102 @@ int dq_decode_symbols(const dq_tables* t, int which, const uint8_t* containers, 
     hipError_t e = dq::launch_decode_symbols(t->d_entries + which * dq::kTableSlots, ti.prob_bits,
                                              ti.levels, ti.container, containers, n_streams,
                                              symbols_out, err_word, (hipStream_t)stream);
+    return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
+size_t dq_token_workspace_size(int batch, int num_q_heads, int max_context, int num_splits) {
+    if (batch <= 0 || num_q_heads <= 0 || max_context < 0 || num_splits < 0) return 0;
+    const int s = num_splits ? num_splits : dq::token_choose_splits(batch, max_context);
+    return (size_t)batch * num_q_heads * (s + 1) * dq::kPartStride * sizeof(float);
+}
+
+int dq_token_decode_attention(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
+                              const uint8_t* v_cache, const uint16_t* k_meta, const uint16_t* v_meta,
+                              const int32_t* block_table, const int32_t* context_lens, int batch, int num_q_heads,
+                              int max_pages_per_seq, int page_size, int max_context, float softmax_scale,
+                              int num_splits, float* out, void* workspace, size_t workspace_bytes,
+                              uint32_t* err_word, void* stream) {
+    if (!t || t->format != 1 || !q || !k_cache || !v_cache || !k_meta || !v_meta || !block_table ||
+        !context_lens || !out || !workspace)
+        return DQ_ERR_INVALID_ARG;
+    if (q_dtype != DQ_DTYPE_F32 && q_dtype != DQ_DTYPE_BF16) return DQ_ERR_INVALID_ARG;
+    if (batch <= 0 || num_q_heads <= 0 || max_pages_per_seq <= 0 || page_size <= 0 || max_context < 0 ||
+        num_splits < 0 || (long)max_pages_per_seq * page_size < max_context)
+        return DQ_ERR_INVALID_ARG;
+    if (num_q_heads % dq::kTokHeads || num_q_heads / dq::kTokHeads > 4 || (page_size & (page_size - 1)))
+        return DQ_ERR_UNSUPPORTED;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) || ((uintptr_t)k_meta & 3u) ||
+        ((uintptr_t)v_meta & 3u))
+        return DQ_ERR_INVALID_ARG;
+    const int splits = num_splits ? num_splits : dq::token_choose_splits(batch, max_context);
+    if (workspace_bytes < dq_token_workspace_size(batch, num_q_heads, max_context, splits)) return DQ_ERR_WORKSPACE;
+    if ((long)batch * splits > (long)INT32_MAX / 4) return DQ_ERR_INVALID_ARG;
+    dq::TokAttnArgs a;
+    a.q = q;
+    a.q_dtype = q_dtype;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_meta = k_meta;
+    a.v_meta = v_meta;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.group = num_q_heads / dq::kTokHeads;
+    a.max_pages_per_seq = max_pages_per_seq;
+    a.page_size = page_size;
+    a.log2p = 31 - __builtin_clz((unsigned)page_size);
+    a.num_splits = splits;
+    a.split_len = dq::split_tokens(max_context, splits);
+    a.slot_count = splits + 1;
+    a.token_cap = dq::token_cap(max_pages_per_seq, page_size, splits, a.split_len);
+    a.ck = t->info[0].container;
+    a.cv = t->info[1].container;
+    a.pk = t->info[0].prob_bits;
+    a.pv = t->info[1].prob_bits;
+    a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
+    a.entries = t->d_entries;
+    a.partials = (float*)workspace;
+    a.out = out;
+    a.err_word = err_word;
+    hipError_t e = dq::launch_token_attention(a, (hipStream_t)stream);
+    return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
+int dq_encode_tokens(const dq_tables* t, const void* k, const void* v, int dtype, int num_tokens,
+                     int page_size, const int32_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                     uint16_t* k_meta, uint16_t* v_meta, uint32_t* drift_stats, uint32_t* err_word, void* stream) {
+    if (!t || t->format != 1 || num_tokens < 0 || page_size <= 0) return DQ_ERR_INVALID_ARG;
+    if (dtype != DQ_DTYPE_F32 && dtype != DQ_DTYPE_BF16) return DQ_ERR_INVALID_ARG;
+    if (num_tokens == 0) return DQ_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_meta || !v_meta) return DQ_ERR_INVALID_ARG;
+    if ((long)num_tokens * 2 > (long)INT32_MAX / 2) return DQ_ERR_INVALID_ARG;
+    dq::TokEncArgs a;
+    a.k = k;
+    a.v = v;
+    a.dtype = dtype;
+    a.num_tokens = num_tokens;
+    a.page_size = page_size;
+    a.slot_mapping = slot_mapping;
+    a.cache[0] = k_cache;
+    a.cache[1] = v_cache;
+    a.meta[0] = k_meta;
+    a.meta[1] = v_meta;
+    a.drift_stats = drift_stats;
+    a.err_word = err_word;
+    a.tables = t->d_enc;
+    hipError_t e = dq::launch_token_encode(a, (hipStream_t)stream);
+    return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
+int dq_token_decode_symbols(const dq_tables* t, int which, const uint8_t* containers, int n_streams,
+                            uint8_t* symbols_out, uint32_t* err_word, void* stream) {
+    if (!t || t->format != 1 || (which != DQ_KEYS && which != DQ_VALUES) || n_streams < 0)
+        return DQ_ERR_INVALID_ARG;
+    if (n_streams == 0) return DQ_OK;
+    if (!containers || !symbols_out) return DQ_ERR_INVALID_ARG;
+    hipError_t e = dq::launch_token_decode_symbols(t->d_enc + which, containers, n_streams, symbols_out, err_word,
+                                                   (hipStream_t)stream);
     return e == hipSuccess ? DQ_OK : hip_fail(e);
 }
 

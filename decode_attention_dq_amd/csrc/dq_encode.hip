@@ -604,6 +604,333 @@ __global__ void selftest_kernel(const double* __restrict__ a, const double* __re
     f16[i] = f64_to_f16_rne(x);
 }
 
+// ---------------------------------------------------------------------------
+// Per-token format (sections 4.5 "Encoding", 5.1, 5.5): one stream of the 8
+// KV heads' 1024 rotated values per token, one wave per stream, its values in
+// registers from the load to the final refit. Lane l holds channels l and
+// l + 64 of every head, i.e. stream positions 128h + l and 128h + 64 + l:
+// value i of a lane (i = 2h + j) sits at position tok_pos(i, lane).
+
+struct __attribute__((aligned(16))) TokLds {
+    uint8_t sym[kTokN];          // the stream's current symbols, by position
+    uint8_t buf[kTokMaxC];       // the container before it is stored
+};
+
+__device__ __forceinline__ int tok_pos(int i, int lane) { return 128 * (i >> 1) + 64 * (i & 1) + lane; }
+
+// rANS encode of sym[1023..0] by one lane, counting bytes (rans_count_lane
+// over 1024 symbols, four symbols per LDS read): the emitted bytes, or -1
+// once more than cap would be emitted.
+__device__ int tok_rans_count(const uint8_t* sym, const SymConst* sc, int p, int cap) {
+    uint32_t x = kStateLow;
+    int cnt = 0;
+    for (int i = kTokN - 4; i >= 0; i -= 4) {
+        const uint32_t w = *(const uint32_t*)(sym + i);
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+            const SymConst c = sc[(w >> (8 * b)) & 255u];
+            if (x >= c.lim) {
+                ++cnt;
+                x >>= 8;
+            }
+            const uint32_t q = __umulhi(x, c.magic) >> c.shift;
+            x = x + c.cum + q * ((1u << p) - c.freq);
+        }
+    }
+    return cnt <= cap ? cnt : -1;
+}
+
+// The same encode writing the container to dst (LDS): the 3-byte state, then
+// the cnt emitted bytes in decode order, then zeros up to C.
+__device__ void tok_rans_write(const uint8_t* sym, const SymConst* sc, int p, int cnt, int C, uint8_t* dst) {
+    uint32_t x = kStateLow;
+    int j = kStateBytes + cnt;
+    for (int i = kTokN - 4; i >= 0; i -= 4) {
+        const uint32_t w = *(const uint32_t*)(sym + i);
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+            const SymConst c = sc[(w >> (8 * b)) & 255u];
+            if (x >= c.lim) {
+                dst[--j] = (uint8_t)(x & 255u);
+                x >>= 8;
+            }
+            const uint32_t q = __umulhi(x, c.magic) >> c.shift;
+            x = x + c.cum + q * ((1u << p) - c.freq);
+        }
+    }
+    dst[0] = (uint8_t)x;
+    dst[1] = (uint8_t)(x >> 8);
+    dst[2] = (uint8_t)(x >> 16);
+    for (int k = kStateBytes + cnt; k < C; ++k) dst[k] = 0;
+}
+
+// Sum of the 16 values of every lane by the fixed halving tree over stream
+// positions (v_j += v_{j+w}, w = 512, 256, .., 1): w = 512, 256, 128 pair
+// heads inside a lane, w = 64 the lane's two channels, w = 32 .. 1 lanes.
+// Every lane gets the total.
+__device__ __forceinline__ double tok_fold_sum(const double (&t)[16]) {
+    double a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = t[i] + t[i + 8];       // heads h, h + 4
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = a[i] + a[i + 4];       // heads h, h + 2
+    const double b0 = a[0] + a[2], b1 = a[1] + a[3];          // heads 0, 1
+    double v = b0 + b1;                                        // channels l, l + 64
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) {
+        const double o = __shfl_xor(v, w);
+        v = v + o;   // meaningful for lane < w, as the tree requires
+    }
+    return __shfl(v, 0);
+}
+
+__global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a) {
+    __shared__ TokLds tl_all[kWaves];
+    __shared__ SymConst sconst[2][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < 32) {
+        const EncTable* t = a.tables + (tid >> 4);
+        const int m = tid & 15;
+        SymConst c;
+        c.freq = t->freq[m];
+        c.cum = t->cum[m];
+        c.lim = t->renorm_lim[m];
+        c.magic = t->div_magic[m];
+        c.shift = t->div_shift[m];
+        c.inner = (uint32_t)t->inner[m];
+        c.pad0 = c.pad1 = 0;
+        sconst[tid >> 4][m] = c;
+    }
+    __syncthreads();
+    const long sid = (long)blockIdx.x * kWaves + wave;
+    const int token = (int)(sid >> 1), kv = (int)(sid & 1);
+    if (token >= a.num_tokens) return;
+    const int slot = a.slot_mapping[token];
+    if (slot < 0) return;
+    TokLds& W = tl_all[wave];
+    const EncTable* T = a.tables + kv;
+    const SymConst* sc = sconst[kv];
+    const int M = T->levels, C = T->container, p = T->prob_bits;
+    const int B = T->budget_fx;
+
+    // load and rotate each head: y = H x, exact inputs in fp64
+    double y[16];
+    {
+        const size_t base = (size_t)token * kTokN;
+        const void* src = kv ? a.v : a.k;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const size_t at = base + tok_pos(i, lane);
+            y[i] = a.dtype == DQ_DTYPE_BF16
+                       ? (double)__uint_as_float((uint32_t)((const uint16_t*)src)[at] << 16)
+                       : (double)((const float*)src)[at];
+        }
+#pragma unroll
+        for (int h = 0; h < 8; ++h) fwht_f64(y[2 * h], y[2 * h + 1], lane);
+    }
+
+    // token-wise min-max grid: o = min, s = (max - min) / (M - 1), u = (y - o) / s
+    double mn = y[0], mx = y[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+        mn = fmin(mn, y[i]);
+        mx = fmax(mx, y[i]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mn = fmin(mn, __shfl_xor(mn, o));
+        mx = fmax(mx, __shfl_xor(mx, o));
+    }
+    const double go = mn, gs = (mx - mn) / (double)(M - 1);
+    const double half = (double)(M - 1) / 2.0;
+    double u[16];
+    int m[16], nearest[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        u[i] = gs > 0.0 ? (y[i] - go) / gs : 0.0;
+        int q = 0;
+        for (int j = 1; j < M; ++j) {
+            const double b = (double)j - 0.5;
+            q += b >= half ? (u[i] > b) : (u[i] >= b);
+        }
+        m[i] = gs > 0.0 ? q : (M - 1) / 2;
+        nearest[i] = m[i];
+        W.sym[tok_pos(i, lane)] = (uint8_t)m[i];
+    }
+
+    // cost, then the drift rounds of the per-head coder in grid units: the
+    // candidates of a round leave in (key, position) order, each by a wave
+    // argmin, until the rate fits the budget and the rANS stream the container
+    int R = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) R += T->cost[m[i]];
+    R = wave_sum_i(R);
+    bool done = false, failed = false;
+    int cnt = -1, rounds = 0;
+    if (R <= B) {
+        wave_sync();
+        if (lane == 0) cnt = tok_rans_count(W.sym, sc, p, C - kStateBytes);
+        cnt = __shfl(cnt, 0);
+        done = cnt >= 0;
+    }
+    while (!done) {
+        if (++rounds > kMaxRounds) {
+            failed = true;
+            break;
+        }
+        uint64_t key[16];
+        int dr[16], mr[16];
+        bool any = false;
+        R = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            mr[i] = m[i];
+            R += T->cost[m[i]];
+            const int inn = T->inner[m[i]];
+            dr[i] = inn >= 0 ? T->cost[m[i]] - T->cost[inn] : 0;
+            key[i] = ~0ull;
+            if (inn >= 0 && dr[i] > 0) {
+                const double e1 = u[i] - (double)inn, e0 = u[i] - (double)m[i];
+                const double dd = e1 * e1 - e0 * e0;
+                key[i] = order_key(dd / (double)dr[i]);
+                any = true;
+            }
+        }
+        R = wave_sum_i(R);
+        if (!__any(any)) {
+            failed = true;
+            break;
+        }
+        int removed = 0;
+        // the next candidate in (key, position) order moves inward; false when none is left
+        auto take = [&]() -> bool {
+            uint64_t bk = ~0ull;
+            int bi = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (key[i] < bk) {   // positions grow with i: the first minimum has the lowest position
+                    bk = key[i];
+                    bi = i;
+                }
+            int bp = tok_pos(bi, lane);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const uint64_t ok = __shfl_xor(bk, o);
+                const int op = __shfl_xor(bp, o);
+                if (ok < bk || (ok == bk && op < bp)) {
+                    bk = ok;
+                    bp = op;
+                }
+            }
+            if (bk == ~0ull) return false;
+            const int owner = bp & 63, wi = 2 * (bp >> 7) + ((bp >> 6) & 1);
+            int d = 0;
+            if (lane == owner) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (i == wi) {
+                        d = dr[i];
+                        key[i] = ~0ull;
+                        m[i] = T->inner[mr[i]];
+                        W.sym[bp] = (uint8_t)m[i];
+                    }
+            }
+            removed += __shfl(d, owner);
+            return true;
+        };
+        bool left = true;
+        while (R - removed > B && (left = take())) {
+        }
+        if (R - removed <= B) {
+            for (;;) {
+                wave_sync();
+                if (lane == 0) cnt = tok_rans_count(W.sym, sc, p, C - kStateBytes);
+                cnt = __shfl(cnt, 0);
+                if (cnt >= 0) {
+                    done = true;
+                    break;
+                }
+                if (!take()) break;
+            }
+        }
+        (void)left;
+    }
+    if (failed) {
+        if (lane == 0 && a.err_word) atomicOr(a.err_word, DQ_DEVERR_ENCODE);
+        return;
+    }
+
+    // least-squares refit of (o, s) to the stored symbols, sums by the halving tree
+    double t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = (double)m[i];
+    const double mbar = tok_fold_sum(t) / (double)kTokN;
+    const double ybar = tok_fold_sum(y) / (double)kTokN;
+    double dm[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        dm[i] = (double)m[i] - mbar;
+        t[i] = dm[i] * dm[i];
+    }
+    const double smm = tok_fold_sum(t);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const double dy = y[i] - ybar;
+        t[i] = dm[i] * dy;
+    }
+    const double smy = tok_fold_sum(t);
+    const double s_star = smm > 0.0 ? smy / smm : 0.0;
+    const double o_star = ybar - s_star * mbar;
+
+    // the container, then (o16, s16), at the token's slot
+    wave_sync();
+    if (lane == 0) tok_rans_write(W.sym, sc, p, cnt, C, W.buf);
+    wave_sync();
+    const int page = slot / a.page_size, po = slot - page * a.page_size;
+    const size_t idx = (size_t)page * a.page_size + po;
+    uint8_t* dst = a.cache[kv] + idx * C;
+    for (int k = lane; k < C; k += 64) dst[k] = W.buf[k];
+    if (lane == 0) {
+        a.meta[kv][2 * idx] = f64_to_f16_rne(o_star);
+        a.meta[kv][2 * idx + 1] = f64_to_f16_rne(s_star);
+    }
+    if (a.drift_stats) {
+        int changed = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) changed += m[i] != nearest[i];
+        changed = wave_sum_i(changed);
+        if (lane == 0) a.drift_stats[(size_t)token * 2 + kv] = (uint32_t)changed | ((uint32_t)rounds << 16);
+    }
+}
+
+// Symbols of per-token containers, one stream per thread, straight from the
+// container bytes (a plain decoder for checking the cache write): slot =
+// x mod 2^p, m = the symbol whose [c_m, c_m + f_m) holds the slot, x =
+// f_m floor(x / 2^p) + slot - c_m, one byte shifted in while x < 2^16.
+__global__ void token_decode_symbols_kernel(const EncTable* __restrict__ T, const uint8_t* __restrict__ cont,
+                                            int n, uint8_t* __restrict__ out, uint32_t* err) {
+    const int sid = blockIdx.x * blockDim.x + threadIdx.x;
+    if (sid >= n) return;
+    const int M = T->levels, C = T->container, p = T->prob_bits;
+    const uint8_t* c = cont + (size_t)sid * C;
+    uint32_t x = (uint32_t)c[0] | ((uint32_t)c[1] << 8) | ((uint32_t)c[2] << 16);
+    int ptr = kStateBytes;
+    bool ok = true;
+    for (int i = 0; i < kTokN; ++i) {
+        const uint32_t slot = x & ((1u << p) - 1u);
+        int s = 0;
+        while (s + 1 < M && T->cum[s + 1] <= slot) ++s;
+        x = T->freq[s] * (x >> p) + slot - T->cum[s];
+        if (x < kStateLow) {
+            x = (x << 8) | (ptr < C ? c[ptr] : 0u);
+            ++ptr;
+            if (x < kStateLow) ok = false;
+        }
+        out[(size_t)sid * kTokN + i] = (uint8_t)s;
+    }
+    if (!(ok && x == kStateLow && ptr <= C) && err) atomicOr(err, DQ_DEVERR_DECODE);
+}
+
 }  // namespace
 
 // Streams per wave: 64 (one per lane in the serial phase) for large writes;
@@ -622,6 +949,20 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
     const long per_block = (long)per_wave * kWaves;
     dim3 grid((unsigned)((streams + per_block - 1) / per_block));
     hipLaunchKernelGGL(encode_kernel, grid, dim3(64 * kWaves), 0, s, a, per_wave);
+    return hipGetLastError();
+}
+
+hipError_t launch_token_encode(const TokEncArgs& a, hipStream_t s) {
+    const long streams = 2l * a.num_tokens;
+    dim3 grid((unsigned)((streams + kWaves - 1) / kWaves));
+    hipLaunchKernelGGL(token_encode_kernel, grid, dim3(64 * kWaves), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_token_decode_symbols(const EncTable* table, const uint8_t* containers, int n, uint8_t* out,
+                                       uint32_t* err, hipStream_t s) {
+    hipLaunchKernelGGL(token_decode_symbols_kernel, dim3((n + 63) / 64), dim3(64), 0, s, table, containers, n,
+                       out, err);
     return hipGetLastError();
 }
 

@@ -1,0 +1,278 @@
+// Decode attention over per-token streams (D-Quant section 4.5 "Decoding"):
+// a work-group owns a token range of one sequence and decodes each token's K
+// and V stream once; the levels of KV head g feed the query heads of group g
+// while the stream moves on to head g + 1. The affine grid folds into both
+// products (section 4.2): q~ . y_hat = o sum(q~) + s (q~ . m), and
+// sum_t p_t y_hat_t = sum_t p_t o_t + sum_t (p_t s_t) m_t.
+//
+// Work decomposition: 4 waves; a wave takes 64-token tiles, one token per
+// lane. Per tile it decodes K head 0, then for g = 0..7 updates the softmax
+// of group g, decodes V head g together with K head g + 1 (two independent
+// rANS chains per lane), moves the V levels through an LDS transpose, and
+// accumulates p.v with each lane owning two channels of every query head.
+// Container bytes are read straight from HBM through a 4-byte window that is
+// refilled every 4 steps; the refill reads two aligned dwords clamped to the
+// container's last dword, so no read leaves the container.
+#include "dq_device.h"
+#include "dq_internal.h"
+#include "dq_sched.h"
+#include "dq_wave.h"
+
+namespace dq {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 64;           // tokens per wave tile, one per lane
+constexpr int kGrp = 4;             // query heads per KV head held (GQA group <= 4)
+constexpr int kVtRowDw = kTile + 1; // dwords per row of the V level transpose (padded)
+
+struct TokShared {
+    uint32_t tab[2][kTableSlots];                 // decode tables, K then V
+    float qt[kTokHeads][kHeadDim][kGrp];          // rotated queries [KV head][channel][head in group]
+    float qsum[kTokHeads][kGrp];                  // their sums over the channels
+    union {
+        struct {
+            uint32_t vt[kHeadDim / 4][kVtRowDw];  // V levels: row k holds channels 4k..4k+3, column = token
+            float w[kTile][kGrp];                 // p * s_v per token and head
+        } wave[kWaves];
+        struct {
+            float acc[kWaves][kGrp][kHeadDim];
+            float m[kWaves][kGrp];
+            float l[kWaves][kGrp];
+        } red;
+    } u;
+};
+
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// Stream state from the container at byte offset rel0 (of C bytes) of the
+// cache: the 3-byte flush, then the window at byte 3.
+__device__ __forceinline__ void grans_refill(RansLane& r, const uint32_t* __restrict__ base, uint32_t last) {
+    r.ptr += r.sel - kSel0;
+    const uint32_t a = r.ptr & ~3u;
+    const uint32_t lo = base[min(a, last) >> 2];
+    const uint32_t hi = base[min(a + 4u, last) >> 2];
+    r.win = __builtin_amdgcn_alignbyte(hi, lo, r.ptr);
+    r.sel = kSel0;
+}
+__device__ __forceinline__ void grans_init(RansLane& r, const uint32_t* __restrict__ base, uint32_t rel0,
+                                           uint32_t last) {
+    r.ptr = rel0;
+    r.sel = kSel0;
+    grans_refill(r, base, last);
+    r.x = r.win & 0xFFFFFFu;
+    r.sel = kSel0 + (uint32_t)kStateBytes;
+    grans_refill(r, base, last);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void token_attn_kernel(TokAttnArgs a) {
+    __shared__ TokShared S;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int b, split;
+    if (!pick_job(a.context_lens, a.batch, a.token_cap, a.split_len, blockIdx.x, lane, b, split)) return;
+    const int G = a.group;
+    const int T = covered_tokens(a.context_lens[b], a.token_cap);
+    const int start = split * a.split_len;
+    const int end = min(T, start + a.split_len);
+
+    // ---- prologue: decode tables, rotated queries q~ = H q and their sums
+    for (int i = tid; i < 2 * kTableSlots; i += kThreads) (&S.tab[0][0])[i] = a.entries[i];
+    for (int i = tid; i < kTokHeads * kHeadDim * kGrp; i += kThreads) (&S.qt[0][0][0])[i] = 0.0f;
+    if (tid < kTokHeads * kGrp) (&S.qsum[0][0])[tid] = 0.0f;
+    __syncthreads();
+    for (int h = wave; h < a.num_q_heads; h += kWaves) {
+        const size_t qo = ((size_t)b * a.num_q_heads + h) * kHeadDim;
+        float v0, v1;
+        if (a.q_dtype == DQ_DTYPE_BF16) {
+            const uint16_t* q = (const uint16_t*)a.q + qo;
+            v0 = bf16_to_f32(q[lane]);
+            v1 = bf16_to_f32(q[lane + 64]);
+        } else {
+            const float* q = (const float*)a.q + qo;
+            v0 = q[lane];
+            v1 = q[lane + 64];
+        }
+        fwht128_f32(v0, v1, lane);
+        const int g = h / G, hh = h - g * G;
+        S.qt[g][lane][hh] = v0;
+        S.qt[g][lane + 64][hh] = v1;
+        const float sum = wave_sum(v0 + v1);
+        if (lane == 0) S.qsum[g][hh] = sum;
+    }
+    __syncthreads();
+
+    const uint32_t tabK = (uint32_t)(size_t)(__attribute__((address_space(3))) uint32_t*)&S.tab[0][0];
+    const uint32_t tabV = tabK + kTableSlots * 4u;
+    const uint32_t maskK = (1u << a.pk) - 1u, maskV = (1u << a.pv) - 1u;
+    const uint32_t* kbase = (const uint32_t*)a.k_cache;
+    const uint32_t* vbase = (const uint32_t*)a.v_cache;
+    const float cs = a.softmax_scale * kLog2e / (float)kHeadDim;
+
+    float acc[kTokHeads][kGrp][2];
+#pragma unroll
+    for (int g = 0; g < kTokHeads; ++g)
+#pragma unroll
+        for (int hh = 0; hh < kGrp; ++hh) acc[g][hh][0] = acc[g][hh][1] = 0.0f;
+    float mrun = -INFINITY, lrun = 0.0f;   // lane 4g + hh: running max and sum of head (g, hh)
+    bool bad = false;
+    auto& Wv = S.u.wave[wave];
+    const uint32_t vrow = (uint32_t)lane >> 1, vsh = ((uint32_t)lane & 1u) * 16u;
+
+    for (int t0 = start + wave * kTile; t0 < end; t0 += kWaves * kTile) {
+        const int t = t0 + lane;
+        const bool valid = t < end;
+        const int tt = valid ? t : t0;   // lanes past the end decode a real stream and are masked
+        const int page = a.block_table[(size_t)b * a.max_pages_per_seq + (tt >> a.log2p)];
+        const uint32_t idx = (uint32_t)page * (uint32_t)a.page_size + (uint32_t)(tt & (a.page_size - 1));
+        const uint32_t km = ((const uint32_t*)a.k_meta)[idx], vm = ((const uint32_t*)a.v_meta)[idx];
+        const float ok = f16_to_f32((uint16_t)(km & 0xFFFFu)), sk = f16_to_f32((uint16_t)(km >> 16));
+        const float ov = f16_to_f32((uint16_t)(vm & 0xFFFFu)), sv = f16_to_f32((uint16_t)(vm >> 16));
+        const uint32_t relk = idx * (uint32_t)a.ck, relv = idx * (uint32_t)a.cv;
+        const uint32_t lastk = (relk + (uint32_t)a.ck - 1u) & ~3u, lastv = (relv + (uint32_t)a.cv - 1u) & ~3u;
+        RansLane rk, rv;
+        grans_init(rk, kbase, relk, lastk);
+        grans_init(rv, vbase, relv, lastv);
+
+        // K head 0 alone
+        float s4[kGrp] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
+            if (c4) grans_refill(rk, kbase, lastk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t ek = rans_lookup(rk, tabK, maskK);
+                rans_advance(rk, ek, (uint32_t)a.pk);
+                const float mk = (float)(ek >> 28);
+                const float4_t q = *(const float4_t*)&S.qt[0][4 * c4 + i][0];
+#pragma unroll
+                for (int hh = 0; hh < kGrp; ++hh) s4[hh] += q[hh] * mk;
+            }
+        }
+        grans_refill(rk, kbase, lastk);
+
+#pragma unroll
+        for (int g = 0; g < kTokHeads; ++g) {
+            // softmax of group g over this tile (log2 domain), and the weights of its p.v
+            float4_t wv;
+#pragma unroll
+            for (int hh = 0; hh < kGrp; ++hh) {
+                const float L = valid ? (ok * S.qsum[g][hh] + sk * s4[hh]) * cs : -INFINITY;
+                const float mt = wave_max_uniform(L);
+                const float mo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), 4 * g + hh));
+                const float mn = fmaxf(mo, mt);
+                const float fac = exp2f(mo - mn);
+                const float p = valid ? exp2f(L - mn) : 0.0f;
+                const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lrun), 4 * g + hh));
+                const float ln = lo * fac + wave_sum_uniform(p);
+                const float os = wave_sum_uniform(p * ov);
+                acc[g][hh][0] = acc[g][hh][0] * fac + os;
+                acc[g][hh][1] = acc[g][hh][1] * fac + os;
+                mrun = lane == 4 * g + hh ? mn : mrun;
+                lrun = lane == 4 * g + hh ? ln : lrun;
+                wv[hh] = p * sv;
+            }
+            *(float4_t*)&Wv.w[lane][0] = wv;
+
+            // V head g, fused with K head g + 1
+            s4[0] = s4[1] = s4[2] = s4[3] = 0.0f;
+            for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
+                if (c4) {
+                    grans_refill(rv, vbase, lastv);
+                    if (g + 1 < kTokHeads) grans_refill(rk, kbase, lastk);
+                }
+                uint32_t packed = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t ev = rans_lookup(rv, tabV, maskV);
+                    uint32_t ek = 0;
+                    if (g + 1 < kTokHeads) ek = rans_lookup(rk, tabK, maskK);
+                    rans_advance(rv, ev, (uint32_t)a.pv);
+                    if (g + 1 < kTokHeads) rans_advance(rk, ek, (uint32_t)a.pk);
+                    packed |= (ev >> 28) << (8 * i);
+                    if (g + 1 < kTokHeads) {
+                        const float mk = (float)(ek >> 28);
+                        const float4_t q = *(const float4_t*)&S.qt[g + 1][4 * c4 + i][0];
+#pragma unroll
+                        for (int hh = 0; hh < kGrp; ++hh) s4[hh] += q[hh] * mk;
+                    }
+                }
+                Wv.vt[c4][lane] = packed;
+            }
+            grans_refill(rv, vbase, lastv);
+            if (g + 1 < kTokHeads) grans_refill(rk, kbase, lastk);
+            wave_lds_sync();
+
+            // p.v of V head g: lane owns channels 2 lane and 2 lane + 1
+            for (int j = 0; j < kTile; ++j) {
+                const uint32_t d = Wv.vt[vrow][j] >> vsh;
+                const float m0 = (float)(d & 255u), m1 = (float)((d >> 8) & 255u);
+                const float4_t w4 = *(const float4_t*)&Wv.w[j][0];
+#pragma unroll
+                for (int hh = 0; hh < kGrp; ++hh) {
+                    acc[g][hh][0] += w4[hh] * m0;
+                    acc[g][hh][1] += w4[hh] * m1;
+                }
+            }
+            wave_lds_sync();
+        }
+        // both streams must end in the initial state having read no byte past C
+        const bool okk = rk.x == kStateLow && rk.ptr + (rk.sel - kSel0) - relk <= (uint32_t)a.ck;
+        const bool okv = rv.x == kStateLow && rv.ptr + (rv.sel - kSel0) - relv <= (uint32_t)a.cv;
+        bad = bad || (valid && !(okk && okv));
+    }
+    if (__any(bad) && lane == 0 && a.err_word) atomicOr(a.err_word, DQ_DEVERR_DECODE);
+
+    // ---- combine the 4 waves' partials per KV head and write them
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < kTokHeads; ++g) {
+#pragma unroll
+        for (int hh = 0; hh < kGrp; ++hh) {
+            S.u.red.acc[wave][hh][2 * lane] = acc[g][hh][0];
+            S.u.red.acc[wave][hh][2 * lane + 1] = acc[g][hh][1];
+        }
+        const float mg = __shfl(mrun, 4 * g + (lane & 3)), lg = __shfl(lrun, 4 * g + (lane & 3));
+        if (lane < kGrp) {
+            S.u.red.m[wave][lane] = mg;
+            S.u.red.l[wave][lane] = lg;
+        }
+        __syncthreads();
+        if (wave < G) {
+            const int hh = wave, h = g * G + hh;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, S.u.red.m[w][hh]);
+            float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float mw = S.u.red.m[w][hh];
+                if (mw == -INFINITY) continue;
+                const float f = exp2f(mw - M);
+                L += S.u.red.l[w][hh] * f;
+                o0 += S.u.red.acc[w][hh][lane] * f;
+                o1 += S.u.red.acc[w][hh][lane + 64] * f;
+            }
+            float* part = a.partials + (((size_t)b * a.num_q_heads + h) * a.slot_count + split) * kPartStride;
+            if (lane == 0) {
+                part[0] = M;
+                part[1] = L;
+            }
+            part[4 + lane] = o0;
+            part[4 + 64 + lane] = o1;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_token_attention(const TokAttnArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)(a.num_splits * a.batch));
+    hipLaunchKernelGGL(token_attn_kernel, grid, dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    MergeArgs m = {a.partials, a.slot_count, a.context_lens, a.token_cap, a.split_len, a.num_q_heads, -1, a.out};
+    return launch_merge(m, a.batch * a.num_q_heads, true, s);
+}
+
+}  // namespace dq

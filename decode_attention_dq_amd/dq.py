@@ -87,6 +87,14 @@ _sig = {
                                       ctypes.c_size_t, _p]),
     "dq_decode_symbols": (_i, [_p, _i, _p, _i, _p, _p, _p]),
     "dq_selftest_fp64": (_i, [_p, _p, _i, _p, _p, _p, _p]),
+    "dq_token_tables_init": (_i, [ctypes.POINTER(_p), ctypes.POINTER(dq_table_params),
+                                  ctypes.POINTER(dq_table_params)]),
+    "dq_token_table_describe": (_i, [ctypes.POINTER(dq_table_params), ctypes.POINTER(dq_table_info)]),
+    "dq_encode_tokens": (_i, [_p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "dq_token_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "dq_token_decode_attention": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, ctypes.c_float, _i,
+                                       _p, _p, ctypes.c_size_t, _p, _p]),
+    "dq_token_decode_symbols": (_i, [_p, _i, _p, _i, _p, _p, _p]),
     "dq_strerror": (ctypes.c_char_p, [_i]),
     "dq_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -142,13 +150,16 @@ def dq_table_describe(params: dq_table_params) -> dict:
 
 
 class Tables:
-    """Owns a dq_tables handle (keys and values) on the current device."""
+    """Owns a dq_tables handle (keys and values) on the current device;
+    ``token``: tables of the per-token format."""
 
-    def __init__(self, keys: dq_table_params, values: dq_table_params):
+    def __init__(self, keys: dq_table_params, values: dq_table_params, token: bool = False):
         h = _p()
-        _check(_lib.dq_tables_init(ctypes.byref(h), ctypes.byref(keys), ctypes.byref(values)),
-               "dq_tables_init")
+        init = _lib.dq_token_tables_init if token else _lib.dq_tables_init
+        _check(init(ctypes.byref(h), ctypes.byref(keys), ctypes.byref(values)),
+               "dq_token_tables_init" if token else "dq_tables_init")
         self.handle = h
+        self.token = token
 
     def info(self, which: int) -> dict:
         info = dq_table_info()
@@ -391,6 +402,102 @@ def dq_decode_symbols(tables: Tables, which: int, containers, symbols_out, err_w
         _need(err_word, "err_word")
     _check(_lib.dq_decode_symbols(tables.handle, int(which), _ptr(containers), n, _ptr(symbols_out),
                                   _ptr(err_word), _stream(stream)), "dq_decode_symbols")
+
+
+# ---- per-token format: one 1024-value stream per token over the 8 KV heads
+
+TOKEN_HEADS, TOKEN_VALUES = 8, 1024
+
+
+def dq_token_table_describe(params: dq_table_params) -> dict:
+    info = dq_table_info()
+    _check(_lib.dq_token_table_describe(ctypes.byref(params), ctypes.byref(info)), "dq_token_table_describe")
+    return info.as_dict()
+
+
+def dq_token_tables_init(keys: dq_table_params, values: dq_table_params) -> Tables:
+    return Tables(keys, values, token=True)
+
+
+def dq_encode_tokens(tables: Tables, k, v, slot_mapping, k_cache, v_cache, k_meta, v_meta, page_size: int,
+                     drift_stats=None, err_word=None, stream=None) -> None:
+    """k, v: [num_tokens][8][128] float32 or bfloat16; caches uint8
+    [pages][page_size][C]; metadata 16-bit [pages][page_size][2] (o16, s16);
+    drift_stats optional int32/uint32 [num_tokens][2]."""
+    import torch
+    if k.dtype != v.dtype or k.shape != v.shape or k.dim() != 3 or tuple(k.shape[1:]) != (TOKEN_HEADS, HEAD_DIM):
+        raise ValueError("k and v must both be [num_tokens][8][128] of one dtype")
+    dtype = {torch.float32: DQ_DTYPE_F32, torch.bfloat16: DQ_DTYPE_BF16}.get(k.dtype)
+    if dtype is None:
+        raise ValueError("k/v dtype must be float32 or bfloat16")
+    n = int(k.shape[0])
+    _need(k, "k"); _need(v, "v")
+    _need(slot_mapping, "slot_mapping", torch.int32, (n,))
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, torch.uint8)
+    for t, nm in ((k_meta, "k_meta"), (v_meta, "v_meta")):
+        _need(t, nm)
+        if t.element_size() != 2:
+            raise ValueError(f"{nm} must hold 16-bit elements")
+    if drift_stats is not None:
+        _need(drift_stats, "drift_stats", shape=(n, 2))
+        if drift_stats.element_size() != 4:
+            raise ValueError("drift_stats must hold 32-bit elements")
+    if err_word is not None:
+        _need(err_word, "err_word")
+    _check(_lib.dq_encode_tokens(tables.handle, _ptr(k), _ptr(v), dtype, n, int(page_size), _ptr(slot_mapping),
+                                 _ptr(k_cache), _ptr(v_cache), _ptr(k_meta), _ptr(v_meta), _ptr(drift_stats),
+                                 _ptr(err_word), _stream(stream)), "dq_encode_tokens")
+
+
+def dq_token_workspace_size(batch: int, num_q_heads: int, max_context: int, num_splits: int = 0) -> int:
+    return int(_lib.dq_token_workspace_size(int(batch), int(num_q_heads), int(max_context), int(num_splits)))
+
+
+def dq_token_decode_attention(tables: Tables, q, k_cache, v_cache, k_meta, v_meta, block_table, context_lens,
+                              page_size: int, max_context: int, out, workspace, softmax_scale: float = 0.0,
+                              num_splits: int = 0, err_word=None, stream=None) -> None:
+    """q: [B][Hq][128] float32 or bfloat16 with Hq = 8 G, G <= 4; out: [B][Hq][128] float32."""
+    import torch
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [B][Hq][128]")
+    q_dtype = {torch.float32: DQ_DTYPE_F32, torch.bfloat16: DQ_DTYPE_BF16}.get(q.dtype)
+    if q_dtype is None:
+        raise ValueError("q dtype must be float32 or bfloat16")
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    _need(q, "q")
+    _need(out, "out", torch.float32, (B, hq, HEAD_DIM))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages_per_seq]")
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache"), (workspace, "workspace")):
+        _need(t, nm, torch.uint8)
+    for t, nm in ((k_meta, "k_meta"), (v_meta, "v_meta")):
+        _need(t, nm)
+        if t.element_size() != 2:
+            raise ValueError(f"{nm} must hold 16-bit elements")
+    if err_word is not None:
+        _need(err_word, "err_word")
+    _check(_lib.dq_token_decode_attention(tables.handle, _ptr(q), q_dtype, _ptr(k_cache), _ptr(v_cache), _ptr(k_meta),
+                                          _ptr(v_meta), _ptr(block_table), _ptr(context_lens), B, hq,
+                                          int(block_table.shape[1]), int(page_size), int(max_context),
+                                          float(softmax_scale), int(num_splits), _ptr(out), _ptr(workspace),
+                                          int(workspace.numel()), _ptr(err_word), _stream(stream)),
+           "dq_token_decode_attention")
+
+
+def dq_token_decode_symbols(tables: Tables, which: int, containers, symbols_out, err_word=None,
+                            stream=None) -> None:
+    """containers: uint8 [n][C]; symbols_out: uint8 [n][1024]."""
+    import torch
+    _need(containers, "containers", torch.uint8)
+    n = int(containers.shape[0])
+    _need(symbols_out, "symbols_out", torch.uint8, (n, TOKEN_VALUES))
+    if err_word is not None:
+        _need(err_word, "err_word")
+    _check(_lib.dq_token_decode_symbols(tables.handle, int(which), _ptr(containers), n, _ptr(symbols_out),
+                                        _ptr(err_word), _stream(stream)), "dq_token_decode_symbols")
 
 
 def dq_selftest_fp64(a, b, sqrt_out, div_out, f16_out, stream=None) -> None:

@@ -322,6 +322,85 @@ int dq_decode_symbols(const dq_tables* tables, int which, const uint8_t* contain
 int dq_selftest_fp64(const double* a, const double* b, int n, double* sqrt_out,
                      double* div_out, uint16_t* f16_out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Per-token format (sections 4.2, 4.5 and 5.1 of the paper: each token is one
+ * group of 1024 values, the 8 KV heads' rotated rows in head order, coded as a
+ * single stream on a token-wise min-max affine grid x_hat = o + s*m, with the
+ * least-squares refit of (o, s) stored as two fp16 values; 331 / 231-byte
+ * key / value containers with 8 / 6 levels by default).
+ * The KV head count is fixed at 8 (DQ_TOKEN_HEADS).
+ * ------------------------------------------------------------------------ */
+#define DQ_TOKEN_HEADS 8
+#define DQ_TOKEN_VALUES 1024
+
+/*
+ * Tables of the per-token format. As dq_tables_init, with 1024 symbols per
+ * stream and containers of 16..1024 bytes; params.step = 0 selects the
+ * min-max grid of an average stream, 2 E[max of 1024 N(0,1)] / (M - 1).
+ * The tables serve only the dq_*token* calls (the per-head calls return
+ * DQ_ERR_INVALID_ARG for them, and the token calls for per-head tables).
+ */
+int dq_token_tables_init(dq_tables** out, const dq_table_params* keys, const dq_table_params* values);
+int dq_token_table_describe(const dq_table_params* params, dq_table_info* out);
+
+/*
+ * Per-token cache write (sections 4.2, 4.3, 4.5 "Encoding"): per token and
+ * tensor, y = H x for each of the 8 heads, the min-max grid o = min y,
+ * s = (max y - min y)/(M-1), nearest levels, drift until the stream fits,
+ * rANS, then the least-squares refit of (o, s).
+ *   k, v          [num_tokens][8][128], DQ_DTYPE_F32 or DQ_DTYPE_BF16; finite
+ *   slot_mapping  int32 [num_tokens]: slot = page * page_size + offset; < 0
+ *                 skips the token
+ *   k_cache       uint8 [pages][page_size][C_K] (C_V for v_cache), written at
+ *                 each slot; nothing else is touched
+ *   k_meta        fp16 bits [pages][page_size][2]: (o16, s16) per slot
+ *   drift_stats   optional uint32 [num_tokens][2] (K, V): symbols changed by
+ *                 drift | rounds << 16
+ *   err_word      optional; DQ_DEVERR_ENCODE if a stream cannot be fitted
+ * Ownership: all buffers are the caller's device memory; asynchronous on
+ * `stream`.
+ */
+int dq_encode_tokens(const dq_tables* tables, const void* k, const void* v, int dtype, int num_tokens,
+                     int page_size, const int32_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                     uint16_t* k_meta, uint16_t* v_meta, uint32_t* drift_stats, uint32_t* err_word,
+                     void* stream);
+
+/* Workspace bytes of dq_token_decode_attention (0 = library split rule). */
+size_t dq_token_workspace_size(int batch, int num_q_heads, int max_context, int num_splits);
+
+/*
+ * Decode attention over the per-token format (section 4.5 "Decoding": each
+ * stream is decoded once and feeds every query head of its KV heads).
+ * out[b][h] = softmax(q . K^T * scale) V over the context_lens[b] tokens,
+ * K and V the reconstructions H (o16 + s16 m) / 128 per head; query head h
+ * uses KV head h / (Hq / 8).
+ *   q             [batch][num_q_heads][128], F32 or BF16; num_q_heads = 8 * G,
+ *                 G <= 4 (else DQ_ERR_UNSUPPORTED)
+ *   k_cache, v_cache, k_meta, v_meta   as written by dq_encode_tokens; the
+ *                 caches 16-byte aligned and under 4 GiB each, the metadata
+ *                 4-byte aligned
+ *   block_table   int32 [batch][max_pages_per_seq]; page_size a power of two
+ *   context_lens  int32 [batch], 0 <= len <= max_context (0 gives zeros)
+ *   workspace     dq_token_workspace_size bytes, 16-byte aligned
+ *   err_word      optional; DQ_DEVERR_DECODE when a stream does not end in
+ *                 the initial state or reads past its container
+ * Returns DQ_ERR_WORKSPACE if the workspace is too small.
+ */
+int dq_token_decode_attention(const dq_tables* tables, const void* q, int q_dtype, const uint8_t* k_cache,
+                              const uint8_t* v_cache, const uint16_t* k_meta, const uint16_t* v_meta,
+                              const int32_t* block_table, const int32_t* context_lens, int batch,
+                              int num_q_heads, int max_pages_per_seq, int page_size, int max_context,
+                              float softmax_scale, int num_splits, float* out, void* workspace,
+                              size_t workspace_bytes, uint32_t* err_word, void* stream);
+
+/*
+ * Test hook: decode n_streams contiguous per-token containers ([n][C] bytes
+ * of table `which`) into symbols uint8 [n][1024] by a plain per-thread
+ * decoder. Streams failing the integrity check set DQ_DEVERR_DECODE.
+ */
+int dq_token_decode_symbols(const dq_tables* tables, int which, const uint8_t* containers, int n_streams,
+                            uint8_t* symbols_out, uint32_t* err_word, void* stream);
+
 const char* dq_strerror(int code);
 const char* dq_last_hip_error(void);
 

@@ -112,3 +112,31 @@ def test_split_rule(dq, B, hkv, ctx, splits):
     """The automatic split count, read back from the workspace size (one
     partial slot per split plus one for a window)."""
     assert dq.dq_workspace_size(B, 4 * hkv, hkv, ctx) == B * 4 * hkv * (splits + 1) * 132 * 4
+
+
+@pytest.mark.parametrize("M,C", [(8, 331), (6, 231), (4, 160), (9, 400), (2, 140)])
+def test_host_token_tables_equal_oracle(dq, M, C):
+    """Per-token tables (1024 symbols per stream, default min-max step) on the
+    host equal the oracle's, including the step from the expected maximum."""
+    t = oracle.make_token_table(M, C)
+    try:
+        d = dq.dq_token_table_describe(dq.make_params(M, C))
+    except dq.DQError as e:
+        assert e.code == dq.DQ_ERR_INFEASIBLE and not t.feasible
+        return
+    assert t.feasible
+    assert d["step"] == pytest.approx(t.step, rel=1e-14)
+    assert d["freq"] == t.freq.tolist() and d["cum"] == t.cum.tolist()
+    assert d["cost"] == t.cost.tolist() and d["inner"] == t.inner.tolist()
+    assert d["budget_fx"] == t.budget_fx
+
+
+def test_token_tables_unsupported_sizes(dq):
+    for bad in (dq.make_params(8, 15), dq.make_params(8, 1025), dq.make_params(10, 331)):
+        with pytest.raises(dq.DQError) as ei:
+            dq.dq_token_table_describe(bad)
+        assert ei.value.code == dq.DQ_ERR_UNSUPPORTED
+    # a budget too small for 1024 central symbols is refused
+    with pytest.raises(dq.DQError) as ei:
+        dq.dq_token_table_describe(dq.make_params(8, 100))
+    assert ei.value.code == dq.DQ_ERR_INFEASIBLE

@@ -1,0 +1,212 @@
+"""The per-token format on the device (one 1024-value stream per token over
+the 8 KV heads, min-max affine grid, least-squares refit; sections 4.2, 4.5,
+5.1): the cache write bit-exact against the oracle (containers, fp16 (o, s),
+drift statistics), the symbol decode exact, and decode attention over oracle
+containers within the 2e-3 bar against the oracle's fp64 attention over its
+reconstructions. Expected values come from the oracle only."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_dq_amd import synth
+from dq_cases import TOL, row_rel_err
+
+pytestmark = pytest.mark.gpu
+K_CFG, V_CFG = (8, 331), (6, 231)
+
+
+@pytest.fixture(scope="module")
+def setup(gpu_lib):
+    dq = gpu_lib
+    tk, tv = oracle.make_token_table(*K_CFG), oracle.make_token_table(*V_CFG)
+    tabs = dq.dq_token_tables_init(dq.make_params(*K_CFG), dq.make_params(*V_CFG))
+    return dq, tk, tv, tabs
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _tokens(seed, tensor, n, part=0, bf16=False):
+    """[n][8][128] float32 rows (K with 4 outlier channels per head)."""
+    return synth.gaussian_kv(700 + seed, tensor, n, 8, part=part, outliers=4 if tensor == synth.T_K else 0,
+                             bf16=bf16)
+
+
+def _layout(lens, P, perm_seed):
+    """Block table and the slot of every token, pages handed out per sequence."""
+    npages = [max(1, -(-T // P)) for T in lens]
+    total = sum(npages)
+    perm = np.random.default_rng(perm_seed).permutation(total)
+    bt = np.zeros((len(lens), max(npages)), np.int32)
+    slots, nxt = [], 0
+    for b, T in enumerate(lens):
+        for lp in range(npages[b]):
+            bt[b, lp] = perm[nxt]
+            nxt += 1
+        t = np.arange(T)
+        slots.append((bt[b, t // P] * P + t % P).astype(np.int32))
+    return bt, total, slots
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_token_encode_bit_exact(setup, bf16):
+    """Containers, (o16, s16) and drift statistics equal the oracle's; a
+    constant token and a zero token included; a slot of -1 writes nothing."""
+    dq, tk, tv, tabs = setup
+    n, P = 300, 16
+    k = _tokens(1, synth.T_K, n, bf16=bf16)
+    v = _tokens(1, synth.T_V, n, bf16=bf16)
+    k[7] = 0.0
+    v[7] = 0.0
+    k[8] = 0.0
+    k[8, :, 0] = 3.0                      # rotates to a constant 3 in every channel
+    slots = np.random.default_rng(2).permutation(n + 20)[:n].astype(np.int32)
+    slots[11] = -1
+    pages = -(-(n + 20) // P)
+    kc = torch.zeros((pages, P, K_CFG[1]), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros((pages, P, V_CFG[1]), dtype=torch.uint8, device="cuda")
+    km = torch.zeros((pages, P, 2), dtype=torch.int16, device="cuda")
+    vm = torch.zeros_like(km)
+    ds = torch.zeros((n, 2), dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kd, vd = _dev(k), _dev(v)
+    if bf16:
+        kd, vd = kd.to(torch.bfloat16), vd.to(torch.bfloat16)   # exact: the rows hold bf16 values
+    dq.dq_encode_tokens(tabs, kd, vd, _dev(slots), kc, vc, km, vm, P, drift_stats=ds, err_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    rk = oracle.encode_tokens(k.astype(np.float64), tk)
+    rv = oracle.encode_tokens(v.astype(np.float64), tv)
+    kc, vc = kc.cpu().numpy().reshape(-1, K_CFG[1]), vc.cpu().numpy().reshape(-1, V_CFG[1])
+    km, vm = km.cpu().numpy().view(np.uint16).reshape(-1, 2), vm.cpu().numpy().view(np.uint16).reshape(-1, 2)
+    ds = ds.cpu().numpy().view(np.uint32)
+    live = slots >= 0
+    s = slots[live]
+    assert np.array_equal(kc[s], rk.containers[live]) and np.array_equal(vc[s], rv.containers[live])
+    assert np.array_equal(km[s, 0], rk.o16[live].view(np.uint16))
+    assert np.array_equal(km[s, 1], rk.s16[live].view(np.uint16))
+    assert np.array_equal(vm[s, 0], rv.o16[live].view(np.uint16))
+    assert np.array_equal(vm[s, 1], rv.s16[live].view(np.uint16))
+    assert np.array_equal(ds[live, 0] & 0xFFFF, rk.changed[live]) and np.array_equal(ds[live, 0] >> 16, rk.rounds[live])
+    assert np.array_equal(ds[live, 1] & 0xFFFF, rv.changed[live]) and np.array_equal(ds[live, 1] >> 16, rv.rounds[live])
+    unused = np.setdiff1d(np.arange(pages * P), s)
+    assert not kc[unused].any() and not km[unused].any()
+
+
+def test_token_decode_symbols(setup):
+    """Oracle containers decode to the oracle's symbols; a corrupted container
+    sets the decode flag."""
+    dq, tk, tv, tabs = setup
+    for tab, cfg, t, tensor in ((tk, K_CFG, dq.DQ_KEYS, synth.T_K), (tv, V_CFG, dq.DQ_VALUES, synth.T_V)):
+        r = oracle.encode_tokens(_tokens(3, tensor, 64).astype(np.float64), tab)
+        cont = _dev(r.containers)
+        sym = torch.zeros((64, 1024), dtype=torch.uint8, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        dq.dq_token_decode_symbols(tabs, t, cont, sym, err_word=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert np.array_equal(sym.cpu().numpy(), r.symbols.astype(np.uint8))
+        bad = r.containers.copy()
+        bad[5, 0] ^= 0x5A                   # a different initial state
+        dq.dq_token_decode_symbols(tabs, t, _dev(bad), sym, err_word=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) & dq.DQ_DEVERR_DECODE
+
+
+def _attention_case(setup, lens, G, P=16, seed=5, perm_seed=3):
+    dq, tk, tv, tabs = setup
+    bt, pages, slots = _layout(lens, P, perm_seed)
+    kc = np.zeros((pages * P, K_CFG[1]), np.uint8)
+    vc = np.zeros((pages * P, V_CFG[1]), np.uint8)
+    km = np.zeros((pages * P, 2), np.uint16)
+    vm = np.zeros((pages * P, 2), np.uint16)
+    kh, vh = [], []
+    for b, T in enumerate(lens):
+        if T == 0:
+            kh.append(np.zeros((8, 0, 128)))
+            vh.append(np.zeros((8, 0, 128)))
+            continue
+        rk = oracle.encode_tokens(_tokens(seed, synth.T_K, T, part=b).astype(np.float64), tk)
+        rv = oracle.encode_tokens(_tokens(seed, synth.T_V, T, part=b).astype(np.float64), tv)
+        s = slots[b]
+        kc[s], vc[s] = rk.containers, rv.containers
+        km[s, 0], km[s, 1] = rk.o16.view(np.uint16), rk.s16.view(np.uint16)
+        vm[s, 0], vm[s, 1] = rv.o16.view(np.uint16), rv.s16.view(np.uint16)
+        kh.append(oracle.reconstruct_tokens(rk.symbols, rk.o16, rk.s16).transpose(1, 0, 2))
+        vh.append(oracle.reconstruct_tokens(rv.symbols, rv.o16, rv.s16).transpose(1, 0, 2))
+    hq = 8 * G
+    q = synth.queries(800 + seed, len(lens), hq, bf16=True)
+    ref = np.zeros((len(lens), hq, 128))
+    for b, T in enumerate(lens):
+        if T:
+            ref[b] = oracle.attention(q[b:b + 1], [kh[b]], [vh[b]])[0]
+    dev = dict(q=_dev(q).to(torch.bfloat16), kc=_dev(kc.reshape(pages, P, -1)), vc=_dev(vc.reshape(pages, P, -1)),
+               km=_dev(km.view(np.int16).reshape(pages, P, 2)), vm=_dev(vm.view(np.int16).reshape(pages, P, 2)),
+               bt=_dev(bt), lens=_dev(np.asarray(lens, np.int32)))
+    return dq, tabs, dev, ref, P
+
+
+def _run(dq, tabs, d, lens, P, splits=0):
+    B, hq = d["q"].shape[:2]
+    max_ctx = max(1, max(lens))
+    out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((dq.dq_token_workspace_size(B, hq, max_ctx, splits),), 0xFF, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_token_decode_attention(tabs, d["q"], d["kc"], d["vc"], d["km"], d["vm"], d["bt"], d["lens"], P, max_ctx,
+                                 out, ws, num_splits=splits, err_word=err)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), int(err.item())
+
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_token_attention_ragged_paged(setup, G):
+    lens = [1, 63, 64, 65, 300, 700, 0]
+    dq, tabs, d, ref, P = _attention_case(setup, lens, G)
+    out, err = _run(dq, tabs, d, lens, P)
+    assert err == 0
+    assert np.all(out[6] == 0)
+    assert row_rel_err(out[:6], ref[:6]).max() <= TOL
+
+
+@pytest.mark.parametrize("splits", [1, 3, 7])
+def test_token_attention_split_counts(setup, splits):
+    lens = [1500, 257, 1024]
+    dq, tabs, d, ref, P = _attention_case(setup, lens, 4, seed=6, perm_seed=9)
+    out, err = _run(dq, tabs, d, lens, P, splits)
+    assert err == 0
+    assert row_rel_err(out, ref).max() <= TOL
+
+
+def test_token_attention_flags_corrupt_stream(setup):
+    lens = [100]
+    dq, tabs, d, ref, P = _attention_case(setup, lens, 1, seed=7)
+    d["kc"][0, 3, 0] ^= 0x5A
+    out, err = _run(dq, tabs, d, lens, P)
+    assert err & dq.DQ_DEVERR_DECODE
+
+
+def test_token_encode_then_attend(setup):
+    """The device cache write feeding the device attention: the same output as
+    attention over the oracle's containers, within the bar of the oracle."""
+    dq, tk, tv, tabs = setup
+    lens, P, G = [200, 333], 32, 4
+    bt, pages, slots = _layout(lens, P, 4)
+    kc = torch.zeros((pages, P, K_CFG[1]), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros((pages, P, V_CFG[1]), dtype=torch.uint8, device="cuda")
+    km = torch.zeros((pages, P, 2), dtype=torch.int16, device="cuda")
+    vm = torch.zeros_like(km)
+    kh, vh = [], []
+    for b, T in enumerate(lens):
+        k, v = _tokens(9, synth.T_K, T, part=b), _tokens(9, synth.T_V, T, part=b)
+        dq.dq_encode_tokens(tabs, _dev(k), _dev(v), _dev(slots[b]), kc, vc, km, vm, P)
+        rk, rv = oracle.encode_tokens(k.astype(np.float64), tk), oracle.encode_tokens(v.astype(np.float64), tv)
+        kh.append(oracle.reconstruct_tokens(rk.symbols, rk.o16, rk.s16).transpose(1, 0, 2))
+        vh.append(oracle.reconstruct_tokens(rv.symbols, rv.o16, rv.s16).transpose(1, 0, 2))
+    q = synth.queries(809, 2, 8 * G, bf16=True)
+    ref = oracle.attention(q, kh, vh)
+    d = dict(q=_dev(q).to(torch.bfloat16), kc=kc, vc=vc, km=km, vm=vm, bt=_dev(bt), lens=_dev(np.asarray(lens, np.int32)))
+    out, err = _run(dq, tabs, d, lens, P)
+    assert err == 0
+    assert row_rel_err(out, ref).max() <= TOL
