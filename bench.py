@@ -203,6 +203,70 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
     return res
 
 
+def token_measurement(dq, torch, workloads, name: str = "token_qwen3_8b", copies: int = 2, reps: int = 5,
+                      enc_seqs: int = 16) -> dict:
+    """The per-token format on the Qwen3-8B layer (one 1024-value stream per
+    token over the 8 KV heads, 331 / 231-byte containers, 8 / 6 levels):
+    decode attention rotating through `copies` caches (each above the MALL),
+    and the cache write of `enc_seqs` sequences in one call."""
+    from decode_attention_dq_amd import synth
+    w = workloads.WORKLOADS[name]
+    tables = dq.dq_token_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.cv))
+    caches = [workloads.build_token_cache(dq, tables, w, layer=l) for l in range(copies)]
+    qs = [workloads.query_rows(w, l) for l in range(copies)]
+    B, hq, P = w.batch, w.num_q_heads, w.page_size
+    lens = caches[0].lens
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dq.dq_token_workspace_size(B, hq, w.context), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = []
+    for it in range(reps + 2):
+        for l in range(copies):
+            c = caches[l]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dq.dq_token_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
+                                         c.context_lens, P, w.context, out, ws, err_word=err, stream=stream)
+            e1.record(stream)
+            if it >= 2:
+                ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    ntok = int(np.sum(lens))
+    nbytes = ntok * (w.container + 4 + w.cv + 4)
+    del caches
+    # cache write of enc_seqs sequences in one call
+    n = enc_seqs * w.context
+    k = torch.cat([workloads.kv_rows(w, 0, synth.T_K, b, w.context) for b in range(enc_seqs)])
+    v = torch.cat([workloads.kv_rows(w, 0, synth.T_V, b, w.context) for b in range(enc_seqs)])
+    slots = torch.arange(n, dtype=torch.int32, device="cuda")
+    kc = torch.zeros(dq.token_cache_shape(n // P, P, w.container), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros(dq.token_cache_shape(n // P, P, w.cv), dtype=torch.uint8, device="cuda")
+    km = torch.zeros((n // P, P, 2), dtype=torch.int16, device="cuda")
+    vm = torch.zeros_like(km)
+    st = torch.zeros((n, 2), dtype=torch.int32, device="cuda")
+    dq.dq_encode_tokens(tables, k, v, slots, kc, vc, km, vm, P, drift_stats=st, err_word=err, stream=stream)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    dq.dq_encode_tokens(tables, k, v, slots, kc, vc, km, vm, P, drift_stats=st, err_word=err, stream=stream)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    te = a0.elapsed_time(a1) / 1e3
+    s = st.cpu().numpy().view(np.uint32)
+    changed, rounds = s & 0xFFFF, s >> 16
+    return {"workload": name, "batch": B, "context": w.context, "container_bytes": [w.container, w.cv],
+            "levels": [w.k_levels, w.v_levels], "kv_heads_per_stream": 8, "cache_copies": copies,
+            "us_per_call": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 2),
+            "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes,
+            "symbols_per_s": round(ntok * 2048 / t, 1), "device_errors": int(err.item()),
+            "encode": {"streams": 2 * n, "ms": round(te * 1e3, 3), "streams_per_s": round(2 * n / te, 1),
+                       "drift_rate_symbols": {"K": round(float(changed[:, 0].sum()) / (n * 1024), 5),
+                                              "V": round(float(changed[:, 1].sum()) / (n * 1024), 5)},
+                       "fallback_streams": int((rounds > 1).sum())}}
+
+
 def bf16_measurement(dq, torch, workloads, name: str, copies: int, dq_us: float, reps: int = 5) -> dict:
     """The uncompressed bf16 reference kernel on the same shape, rotating
     through `copies` bf16 caches (each far above the 256 MB MALL)."""
@@ -307,7 +371,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=0,
                     help="counter collection only: build and run this many layer caches (marked in the output)")
-    ap.add_argument("--section", choices=["encode", "bf16"], default=None,
+    ap.add_argument("--section", choices=["encode", "bf16", "token"], default=None,
                     help="profiling only: run just this measurement and print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (reference for HBM byte counters)")
@@ -337,6 +401,9 @@ def main() -> int:
 
     if args.section == "encode":
         print(json.dumps({"encode": encode_measurement(dq, torch, workloads)}), flush=True)
+        return 0
+    if args.section == "token":
+        print(json.dumps({"token_format": token_measurement(dq, torch, workloads)}), flush=True)
         return 0
     if args.section == "bf16":
         print(json.dumps({"bf16_reference": bf16_measurement(dq, torch, workloads, args.workload, copies=2,
@@ -444,6 +511,8 @@ def main() -> int:
         }
         result["bf16_reference"] = bf16_measurement(dq, torch, workloads, w.name, copies=2,
                                                     dq_us=per_call_s * 1e6)
+        torch.cuda.empty_cache()
+        result["token_format"] = token_measurement(dq, torch, workloads)
     if not args.no_cpu_baseline:
         import oracle
         tk = oracle.make_table(w.k_levels, w.container)

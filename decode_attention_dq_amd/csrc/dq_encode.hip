@@ -882,14 +882,20 @@ __global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a)
     const double s_star = smm > 0.0 ? smy / smm : 0.0;
     const double o_star = ybar - s_star * mbar;
 
-    // the container, then (o16, s16), at the token's slot
+    // the container, as dwords interleaved across the page's slots (dword j
+    // of slot po at row j of the page), zero-padded to whole dwords; then
+    // (o16, s16) at the slot
+    const int C4 = (C + 3) >> 2;
     wave_sync();
-    if (lane == 0) tok_rans_write(W.sym, sc, p, cnt, C, W.buf);
+    if (lane == 0) {
+        tok_rans_write(W.sym, sc, p, cnt, C, W.buf);
+        for (int k = C; k < 4 * C4; ++k) W.buf[k] = 0;
+    }
     wave_sync();
     const int page = slot / a.page_size, po = slot - page * a.page_size;
     const size_t idx = (size_t)page * a.page_size + po;
-    uint8_t* dst = a.cache[kv] + idx * C;
-    for (int k = lane; k < C; k += 64) dst[k] = W.buf[k];
+    uint32_t* dst = (uint32_t*)a.cache[kv] + (size_t)page * C4 * a.page_size + po;
+    for (int j = lane; j < C4; j += 64) dst[(size_t)j * a.page_size] = *(const uint32_t*)(W.buf + 4 * j);
     if (lane == 0) {
         a.meta[kv][2 * idx] = f64_to_f16_rne(o_star);
         a.meta[kv][2 * idx + 1] = f64_to_f16_rne(s_star);

@@ -10,13 +10,20 @@
 // of group g, decodes V head g together with K head g + 1 (two independent
 // rANS chains per lane), moves the V levels through an LDS transpose, and
 // accumulates p.v with each lane owning two channels of every query head.
-// Container bytes are read straight from HBM through a 4-byte window that is
-// refilled every 4 steps; the refill reads two aligned dwords clamped to the
-// container's last dword, so no read leaves the container.
+// Containers sit in the cache dword-interleaved across the slots of a page
+// (dword j of every slot in row j), so the 64 lanes of a wave read
+// neighbouring dwords of the same few rows and every cache line is shared
+// while it is resident. A lane reads its stream through a 4-byte window that
+// is refilled every 4 steps from three dwords loaded at the previous refill
+// (at most 4 bytes are consumed in between, so the window lies inside them);
+// each refill issues the loads for the next one, clamped to the container's
+// last row, so no read leaves the container.
 #include "dq_device.h"
 #include "dq_internal.h"
 #include "dq_sched.h"
 #include "dq_wave.h"
+
+#include <type_traits>
 
 namespace dq {
 namespace {
@@ -27,13 +34,15 @@ constexpr int kTile = 64;           // tokens per wave tile, one per lane
 constexpr int kGrp = 4;             // query heads per KV head held (GQA group <= 4)
 constexpr int kVtRowDw = kTile + 1; // dwords per row of the V level transpose (padded)
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
 struct TokShared {
     uint32_t tab[2][kTableSlots];                 // decode tables, K then V
-    float qt[kTokHeads][kHeadDim][kGrp];          // rotated queries [KV head][channel][head in group]
-    float qsum[kTokHeads][kGrp];                  // their sums over the channels
+    _Float16 qt[kTokHeads][kHeadDim][kGrp];       // rotated queries [KV head][channel][head in group]
+    float qsum[kTokHeads][kGrp];                  // their sums over the channels (fp32)
     union {
         struct {
-            uint32_t vt[kHeadDim / 4][kVtRowDw];  // V levels: row k holds channels 4k..4k+3, column = token
+            uint32_t vt[kHeadDim / 8][kVtRowDw];  // V levels, 4 bits: row k holds channels 8k..8k+7, column = token
             float w[kTile][kGrp];                 // p * s_v per token and head
         } wave[kWaves];
         struct {
@@ -46,27 +55,45 @@ struct TokShared {
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-// Stream state from the container at byte offset rel0 (of C bytes) of the
-// cache: the 3-byte flush, then the window at byte 3.
-__device__ __forceinline__ void grans_refill(RansLane& r, const uint32_t* __restrict__ base, uint32_t last) {
+// The three container dwords from byte a (aligned) on, the next refill's
+// source. Row r of a container is dword row0 + r * P of the cache.
+struct GWin {
+    uint32_t a, d0, d1, d2;
+};
+struct GSrc {
+    const uint32_t* base;   // the cache as dwords
+    uint32_t row0;          // dword index of the container's first dword
+    uint32_t stride;        // dwords between rows (the page size)
+    uint32_t last;          // index of the container's last row
+};
+__device__ __forceinline__ void gwin_load(GWin& g, const GSrc& src, uint32_t ptr) {
+    g.a = ptr & ~3u;
+    const uint32_t r = g.a >> 2;
+    g.d0 = src.base[src.row0 + min(r, src.last) * src.stride];
+    g.d1 = src.base[src.row0 + min(r + 1u, src.last) * src.stride];
+    g.d2 = src.base[src.row0 + min(r + 2u, src.last) * src.stride];
+}
+// Move the window past the consumed bytes (ptr - g.a is at most 7, so the
+// window's 4 bytes lie in g's dwords), then start the next dwords' loads.
+__device__ __forceinline__ void grans_refill(RansLane& r, GWin& g, const GSrc& src) {
     r.ptr += r.sel - kSel0;
-    const uint32_t a = r.ptr & ~3u;
-    const uint32_t lo = base[min(a, last) >> 2];
-    const uint32_t hi = base[min(a + 4u, last) >> 2];
+    const bool up = r.ptr - g.a >= 4u;
+    const uint32_t lo = up ? g.d1 : g.d0, hi = up ? g.d2 : g.d1;
     r.win = __builtin_amdgcn_alignbyte(hi, lo, r.ptr);
     r.sel = kSel0;
+    gwin_load(g, src, r.ptr);
 }
-__device__ __forceinline__ void grans_init(RansLane& r, const uint32_t* __restrict__ base, uint32_t rel0,
-                                           uint32_t last) {
-    r.ptr = rel0;
-    r.sel = kSel0;
-    grans_refill(r, base, last);
-    r.x = r.win & 0xFFFFFFu;
+// Stream state from the 3-byte flush at the container's start, then the
+// window at byte 3 (byte offsets count from the container's start).
+__device__ __forceinline__ void grans_init(RansLane& r, GWin& g, const GSrc& src) {
+    gwin_load(g, src, 0u);
+    r.ptr = 0u;
+    r.x = g.d0 & 0xFFFFFFu;
     r.sel = kSel0 + (uint32_t)kStateBytes;
-    grans_refill(r, base, last);
+    grans_refill(r, g, src);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void token_attn_kernel(TokAttnArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) {
     __shared__ TokShared S;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int b, split;
@@ -78,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void token_attn_kernel(TokAttnArgs a) 
 
     // ---- prologue: decode tables, rotated queries q~ = H q and their sums
     for (int i = tid; i < 2 * kTableSlots; i += kThreads) (&S.tab[0][0])[i] = a.entries[i];
-    for (int i = tid; i < kTokHeads * kHeadDim * kGrp; i += kThreads) (&S.qt[0][0][0])[i] = 0.0f;
+    for (int i = tid; i < kTokHeads * kHeadDim * kGrp; i += kThreads) (&S.qt[0][0][0])[i] = (_Float16)0.0f;
     if (tid < kTokHeads * kGrp) (&S.qsum[0][0])[tid] = 0.0f;
     __syncthreads();
     for (int h = wave; h < a.num_q_heads; h += kWaves) {
@@ -95,8 +122,8 @@ __global__ __launch_bounds__(kThreads, 2) void token_attn_kernel(TokAttnArgs a) 
         }
         fwht128_f32(v0, v1, lane);
         const int g = h / G, hh = h - g * G;
-        S.qt[g][lane][hh] = v0;
-        S.qt[g][lane + 64][hh] = v1;
+        S.qt[g][lane][hh] = (_Float16)v0;
+        S.qt[g][lane + 64][hh] = (_Float16)v1;
         const float sum = wave_sum(v0 + v1);
         if (lane == 0) S.qsum[g][hh] = sum;
     }
@@ -117,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void token_attn_kernel(TokAttnArgs a) 
     float mrun = -INFINITY, lrun = 0.0f;   // lane 4g + hh: running max and sum of head (g, hh)
     bool bad = false;
     auto& Wv = S.u.wave[wave];
-    const uint32_t vrow = (uint32_t)lane >> 1, vsh = ((uint32_t)lane & 1u) * 16u;
+    const uint32_t vrow = (uint32_t)lane >> 2, vsh = ((uint32_t)lane & 3u) * 8u;
 
     for (int t0 = start + wave * kTile; t0 < end; t0 += kWaves * kTile) {
         const int t = t0 + lane;
@@ -128,108 +155,146 @@ __global__ __launch_bounds__(kThreads, 2) void token_attn_kernel(TokAttnArgs a) 
         const uint32_t km = ((const uint32_t*)a.k_meta)[idx], vm = ((const uint32_t*)a.v_meta)[idx];
         const float ok = f16_to_f32((uint16_t)(km & 0xFFFFu)), sk = f16_to_f32((uint16_t)(km >> 16));
         const float ov = f16_to_f32((uint16_t)(vm & 0xFFFFu)), sv = f16_to_f32((uint16_t)(vm >> 16));
-        const uint32_t relk = idx * (uint32_t)a.ck, relv = idx * (uint32_t)a.cv;
-        const uint32_t lastk = (relk + (uint32_t)a.ck - 1u) & ~3u, lastv = (relv + (uint32_t)a.cv - 1u) & ~3u;
+        const uint32_t ck4 = ((uint32_t)a.ck + 3u) >> 2, cv4 = ((uint32_t)a.cv + 3u) >> 2;
+        const uint32_t pg = (uint32_t)page * (uint32_t)a.page_size, po = idx - pg;
+        const GSrc sk_ = {kbase, pg * ck4 + po, (uint32_t)a.page_size, ck4 - 1u};
+        const GSrc sv_ = {vbase, pg * cv4 + po, (uint32_t)a.page_size, cv4 - 1u};
         RansLane rk, rv;
-        grans_init(rk, kbase, relk, lastk);
-        grans_init(rv, vbase, relv, lastv);
+        GWin gk, gv;
+        grans_init(rk, gk, sk_);
+        grans_init(rv, gv, sv_);
 
         // K head 0 alone
         float s4[kGrp] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
-            if (c4) grans_refill(rk, kbase, lastk);
+            if (c4) grans_refill(rk, gk, sk_);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t ek = rans_lookup(rk, tabK, maskK);
                 rans_advance(rk, ek, (uint32_t)a.pk);
                 const float mk = (float)(ek >> 28);
-                const float4_t q = *(const float4_t*)&S.qt[0][4 * c4 + i][0];
+                const half4_t q = *(const half4_t*)&S.qt[0][4 * c4 + i][0];
 #pragma unroll
-                for (int hh = 0; hh < kGrp; ++hh) s4[hh] += q[hh] * mk;
+                for (int hh = 0; hh < kGrp; ++hh) s4[hh] += (float)q[hh] * mk;
             }
         }
-        grans_refill(rk, kbase, lastk);
+        grans_refill(rk, gk, sk_);
 
-#pragma unroll
+        // KV heads in order: the softmax of group g, V head g (fused with K
+        // head g + 1 while there is one), the group's p.v. The loop is not
+        // unrolled (the kernel stays small in the instruction cache); acc[0]
+        // holds the current group's accumulators and the array rotates by one
+        // group per head, back to its order after the eighth.
+#pragma unroll 1
         for (int g = 0; g < kTokHeads; ++g) {
-            // softmax of group g over this tile (log2 domain), and the weights of its p.v
             float4_t wv;
 #pragma unroll
             for (int hh = 0; hh < kGrp; ++hh) {
+                const int hl = 4 * g + hh;
                 const float L = valid ? (ok * S.qsum[g][hh] + sk * s4[hh]) * cs : -INFINITY;
                 const float mt = wave_max_uniform(L);
-                const float mo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), 4 * g + hh));
+                const float mo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), hl));
                 const float mn = fmaxf(mo, mt);
                 const float fac = exp2f(mo - mn);
                 const float p = valid ? exp2f(L - mn) : 0.0f;
-                const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lrun), 4 * g + hh));
+                const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lrun), hl));
                 const float ln = lo * fac + wave_sum_uniform(p);
                 const float os = wave_sum_uniform(p * ov);
-                acc[g][hh][0] = acc[g][hh][0] * fac + os;
-                acc[g][hh][1] = acc[g][hh][1] * fac + os;
-                mrun = lane == 4 * g + hh ? mn : mrun;
-                lrun = lane == 4 * g + hh ? ln : lrun;
+                acc[0][hh][0] = acc[0][hh][0] * fac + os;
+                acc[0][hh][1] = acc[0][hh][1] * fac + os;
+                mrun = lane == hl ? mn : mrun;
+                lrun = lane == hl ? ln : lrun;
                 wv[hh] = p * sv;
             }
             *(float4_t*)&Wv.w[lane][0] = wv;
 
-            // V head g, fused with K head g + 1
             s4[0] = s4[1] = s4[2] = s4[3] = 0.0f;
-            for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
-                if (c4) {
-                    grans_refill(rv, vbase, lastv);
-                    if (g + 1 < kTokHeads) grans_refill(rk, kbase, lastk);
-                }
-                uint32_t packed = 0;
+            if (g + 1 < kTokHeads) {
+                const _Float16* qn = &S.qt[g + 1][0][0];
+#pragma unroll 1
+                for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
+                    uint32_t packed = 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t ev = rans_lookup(rv, tabV, maskV);
-                    uint32_t ek = 0;
-                    if (g + 1 < kTokHeads) ek = rans_lookup(rk, tabK, maskK);
-                    rans_advance(rv, ev, (uint32_t)a.pv);
-                    if (g + 1 < kTokHeads) rans_advance(rk, ek, (uint32_t)a.pk);
-                    packed |= (ev >> 28) << (8 * i);
-                    if (g + 1 < kTokHeads) {
-                        const float mk = (float)(ek >> 28);
-                        const float4_t q = *(const float4_t*)&S.qt[g + 1][4 * c4 + i][0];
+                    for (int half = 0; half < 2; ++half) {
+                        if (c8 | half) {
+                            grans_refill(rv, gv, sv_);
+                            grans_refill(rk, gk, sk_);
+                        }
 #pragma unroll
-                        for (int hh = 0; hh < kGrp; ++hh) s4[hh] += q[hh] * mk;
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t ev = rans_lookup(rv, tabV, maskV);
+                            const uint32_t ek = rans_lookup(rk, tabK, maskK);
+                            rans_advance(rv, ev, (uint32_t)a.pv);
+                            rans_advance(rk, ek, (uint32_t)a.pk);
+                            packed |= (ev >> 28) << (4 * (4 * half + i));
+                            const float mk = (float)(ek >> 28);
+                            const half4_t q = *(const half4_t*)(qn + (8 * c8 + 4 * half + i) * kGrp);
+#pragma unroll
+                            for (int hh = 0; hh < kGrp; ++hh) s4[hh] += (float)q[hh] * mk;
+                        }
                     }
+                    Wv.vt[c8][lane] = packed;
                 }
-                Wv.vt[c4][lane] = packed;
+                grans_refill(rk, gk, sk_);
+            } else {
+#pragma unroll 1
+                for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
+                    uint32_t packed = 0;
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        if (c8 | half) grans_refill(rv, gv, sv_);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t ev = rans_lookup(rv, tabV, maskV);
+                            rans_advance(rv, ev, (uint32_t)a.pv);
+                            packed |= (ev >> 28) << (4 * (4 * half + i));
+                        }
+                    }
+                    Wv.vt[c8][lane] = packed;
+                }
             }
-            grans_refill(rv, vbase, lastv);
-            if (g + 1 < kTokHeads) grans_refill(rk, kbase, lastk);
+            grans_refill(rv, gv, sv_);
             wave_lds_sync();
 
             // p.v of V head g: lane owns channels 2 lane and 2 lane + 1
+#pragma unroll 4
             for (int j = 0; j < kTile; ++j) {
                 const uint32_t d = Wv.vt[vrow][j] >> vsh;
-                const float m0 = (float)(d & 255u), m1 = (float)((d >> 8) & 255u);
+                const float m0 = (float)(d & 15u), m1 = (float)((d >> 4) & 15u);
                 const float4_t w4 = *(const float4_t*)&Wv.w[j][0];
 #pragma unroll
                 for (int hh = 0; hh < kGrp; ++hh) {
-                    acc[g][hh][0] += w4[hh] * m0;
-                    acc[g][hh][1] += w4[hh] * m1;
+                    acc[0][hh][0] += w4[hh] * m0;
+                    acc[0][hh][1] += w4[hh] * m1;
                 }
             }
             wave_lds_sync();
+            // rotate: the next group's accumulators to the front
+            float first[kGrp][2];
+#pragma unroll
+            for (int hh = 0; hh < kGrp; ++hh) first[hh][0] = acc[0][hh][0], first[hh][1] = acc[0][hh][1];
+#pragma unroll
+            for (int gg = 0; gg + 1 < kTokHeads; ++gg)
+#pragma unroll
+                for (int hh = 0; hh < kGrp; ++hh) acc[gg][hh][0] = acc[gg + 1][hh][0], acc[gg][hh][1] = acc[gg + 1][hh][1];
+#pragma unroll
+            for (int hh = 0; hh < kGrp; ++hh) acc[kTokHeads - 1][hh][0] = first[hh][0], acc[kTokHeads - 1][hh][1] = first[hh][1];
         }
         // both streams must end in the initial state having read no byte past C
-        const bool okk = rk.x == kStateLow && rk.ptr + (rk.sel - kSel0) - relk <= (uint32_t)a.ck;
-        const bool okv = rv.x == kStateLow && rv.ptr + (rv.sel - kSel0) - relv <= (uint32_t)a.cv;
+        const bool okk = rk.x == kStateLow && rk.ptr + (rk.sel - kSel0) <= (uint32_t)a.ck;
+        const bool okv = rv.x == kStateLow && rv.ptr + (rv.sel - kSel0) <= (uint32_t)a.cv;
         bad = bad || (valid && !(okk && okv));
     }
     if (__any(bad) && lane == 0 && a.err_word) atomicOr(a.err_word, DQ_DEVERR_DECODE);
 
     // ---- combine the 4 waves' partials per KV head and write them
     __syncthreads();
-#pragma unroll
-    for (int g = 0; g < kTokHeads; ++g) {
+    auto combine = [&](auto gtag, const float (&ag)[kGrp][2]) {
+        constexpr int g = decltype(gtag)::value;
 #pragma unroll
         for (int hh = 0; hh < kGrp; ++hh) {
-            S.u.red.acc[wave][hh][2 * lane] = acc[g][hh][0];
-            S.u.red.acc[wave][hh][2 * lane + 1] = acc[g][hh][1];
+            S.u.red.acc[wave][hh][2 * lane] = ag[hh][0];
+            S.u.red.acc[wave][hh][2 * lane + 1] = ag[hh][1];
         }
         const float mg = __shfl(mrun, 4 * g + (lane & 3)), lg = __shfl(lrun, 4 * g + (lane & 3));
         if (lane < kGrp) {
@@ -261,7 +326,15 @@ __global__ __launch_bounds__(kThreads, 2) void token_attn_kernel(TokAttnArgs a) 
             part[4 + 64 + lane] = o1;
         }
         __syncthreads();
-    }
+    };
+    combine(std::integral_constant<int, 0>{}, acc[0]);
+    combine(std::integral_constant<int, 1>{}, acc[1]);
+    combine(std::integral_constant<int, 2>{}, acc[2]);
+    combine(std::integral_constant<int, 3>{}, acc[3]);
+    combine(std::integral_constant<int, 4>{}, acc[4]);
+    combine(std::integral_constant<int, 5>{}, acc[5]);
+    combine(std::integral_constant<int, 6>{}, acc[6]);
+    combine(std::integral_constant<int, 7>{}, acc[7]);
 }
 
 }  // namespace

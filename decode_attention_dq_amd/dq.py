@@ -409,6 +409,11 @@ def dq_decode_symbols(tables: Tables, which: int, containers, symbols_out, err_w
 TOKEN_HEADS, TOKEN_VALUES = 8, 1024
 
 
+def token_cache_shape(pages: int, page_size: int, container: int) -> tuple:
+    """Shape of a per-token cache: [pages][ceil(C/4)][page_size][4] bytes."""
+    return (int(pages), (int(container) + 3) // 4, int(page_size), 4)
+
+
 def dq_token_table_describe(params: dq_table_params) -> dict:
     info = dq_table_info()
     _check(_lib.dq_token_table_describe(ctypes.byref(params), ctypes.byref(info)), "dq_token_table_describe")
@@ -422,7 +427,8 @@ def dq_token_tables_init(keys: dq_table_params, values: dq_table_params) -> Tabl
 def dq_encode_tokens(tables: Tables, k, v, slot_mapping, k_cache, v_cache, k_meta, v_meta, page_size: int,
                      drift_stats=None, err_word=None, stream=None) -> None:
     """k, v: [num_tokens][8][128] float32 or bfloat16; caches uint8
-    [pages][page_size][C]; metadata 16-bit [pages][page_size][2] (o16, s16);
+    [pages][ceil(C/4)][page_size][4] (containers dword-interleaved across a
+    page's slots); metadata 16-bit [pages][page_size][2] (o16, s16);
     drift_stats optional int32/uint32 [num_tokens][2]."""
     import torch
     if k.dtype != v.dtype or k.shape != v.shape or k.dim() != 3 or tuple(k.shape[1:]) != (TOKEN_HEADS, HEAD_DIM):

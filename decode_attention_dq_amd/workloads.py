@@ -38,6 +38,7 @@ class Workload:
     window: int = 0              # most recent tokens kept uncompressed in bf16
     key_offset: float = 0.0      # std of a per-(layer, KV head, channel) offset added to the keys
     means: bool = False          # keys written in 128-token blocks with their channel means
+    token: bool = False          # the per-token format: one 1024-value stream per token over the 8 KV heads
 
     @property
     def cv(self) -> int:
@@ -57,6 +58,9 @@ WORKLOADS = {
                                       window=128, config_id=6),
     # keys with a strong channel mean, removed per 128-token block (the paper's key preprocessing)
     "mean_qwen3_8b": Workload("mean_qwen3_8b", 128, 32, 8, 8192, key_offset=2.0, means=True, config_id=7),
+    # the paper's default format: 331 / 231-byte per-token containers, 8 / 6 levels
+    "token_qwen3_8b": Workload("token_qwen3_8b", 128, 32, 8, 8192, container=331, container_v=231, token=True,
+                               config_id=8),
 }
 
 
@@ -183,6 +187,34 @@ def build_cache(dq, tables, w: Workload, layer: int = 0, keep_stats: bool = Fals
         c.win_k, c.win_v = wk, wv
         c.win_lens = torch.as_tensor((full - lens).astype(np.int32), device=device)
     return c
+
+
+def build_token_cache(dq, tables, w: Workload, layer: int = 0, keep_stats: bool = False, device="cuda") -> Cache:
+    """Encode every sequence of one layer into a per-token cache: containers
+    [pages][ceil(C/4)][P][4] (dword-interleaved across a page's slots), and
+    (o16, s16) metadata [pages][P][2] in the norm fields."""
+    import torch
+    lens = context_lengths(w)
+    bt, total = page_plan(w, lens)
+    P = w.page_size
+    kc = torch.zeros(dq.token_cache_shape(total, P, w.container), dtype=torch.uint8, device=device)
+    vc = torch.zeros(dq.token_cache_shape(total, P, w.cv), dtype=torch.uint8, device=device)
+    km = torch.zeros((total, P, 2), dtype=torch.int16, device=device)
+    vm = torch.zeros((total, P, 2), dtype=torch.int16, device=device)
+    stats = []
+    for b in range(w.batch):
+        T = int(lens[b])
+        slots = torch.as_tensor(slot_mapping(bt[b:b + 1], lens[b:b + 1], P), device=device)
+        k = kv_rows(w, layer, synth.T_K, b, T, device)
+        v = kv_rows(w, layer, synth.T_V, b, T, device)
+        st = torch.zeros((T, 2), dtype=torch.int32, device=device) if keep_stats else None
+        if T:
+            dq.dq_encode_tokens(tables, k, v, slots, kc, vc, km, vm, P, drift_stats=st)
+        if keep_stats:
+            stats.append(st)
+        del k, v
+    return Cache(kc, vc, km, vm, torch.as_tensor(bt, device=device), torch.as_tensor(lens, device=device), lens,
+                 torch.cat(stats) if keep_stats else None)
 
 
 def build_bf16_cache(w: Workload, layer: int = 0, device="cuda"):

@@ -351,8 +351,10 @@ int dq_token_table_describe(const dq_table_params* params, dq_table_info* out);
  *   k, v          [num_tokens][8][128], DQ_DTYPE_F32 or DQ_DTYPE_BF16; finite
  *   slot_mapping  int32 [num_tokens]: slot = page * page_size + offset; < 0
  *                 skips the token
- *   k_cache       uint8 [pages][page_size][C_K] (C_V for v_cache), written at
- *                 each slot; nothing else is touched
+ *   k_cache       uint8 [pages][ceil(C_K/4)][page_size][4] (C_V for v_cache):
+ *                 each container as dwords interleaved across the page's slots,
+ *                 dword j of slot s at [page][j][s], zero-padded to whole
+ *                 dwords; written at each slot, nothing else is touched
  *   k_meta        fp16 bits [pages][page_size][2]: (o16, s16) per slot
  *   drift_stats   optional uint32 [num_tokens][2] (K, V): symbols changed by
  *                 drift | rounds << 16

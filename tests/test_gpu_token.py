@@ -34,6 +34,22 @@ def _tokens(seed, tensor, n, part=0, bf16=False):
                              bf16=bf16)
 
 
+def _to_pages(conts, P):
+    """Per-slot containers [pages * P][C] -> the cache layout [pages][C4][P][4]
+    (dword j of slot s at [page][j][s], zero padding to whole dwords)."""
+    n, C = conts.shape
+    C4 = -(-C // 4)
+    pad = np.zeros((n, 4 * C4), np.uint8)
+    pad[:, :C] = conts
+    return np.ascontiguousarray(pad.reshape(n // P, P, C4, 4).transpose(0, 2, 1, 3))
+
+
+def _from_pages(cache, C):
+    """The inverse of _to_pages: [pages][C4][P][4] -> [pages * P][4 C4]."""
+    pages, C4, P, _ = cache.shape
+    return cache.transpose(0, 2, 1, 3).reshape(pages * P, 4 * C4)
+
+
 def _layout(lens, P, perm_seed):
     """Block table and the slot of every token, pages handed out per sequence."""
     npages = [max(1, -(-T // P)) for T in lens]
@@ -65,8 +81,8 @@ def test_token_encode_bit_exact(setup, bf16):
     slots = np.random.default_rng(2).permutation(n + 20)[:n].astype(np.int32)
     slots[11] = -1
     pages = -(-(n + 20) // P)
-    kc = torch.zeros((pages, P, K_CFG[1]), dtype=torch.uint8, device="cuda")
-    vc = torch.zeros((pages, P, V_CFG[1]), dtype=torch.uint8, device="cuda")
+    kc = torch.zeros(dq.token_cache_shape(pages, P, K_CFG[1]), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros(dq.token_cache_shape(pages, P, V_CFG[1]), dtype=torch.uint8, device="cuda")
     km = torch.zeros((pages, P, 2), dtype=torch.int16, device="cuda")
     vm = torch.zeros_like(km)
     ds = torch.zeros((n, 2), dtype=torch.int32, device="cuda")
@@ -79,7 +95,9 @@ def test_token_encode_bit_exact(setup, bf16):
     assert int(err.item()) == 0
     rk = oracle.encode_tokens(k.astype(np.float64), tk)
     rv = oracle.encode_tokens(v.astype(np.float64), tv)
-    kc, vc = kc.cpu().numpy().reshape(-1, K_CFG[1]), vc.cpu().numpy().reshape(-1, V_CFG[1])
+    kc, vc = _from_pages(kc.cpu().numpy(), K_CFG[1]), _from_pages(vc.cpu().numpy(), V_CFG[1])
+    assert not kc[:, K_CFG[1]:].any() and not vc[:, V_CFG[1]:].any()       # padding bytes are zero
+    kc, vc = kc[:, :K_CFG[1]], vc[:, :V_CFG[1]]
     km, vm = km.cpu().numpy().view(np.uint16).reshape(-1, 2), vm.cpu().numpy().view(np.uint16).reshape(-1, 2)
     ds = ds.cpu().numpy().view(np.uint32)
     live = slots >= 0
@@ -142,7 +160,7 @@ def _attention_case(setup, lens, G, P=16, seed=5, perm_seed=3):
     for b, T in enumerate(lens):
         if T:
             ref[b] = oracle.attention(q[b:b + 1], [kh[b]], [vh[b]])[0]
-    dev = dict(q=_dev(q).to(torch.bfloat16), kc=_dev(kc.reshape(pages, P, -1)), vc=_dev(vc.reshape(pages, P, -1)),
+    dev = dict(q=_dev(q).to(torch.bfloat16), kc=_dev(_to_pages(kc, P)), vc=_dev(_to_pages(vc, P)),
                km=_dev(km.view(np.int16).reshape(pages, P, 2)), vm=_dev(vm.view(np.int16).reshape(pages, P, 2)),
                bt=_dev(bt), lens=_dev(np.asarray(lens, np.int32)))
     return dq, tabs, dev, ref, P
@@ -182,7 +200,7 @@ def test_token_attention_split_counts(setup, splits):
 def test_token_attention_flags_corrupt_stream(setup):
     lens = [100]
     dq, tabs, d, ref, P = _attention_case(setup, lens, 1, seed=7)
-    d["kc"][0, 3, 0] ^= 0x5A
+    d["kc"][0, 0, 3, 0] ^= 0x5A                # first byte (state) of slot 3 of page 0
     out, err = _run(dq, tabs, d, lens, P)
     assert err & dq.DQ_DEVERR_DECODE
 
@@ -193,8 +211,8 @@ def test_token_encode_then_attend(setup):
     dq, tk, tv, tabs = setup
     lens, P, G = [200, 333], 32, 4
     bt, pages, slots = _layout(lens, P, 4)
-    kc = torch.zeros((pages, P, K_CFG[1]), dtype=torch.uint8, device="cuda")
-    vc = torch.zeros((pages, P, V_CFG[1]), dtype=torch.uint8, device="cuda")
+    kc = torch.zeros(dq.token_cache_shape(pages, P, K_CFG[1]), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros(dq.token_cache_shape(pages, P, V_CFG[1]), dtype=torch.uint8, device="cuda")
     km = torch.zeros((pages, P, 2), dtype=torch.int16, device="cuda")
     vm = torch.zeros_like(km)
     kh, vh = [], []
