@@ -12,11 +12,12 @@ namespace {
 // or, for partials in the original domain (ROTATED false),
 // out = (sum_s acc_s 2^(m_s - M)) / (sum_s l_s 2^(m_s - M)). The splits are
 // the ceil(T_b / split_len) that hold tokens of sequence b, plus the window
-// slot when there is one. 4 waves share them (wave w takes the w-th, the
-// (w + 4)-th, ...), each lane two channels; the loads of different splits are
-// independent, so many are in flight at once.
-constexpr int kMergeWaves = 4;
-template <bool ROTATED>
+// slot when there is one. W waves share them (wave w takes the w-th, the
+// (w + W)-th, ...), each lane two channels; the loads of different splits are
+// independent, so many are in flight at once. W = 4 waves per row, or 16 when
+// there are few rows with many splits (a long single sequence), so that each
+// wave walks fewer splits one after another.
+template <bool ROTATED, int kMergeWaves>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
     __shared__ float red[kMergeWaves][132];
     const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -72,10 +73,18 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int rows, bool rotated, hipStream_t s) {
-    if (rotated)
-        hipLaunchKernelGGL(merge_kernel<true>, dim3(rows), dim3(64 * kMergeWaves), 0, s, a);
-    else
-        hipLaunchKernelGGL(merge_kernel<false>, dim3(rows), dim3(64 * kMergeWaves), 0, s, a);
+    const bool wide = rows < 1024 && a.slot_count > 32;
+    if (wide) {
+        if (rotated)
+            hipLaunchKernelGGL((merge_kernel<true, 16>), dim3(rows), dim3(64 * 16), 0, s, a);
+        else
+            hipLaunchKernelGGL((merge_kernel<false, 16>), dim3(rows), dim3(64 * 16), 0, s, a);
+    } else {
+        if (rotated)
+            hipLaunchKernelGGL((merge_kernel<true, 4>), dim3(rows), dim3(64 * 4), 0, s, a);
+        else
+            hipLaunchKernelGGL((merge_kernel<false, 4>), dim3(rows), dim3(64 * 4), 0, s, a);
+    }
     return hipGetLastError();
 }
 
