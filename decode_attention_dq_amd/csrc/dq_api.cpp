@@ -212,6 +212,9 @@ void fill_enc_table(const dq_table_info& t, dq::EncTable* e) {
     for (int j = 0; j + 1 < t.levels; ++j) e->bounds[j] = t.bounds[j];
 }
 
+// Decode entries; bits 0..7 hold the fp16 high byte of the centred level
+// m - (M-1)/2 (its low byte is zero for M <= 9). The per-token kernel folds
+// the centre into the grid offset: o + s m = (o + s (M-1)/2) + s (m - (M-1)/2).
 void fill_entries(const dq_table_info& t, uint32_t* ent) {
     const uint32_t total = 1u << t.prob_bits;
     for (int m = 0; m < t.levels; ++m) {
@@ -632,6 +635,8 @@ int dq_token_decode_attention(const dq_tables* t, const void* q, int q_dtype, co
     a.cv = t->info[1].container;
     a.pk = t->info[0].prob_bits;
     a.pv = t->info[1].prob_bits;
+    a.half_k = 0.5f * (float)(t->info[0].levels - 1);
+    a.half_v = 0.5f * (float)(t->info[1].levels - 1);
     a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
     a.entries = t->d_entries;
     a.partials = (float*)workspace;

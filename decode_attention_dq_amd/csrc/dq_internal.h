@@ -139,6 +139,7 @@ struct TokAttnArgs {
     int batch, num_q_heads, group, max_pages_per_seq, page_size, log2p;
     int num_splits, split_len, slot_count, token_cap;
     int ck, cv, pk, pv;
+    float half_k, half_v;               // (M - 1) / 2: the entries carry centred levels
     float softmax_scale;
     const uint32_t* entries;            // [2][kTableSlots] decode tables (K then V)
     float* partials;                    // [batch][Hq][slot_count][kPartStride]

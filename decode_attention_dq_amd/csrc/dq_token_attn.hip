@@ -34,16 +34,22 @@ constexpr int kTile = 64;           // tokens per wave tile, one per lane
 constexpr int kGrp = 4;             // query heads per KV head held (GQA group <= 4)
 constexpr int kVtRowDw = kTile + 1; // dwords per row of the V level transpose (padded)
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
+// Products run on v_dot2_f32_f16 (two fp16 products added into fp32): the
+// logits over channel pairs (queries x key levels), p.v over token pairs
+// (weights x value levels). Levels enter centred, m - (M-1)/2, as fp16 whose
+// high byte is the decode entry's level byte (the low byte is zero); the
+// centre joins the offset, so the offset is near the values' mean and the
+// products carry only the centred part.
 struct TokShared {
     uint32_t tab[2][kTableSlots];                 // decode tables, K then V
-    _Float16 qt[kTokHeads][kHeadDim][kGrp];       // rotated queries [KV head][channel][head in group]
+    half2_t qt[kTokHeads][kHeadDim / 2][kGrp];    // rotated queries [KV head][channel pair][head in group]
     float qsum[kTokHeads][kGrp];                  // their sums over the channels (fp32)
     union {
         struct {
-            uint32_t vt[kHeadDim / 8][kVtRowDw];  // V levels, 4 bits: row k holds channels 8k..8k+7, column = token
-            float w[kTile][kGrp];                 // p * s_v per token and head
+            uint32_t vt[kHeadDim / 4][kVtRowDw];  // V level bytes: row k holds channels 4k..4k+3, column = token
+            half2_t w[kTile / 2][kGrp];           // p * s_v per token pair and head
         } wave[kWaves];
         struct {
             float acc[kWaves][kGrp][kHeadDim];
@@ -105,7 +111,7 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
 
     // ---- prologue: decode tables, rotated queries q~ = H q and their sums
     for (int i = tid; i < 2 * kTableSlots; i += kThreads) (&S.tab[0][0])[i] = a.entries[i];
-    for (int i = tid; i < kTokHeads * kHeadDim * kGrp; i += kThreads) (&S.qt[0][0][0])[i] = (_Float16)0.0f;
+    for (int i = tid; i < kTokHeads * kHeadDim / 2 * kGrp; i += kThreads) (&S.qt[0][0][0])[i] = half2_t{0, 0};
     if (tid < kTokHeads * kGrp) (&S.qsum[0][0])[tid] = 0.0f;
     __syncthreads();
     for (int h = wave; h < a.num_q_heads; h += kWaves) {
@@ -122,8 +128,12 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
         }
         fwht128_f32(v0, v1, lane);
         const int g = h / G, hh = h - g * G;
-        S.qt[g][lane][hh] = (_Float16)v0;
-        S.qt[g][lane + 64][hh] = (_Float16)v1;
+        // lanes 2k, 2k + 1 hold channels 2k, 2k + 1: one half2 per even lane
+        const float o0 = __shfl_xor(v0, 1), o1 = __shfl_xor(v1, 1);
+        if ((lane & 1) == 0) {
+            S.qt[g][lane >> 1][hh] = half2_t{(_Float16)v0, (_Float16)o0};
+            S.qt[g][(lane + 64) >> 1][hh] = half2_t{(_Float16)v1, (_Float16)o1};
+        }
         const float sum = wave_sum(v0 + v1);
         if (lane == 0) S.qsum[g][hh] = sum;
     }
@@ -144,7 +154,12 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
     float mrun = -INFINITY, lrun = 0.0f;   // lane 4g + hh: running max and sum of head (g, hh)
     bool bad = false;
     auto& Wv = S.u.wave[wave];
-    const uint32_t vrow = (uint32_t)lane >> 2, vsh = ((uint32_t)lane & 3u) * 8u;
+    // p.v operands: channel 2 lane sits in byte 2 (lane & 1) of row lane / 2 of
+    // the transpose; the selectors pair that byte of tokens t and t + 1 into
+    // the high bytes of an fp16 pair
+    const uint32_t vrow = (uint32_t)lane >> 1, vb = ((uint32_t)lane & 1u) * 2u;
+    const uint32_t vsel0 = 0x000C000Cu | (vb << 8) | ((vb + 4u) << 24);
+    const uint32_t vsel1 = vsel0 + 0x01000100u;
 
     for (int t0 = start + wave * kTile; t0 < end; t0 += kWaves * kTile) {
         const int t = t0 + lane;
@@ -153,8 +168,10 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
         const int page = a.block_table[(size_t)b * a.max_pages_per_seq + (tt >> a.log2p)];
         const uint32_t idx = (uint32_t)page * (uint32_t)a.page_size + (uint32_t)(tt & (a.page_size - 1));
         const uint32_t km = ((const uint32_t*)a.k_meta)[idx], vm = ((const uint32_t*)a.v_meta)[idx];
-        const float ok = f16_to_f32((uint16_t)(km & 0xFFFFu)), sk = f16_to_f32((uint16_t)(km >> 16));
-        const float ov = f16_to_f32((uint16_t)(vm & 0xFFFFu)), sv = f16_to_f32((uint16_t)(vm >> 16));
+        // centred grid: y_hat = (o + s (M-1)/2) + s (m - (M-1)/2), the products take the centred levels
+        const float sk = f16_to_f32((uint16_t)(km >> 16)), sv = f16_to_f32((uint16_t)(vm >> 16));
+        const float ok = f16_to_f32((uint16_t)(km & 0xFFFFu)) + sk * a.half_k;
+        const float ov = f16_to_f32((uint16_t)(vm & 0xFFFFu)) + sv * a.half_v;
         const uint32_t ck4 = ((uint32_t)a.ck + 3u) >> 2, cv4 = ((uint32_t)a.cv + 3u) >> 2;
         const uint32_t pg = (uint32_t)page * (uint32_t)a.page_size, po = idx - pg;
         const GSrc sk_ = {kbase, pg * ck4 + po, (uint32_t)a.page_size, ck4 - 1u};
@@ -169,13 +186,15 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
         for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
             if (c4) grans_refill(rk, gk, sk_);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t ek = rans_lookup(rk, tabK, maskK);
-                rans_advance(rk, ek, (uint32_t)a.pk);
-                const float mk = (float)(ek >> 28);
-                const half4_t q = *(const half4_t*)&S.qt[0][4 * c4 + i][0];
+            for (int i = 0; i < 4; i += 2) {
+                const uint32_t e0 = rans_lookup(rk, tabK, maskK);
+                rans_advance(rk, e0, (uint32_t)a.pk);
+                const uint32_t e1 = rans_lookup(rk, tabK, maskK);
+                rans_advance(rk, e1, (uint32_t)a.pk);
+                const half2_t mm = __builtin_bit_cast(half2_t, pack_levels(e0, e1));
+                const half2_t* q = &S.qt[0][(4 * c4 + i) >> 1][0];
 #pragma unroll
-                for (int hh = 0; hh < kGrp; ++hh) s4[hh] += (float)q[hh] * mk;
+                for (int hh = 0; hh < kGrp; ++hh) s4[hh] = __builtin_amdgcn_fdot2(q[hh], mm, s4[hh], false);
             }
         }
         grans_refill(rk, gk, sk_);
@@ -206,66 +225,72 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                 lrun = lane == hl ? ln : lrun;
                 wv[hh] = p * sv;
             }
-            *(float4_t*)&Wv.w[lane][0] = wv;
+#pragma unroll
+            for (int hh = 0; hh < kGrp; ++hh) {
+                const float wn = __shfl_xor(wv[hh], 1);   // the pair partner's weight (token lane ^ 1)
+                if ((lane & 1) == 0) Wv.w[lane >> 1][hh] = half2_t{(_Float16)wv[hh], (_Float16)wn};
+            }
 
             s4[0] = s4[1] = s4[2] = s4[3] = 0.0f;
             if (g + 1 < kTokHeads) {
-                const _Float16* qn = &S.qt[g + 1][0][0];
+                const half2_t* qn = &S.qt[g + 1][0][0];
 #pragma unroll 1
-                for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
-                    uint32_t packed = 0;
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        if (c8 | half) {
-                            grans_refill(rv, gv, sv_);
-                            grans_refill(rk, gk, sk_);
-                        }
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const uint32_t ev = rans_lookup(rv, tabV, maskV);
-                            const uint32_t ek = rans_lookup(rk, tabK, maskK);
-                            rans_advance(rv, ev, (uint32_t)a.pv);
-                            rans_advance(rk, ek, (uint32_t)a.pk);
-                            packed |= (ev >> 28) << (4 * (4 * half + i));
-                            const float mk = (float)(ek >> 28);
-                            const half4_t q = *(const half4_t*)(qn + (8 * c8 + 4 * half + i) * kGrp);
-#pragma unroll
-                            for (int hh = 0; hh < kGrp; ++hh) s4[hh] += (float)q[hh] * mk;
-                        }
+                for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
+                    if (c4) {
+                        grans_refill(rv, gv, sv_);
+                        grans_refill(rk, gk, sk_);
                     }
-                    Wv.vt[c8][lane] = packed;
+                    uint32_t ev[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        ev[i] = rans_lookup(rv, tabV, maskV);
+                        const uint32_t e0 = rans_lookup(rk, tabK, maskK);
+                        rans_advance(rv, ev[i], (uint32_t)a.pv);
+                        rans_advance(rk, e0, (uint32_t)a.pk);
+                        ev[i + 1] = rans_lookup(rv, tabV, maskV);
+                        const uint32_t e1 = rans_lookup(rk, tabK, maskK);
+                        rans_advance(rv, ev[i + 1], (uint32_t)a.pv);
+                        rans_advance(rk, e1, (uint32_t)a.pk);
+                        const half2_t mm = __builtin_bit_cast(half2_t, pack_levels(e0, e1));
+                        const half2_t* q = qn + ((4 * c4 + i) >> 1) * kGrp;
+#pragma unroll
+                        for (int hh = 0; hh < kGrp; ++hh) s4[hh] = __builtin_amdgcn_fdot2(q[hh], mm, s4[hh], false);
+                    }
+                    Wv.vt[c4][lane] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(ev[3], ev[2], 0x0C0C0400u),
+                                                            __builtin_amdgcn_perm(ev[1], ev[0], 0x0C0C0400u),
+                                                            0x05040100u);
                 }
                 grans_refill(rk, gk, sk_);
             } else {
 #pragma unroll 1
-                for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
-                    uint32_t packed = 0;
+                for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
+                    if (c4) grans_refill(rv, gv, sv_);
+                    uint32_t ev[4];
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        if (c8 | half) grans_refill(rv, gv, sv_);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const uint32_t ev = rans_lookup(rv, tabV, maskV);
-                            rans_advance(rv, ev, (uint32_t)a.pv);
-                            packed |= (ev >> 28) << (4 * (4 * half + i));
-                        }
+                    for (int i = 0; i < 4; ++i) {
+                        ev[i] = rans_lookup(rv, tabV, maskV);
+                        rans_advance(rv, ev[i], (uint32_t)a.pv);
                     }
-                    Wv.vt[c8][lane] = packed;
+                    Wv.vt[c4][lane] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(ev[3], ev[2], 0x0C0C0400u),
+                                                            __builtin_amdgcn_perm(ev[1], ev[0], 0x0C0C0400u),
+                                                            0x05040100u);
                 }
             }
             grans_refill(rv, gv, sv_);
             wave_lds_sync();
 
-            // p.v of V head g: lane owns channels 2 lane and 2 lane + 1
+            // p.v of V head g over token pairs: lane owns channels 2 lane and 2 lane + 1
 #pragma unroll 4
-            for (int j = 0; j < kTile; ++j) {
-                const uint32_t d = Wv.vt[vrow][j] >> vsh;
-                const float m0 = (float)(d & 15u), m1 = (float)((d >> 4) & 15u);
-                const float4_t w4 = *(const float4_t*)&Wv.w[j][0];
+            for (int j = 0; j < kTile; j += 2) {
+                const uint32_t d0 = Wv.vt[vrow][j], d1 = Wv.vt[vrow][j + 1];
+                const half2_t m0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(d1, d0, vsel0));
+                const half2_t m1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(d1, d0, vsel1));
+                const half2_t* w2 = &Wv.w[j >> 1][0];
 #pragma unroll
                 for (int hh = 0; hh < kGrp; ++hh) {
-                    acc[0][hh][0] += w4[hh] * m0;
-                    acc[0][hh][1] += w4[hh] * m1;
+                    const half2_t wp = w2[hh];
+                    acc[0][hh][0] = __builtin_amdgcn_fdot2(wp, m0, acc[0][hh][0], false);
+                    acc[0][hh][1] = __builtin_amdgcn_fdot2(wp, m1, acc[0][hh][1], false);
                 }
             }
             wave_lds_sync();
