@@ -613,15 +613,19 @@ __global__ void selftest_kernel(const double* __restrict__ a, const double* __re
 
 struct __attribute__((aligned(16))) TokLds {
     uint8_t sym[kTokN];          // the stream's current symbols, by position
-    uint8_t buf[kTokMaxC];       // the container before it is stored
+    uint8_t buf[kTokMaxC + 16];  // emitted bytes (kTokMaxC + 1 used), see tok_rans_emit
 };
 
 __device__ __forceinline__ int tok_pos(int i, int lane) { return 128 * (i >> 1) + 64 * (i & 1) + lane; }
 
-// rANS encode of sym[1023..0] by one lane, counting bytes (rans_count_lane
-// over 1024 symbols, four symbols per LDS read): the emitted bytes, or -1
-// once more than cap would be emitted.
-__device__ int tok_rans_count(const uint8_t* sym, const SymConst* sc, int p, int cap) {
+// The same encode storing each emitted byte as it goes, without branches:
+// every step stores the state's low byte at the next emission slot
+// buf[kTokMaxC - cnt] and advances cnt only when the renormalisation emits,
+// so the k-th emitted byte sits at buf[kTokMaxC - k] and the cnt bytes end up
+// in decode order at buf[kTokMaxC + 1 - cnt ..] (buf has kTokMaxC + 1 bytes;
+// cnt never exceeds the 1024 steps). Returns cnt, or -1 when it exceeds cap;
+// xo gets the final state. One pass serves as both the trial and the write.
+__device__ int tok_rans_emit(const uint8_t* sym, const SymConst* sc, int p, int cap, uint8_t* buf, uint32_t& xo) {
     uint32_t x = kStateLow;
     int cnt = 0;
     for (int i = kTokN - 4; i >= 0; i -= 4) {
@@ -629,39 +633,16 @@ __device__ int tok_rans_count(const uint8_t* sym, const SymConst* sc, int p, int
 #pragma unroll
         for (int b = 3; b >= 0; --b) {
             const SymConst c = sc[(w >> (8 * b)) & 255u];
-            if (x >= c.lim) {
-                ++cnt;
-                x >>= 8;
-            }
+            const bool emit = x >= c.lim;
+            buf[kTokMaxC - cnt] = (uint8_t)(x & 255u);
+            cnt += emit ? 1 : 0;
+            x = emit ? x >> 8 : x;
             const uint32_t q = __umulhi(x, c.magic) >> c.shift;
             x = x + c.cum + q * ((1u << p) - c.freq);
         }
     }
+    xo = x;
     return cnt <= cap ? cnt : -1;
-}
-
-// The same encode writing the container to dst (LDS): the 3-byte state, then
-// the cnt emitted bytes in decode order, then zeros up to C.
-__device__ void tok_rans_write(const uint8_t* sym, const SymConst* sc, int p, int cnt, int C, uint8_t* dst) {
-    uint32_t x = kStateLow;
-    int j = kStateBytes + cnt;
-    for (int i = kTokN - 4; i >= 0; i -= 4) {
-        const uint32_t w = *(const uint32_t*)(sym + i);
-#pragma unroll
-        for (int b = 3; b >= 0; --b) {
-            const SymConst c = sc[(w >> (8 * b)) & 255u];
-            if (x >= c.lim) {
-                dst[--j] = (uint8_t)(x & 255u);
-                x >>= 8;
-            }
-            const uint32_t q = __umulhi(x, c.magic) >> c.shift;
-            x = x + c.cum + q * ((1u << p) - c.freq);
-        }
-    }
-    dst[0] = (uint8_t)x;
-    dst[1] = (uint8_t)(x >> 8);
-    dst[2] = (uint8_t)(x >> 16);
-    for (int k = kStateBytes + cnt; k < C; ++k) dst[k] = 0;
 }
 
 // Sum of the 16 values of every lane by the fixed halving tree over stream
@@ -684,7 +665,17 @@ __device__ __forceinline__ double tok_fold_sum(const double (&t)[16]) {
     return __shfl(v, 0);
 }
 
-__global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a) {
+// The 16 symbols of a lane (value i at stream position tok_pos(i, lane)) as
+// 4-bit fields, so that a wave's registers stay under 128 per lane.
+struct Nib16 {
+    uint32_t w[2];
+    __device__ __forceinline__ int get(int i) const { return (int)((w[i >> 3] >> (4 * (i & 7))) & 15u); }
+    __device__ __forceinline__ void set(int i, int v) {
+        w[i >> 3] = (w[i >> 3] & ~(15u << (4 * (i & 7)))) | ((uint32_t)v << (4 * (i & 7)));
+    }
+};
+
+__global__ __launch_bounds__(64 * kWaves, 2) void token_encode_kernel(TokEncArgs a) {
     __shared__ TokLds tl_all[kWaves];
     __shared__ SymConst sconst[2][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -698,7 +689,8 @@ __global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a)
         c.magic = t->div_magic[m];
         c.shift = t->div_shift[m];
         c.inner = (uint32_t)t->inner[m];
-        c.pad0 = c.pad1 = 0;
+        c.pad0 = (uint32_t)t->cost[m];   // the symbol's fixed-point cost
+        c.pad1 = 0;
         sconst[tid >> 4][m] = c;
     }
     __syncthreads();
@@ -743,33 +735,36 @@ __global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a)
     }
     const double go = mn, gs = (mx - mn) / (double)(M - 1);
     const double half = (double)(M - 1) / 2.0;
-    double u[16];
-    int m[16], nearest[16];
+    Nib16 m = {{0u, 0u}};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        u[i] = gs > 0.0 ? (y[i] - go) / gs : 0.0;
-        int q = 0;
-        for (int j = 1; j < M; ++j) {
-            const double b = (double)j - 0.5;
-            q += b >= half ? (u[i] > b) : (u[i] >= b);
+        int q = (M - 1) / 2;
+        if (gs > 0.0) {
+            const double u = (y[i] - go) / gs;
+            q = 0;
+            for (int j = 1; j < M; ++j) {
+                const double b = (double)j - 0.5;
+                q += b >= half ? (u > b) : (u >= b);
+            }
         }
-        m[i] = gs > 0.0 ? q : (M - 1) / 2;
-        nearest[i] = m[i];
-        W.sym[tok_pos(i, lane)] = (uint8_t)m[i];
+        m.set(i, q);
+        W.sym[tok_pos(i, lane)] = (uint8_t)q;
     }
+    const Nib16 nearest = m;
 
     // cost, then the drift rounds of the per-head coder in grid units: the
     // candidates of a round leave in (key, position) order, each by a wave
     // argmin, until the rate fits the budget and the rANS stream the container
     int R = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) R += T->cost[m[i]];
+    for (int i = 0; i < 16; ++i) R += (int)sc[m.get(i)].pad0;
     R = wave_sum_i(R);
     bool done = false, failed = false;
     int cnt = -1, rounds = 0;
+    uint32_t xfin = 0;
     if (R <= B) {
         wave_sync();
-        if (lane == 0) cnt = tok_rans_count(W.sym, sc, p, C - kStateBytes);
+        if (lane == 0) cnt = tok_rans_emit(W.sym, sc, p, C - kStateBytes, W.buf, xfin);
         cnt = __shfl(cnt, 0);
         done = cnt >= 0;
     }
@@ -778,21 +773,23 @@ __global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a)
             failed = true;
             break;
         }
+        const Nib16 mr = m;   // the round's starting symbols
         uint64_t key[16];
-        int dr[16], mr[16];
         bool any = false;
         R = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            mr[i] = m[i];
-            R += T->cost[m[i]];
-            const int inn = T->inner[m[i]];
-            dr[i] = inn >= 0 ? T->cost[m[i]] - T->cost[inn] : 0;
+            const int mi = mr.get(i);
+            const SymConst ci = sc[mi];
+            R += (int)ci.pad0;
+            const int inn = (int)ci.inner;
+            const int dr = inn >= 0 ? (int)ci.pad0 - (int)sc[inn].pad0 : 0;
             key[i] = ~0ull;
-            if (inn >= 0 && dr[i] > 0) {
-                const double e1 = u[i] - (double)inn, e0 = u[i] - (double)m[i];
+            if (inn >= 0 && dr > 0) {
+                const double u = gs > 0.0 ? (y[i] - go) / gs : 0.0;
+                const double e1 = u - (double)inn, e0 = u - (double)mi;
                 const double dd = e1 * e1 - e0 * e0;
-                key[i] = order_key(dd / (double)dr[i]);
+                key[i] = order_key(dd / (double)dr);
                 any = true;
             }
         }
@@ -829,22 +826,23 @@ __global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     if (i == wi) {
-                        d = dr[i];
+                        const int mi = mr.get(i);
+                        const int inn = (int)sc[mi].inner;
+                        d = (int)sc[mi].pad0 - (int)sc[inn].pad0;
                         key[i] = ~0ull;
-                        m[i] = T->inner[mr[i]];
-                        W.sym[bp] = (uint8_t)m[i];
+                        m.set(i, inn);
+                        W.sym[bp] = (uint8_t)inn;
                     }
             }
             removed += __shfl(d, owner);
             return true;
         };
-        bool left = true;
-        while (R - removed > B && (left = take())) {
+        while (R - removed > B && take()) {
         }
         if (R - removed <= B) {
             for (;;) {
                 wave_sync();
-                if (lane == 0) cnt = tok_rans_count(W.sym, sc, p, C - kStateBytes);
+                if (lane == 0) cnt = tok_rans_emit(W.sym, sc, p, C - kStateBytes, W.buf, xfin);
                 cnt = __shfl(cnt, 0);
                 if (cnt >= 0) {
                     done = true;
@@ -853,7 +851,6 @@ __global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a)
                 if (!take()) break;
             }
         }
-        (void)left;
     }
     if (failed) {
         if (lane == 0 && a.err_word) atomicOr(a.err_word, DQ_DEVERR_ENCODE);
@@ -863,20 +860,20 @@ __global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a)
     // least-squares refit of (o, s) to the stored symbols, sums by the halving tree
     double t[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t[i] = (double)m[i];
+    for (int i = 0; i < 16; ++i) t[i] = (double)m.get(i);
     const double mbar = tok_fold_sum(t) / (double)kTokN;
     const double ybar = tok_fold_sum(y) / (double)kTokN;
-    double dm[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        dm[i] = (double)m[i] - mbar;
-        t[i] = dm[i] * dm[i];
+        const double dm = (double)m.get(i) - mbar;
+        t[i] = dm * dm;
     }
     const double smm = tok_fold_sum(t);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+        const double dm = (double)m.get(i) - mbar;
         const double dy = y[i] - ybar;
-        t[i] = dm[i] * dy;
+        t[i] = dm * dy;
     }
     const double smy = tok_fold_sum(t);
     const double s_star = smm > 0.0 ? smy / smm : 0.0;
@@ -885,17 +882,25 @@ __global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a)
     // the container, as dwords interleaved across the page's slots (dword j
     // of slot po at row j of the page), zero-padded to whole dwords; then
     // (o16, s16) at the slot
+    // container byte b: the flushed state for b < 3, then the cnt emitted
+    // bytes in decode order, then zeros
     const int C4 = (C + 3) >> 2;
-    wave_sync();
-    if (lane == 0) {
-        tok_rans_write(W.sym, sc, p, cnt, C, W.buf);
-        for (int k = C; k < 4 * C4; ++k) W.buf[k] = 0;
-    }
+    const uint32_t xs = (uint32_t)__shfl((int)xfin, 0);
     wave_sync();
     const int page = slot / a.page_size, po = slot - page * a.page_size;
     const size_t idx = (size_t)page * a.page_size + po;
     uint32_t* dst = (uint32_t*)a.cache[kv] + (size_t)page * C4 * a.page_size + po;
-    for (int j = lane; j < C4; j += 64) dst[(size_t)j * a.page_size] = *(const uint32_t*)(W.buf + 4 * j);
+    for (int j = lane; j < C4; j += 64) {
+        uint32_t d = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int b = 4 * j + k;
+            const uint32_t v = b < kStateBytes ? (xs >> (8 * b)) & 255u
+                               : (b < kStateBytes + cnt ? (uint32_t)W.buf[kTokMaxC + 1 - cnt + (b - kStateBytes)] : 0u);
+            d |= v << (8 * k);
+        }
+        dst[(size_t)j * a.page_size] = d;
+    }
     if (lane == 0) {
         a.meta[kv][2 * idx] = f64_to_f16_rne(o_star);
         a.meta[kv][2 * idx + 1] = f64_to_f16_rne(s_star);
@@ -903,7 +908,7 @@ __global__ __launch_bounds__(64 * kWaves) void token_encode_kernel(TokEncArgs a)
     if (a.drift_stats) {
         int changed = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) changed += m[i] != nearest[i];
+        for (int i = 0; i < 16; ++i) changed += m.get(i) != nearest.get(i);
         changed = wave_sum_i(changed);
         if (lane == 0) a.drift_stats[(size_t)token * 2 + kv] = (uint32_t)changed | ((uint32_t)rounds << 16);
     }
