@@ -228,3 +228,44 @@ def test_token_encode_then_attend(setup):
     out, err = _run(dq, tabs, d, lens, P)
     assert err == 0
     assert row_rel_err(out, ref).max() <= TOL
+
+
+def test_token_qwen3_layer_sampled(setup):
+    """The benchmark's per-token layer (128 x 8192 tokens, 256-token pages,
+    the library's split rule), built by the device cache write: the containers
+    and (o16, s16) of two sampled sequences equal the oracle's byte for byte,
+    and their attention rows (all 32 query heads) meet the bar."""
+    from decode_attention_dq_amd import workloads
+    dq, tk, tv, tabs = setup
+    w = workloads.WORKLOADS["token_qwen3_8b"]
+    cache = workloads.build_token_cache(dq, tabs, w)
+    q = workloads.query_rows(w)
+    B, hq, P = w.batch, w.num_q_heads, w.page_size
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dq.dq_token_workspace_size(B, hq, w.context), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_token_decode_attention(tabs, q, cache.k_cache, cache.v_cache, cache.k_norm, cache.v_norm,
+                                 cache.block_table, cache.context_lens, P, w.context, out, ws, err_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    out = out.cpu().numpy()
+    qh = q.float().cpu().numpy()
+    bt = cache.block_table.cpu().numpy()
+    for b in (5, 101):
+        T = int(cache.lens[b])
+        k = workloads.kv_rows(w, 0, synth.T_K, b, T).float().cpu().numpy().astype(np.float64)
+        v = workloads.kv_rows(w, 0, synth.T_V, b, T).float().cpu().numpy().astype(np.float64)
+        rk, rv = oracle.encode_tokens(k, tk), oracle.encode_tokens(v, tv)
+        slots = workloads.slot_mapping(bt[b:b + 1], cache.lens[b:b + 1], P)
+        pg = torch.as_tensor(slots // P, device="cuda", dtype=torch.long)
+        off = torch.as_tensor(slots % P, device="cuda", dtype=torch.long)
+        for c, r, C, meta in ((cache.k_cache, rk, w.container, cache.k_norm), (cache.v_cache, rv, w.cv, cache.v_norm)):
+            got = c.permute(0, 2, 1, 3)[pg, off].reshape(T, -1).cpu().numpy()
+            assert np.array_equal(got[:, :C], r.containers) and not got[:, C:].any(), b
+            mt = meta[pg, off].cpu().numpy().view(np.uint16)
+            assert np.array_equal(mt[:, 0], r.o16.view(np.uint16)) and np.array_equal(mt[:, 1], r.s16.view(np.uint16))
+        kh = oracle.reconstruct_tokens(rk.symbols, rk.o16, rk.s16).transpose(1, 0, 2)
+        vh = oracle.reconstruct_tokens(rv.symbols, rv.o16, rv.s16).transpose(1, 0, 2)
+        ref = oracle.attention(qh[b:b + 1], [kh], [vh])[0]
+        e = row_rel_err(out[b], ref)
+        assert e.max() <= TOL, (b, e.max())
