@@ -591,12 +591,12 @@ size_t dq_token_workspace_size(int batch, int num_q_heads, int max_context, int 
     return (size_t)batch * num_q_heads * (s + 1) * dq::kPartStride * sizeof(float);
 }
 
-int dq_token_decode_attention(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
-                              const uint8_t* v_cache, const uint16_t* k_meta, const uint16_t* v_meta,
-                              const int32_t* block_table, const int32_t* context_lens, int batch, int num_q_heads,
-                              int max_pages_per_seq, int page_size, int max_context, float softmax_scale,
-                              int num_splits, float* out, void* workspace, size_t workspace_bytes,
-                              uint32_t* err_word, void* stream) {
+int dq_token_decode_attention_ext(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
+                                  const uint8_t* v_cache, const uint16_t* k_meta, const uint16_t* v_meta,
+                                  const int32_t* block_table, const int32_t* context_lens, int batch,
+                                  int num_q_heads, int max_pages_per_seq, int page_size, int max_context,
+                                  float softmax_scale, int num_splits, const dq_attention_extras* ex, float* out,
+                                  void* workspace, size_t workspace_bytes, uint32_t* err_word, void* stream) {
     if (!t || t->format != 1 || !q || !k_cache || !v_cache || !k_meta || !v_meta || !block_table ||
         !context_lens || !out || !workspace)
         return DQ_ERR_INVALID_ARG;
@@ -609,6 +609,14 @@ int dq_token_decode_attention(const dq_tables* t, const void* q, int q_dtype, co
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) || ((uintptr_t)k_meta & 3u) ||
         ((uintptr_t)v_meta & 3u))
         return DQ_ERR_INVALID_ARG;
+    const bool win = ex && ex->window_k;
+    if (ex && (ex->k_mean || ex->k_mean_scale)) return DQ_ERR_UNSUPPORTED;
+    if (win) {
+        if (!ex->window_v || !ex->window_lens || ex->window_cap <= 0 || !aligned16(ex->window_k) ||
+            !aligned16(ex->window_v))
+            return DQ_ERR_INVALID_ARG;
+        if (ex->window_cap > dq::kWindowMax) return DQ_ERR_UNSUPPORTED;
+    }
     const int splits = num_splits ? num_splits : dq::token_choose_splits(batch, max_context);
     if (workspace_bytes < dq_token_workspace_size(batch, num_q_heads, max_context, splits)) return DQ_ERR_WORKSPACE;
     if ((long)batch * splits > (long)INT32_MAX / 4) return DQ_ERR_INVALID_ARG;
@@ -637,6 +645,10 @@ int dq_token_decode_attention(const dq_tables* t, const void* q, int q_dtype, co
     a.pv = t->info[1].prob_bits;
     a.half_k = 0.5f * (float)(t->info[0].levels - 1);
     a.half_v = 0.5f * (float)(t->info[1].levels - 1);
+    a.win_k = win ? ex->window_k : nullptr;
+    a.win_v = win ? ex->window_v : nullptr;
+    a.win_lens = win ? ex->window_lens : nullptr;
+    a.win_cap = win ? ex->window_cap : 0;
     a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
     a.entries = t->d_entries;
     a.partials = (float*)workspace;
@@ -644,6 +656,18 @@ int dq_token_decode_attention(const dq_tables* t, const void* q, int q_dtype, co
     a.err_word = err_word;
     hipError_t e = dq::launch_token_attention(a, (hipStream_t)stream);
     return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+
+int dq_token_decode_attention(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
+                              const uint8_t* v_cache, const uint16_t* k_meta, const uint16_t* v_meta,
+                              const int32_t* block_table, const int32_t* context_lens, int batch, int num_q_heads,
+                              int max_pages_per_seq, int page_size, int max_context, float softmax_scale,
+                              int num_splits, float* out, void* workspace, size_t workspace_bytes,
+                              uint32_t* err_word, void* stream) {
+    return dq_token_decode_attention_ext(t, q, q_dtype, k_cache, v_cache, k_meta, v_meta, block_table, context_lens,
+                                         batch, num_q_heads, max_pages_per_seq, page_size, max_context,
+                                         softmax_scale, num_splits, nullptr, out, workspace, workspace_bytes,
+                                         err_word, stream);
 }
 
 int dq_encode_tokens(const dq_tables* t, const void* k, const void* v, int dtype, int num_tokens,

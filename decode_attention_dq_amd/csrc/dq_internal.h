@@ -140,6 +140,10 @@ struct TokAttnArgs {
     int num_splits, split_len, slot_count, token_cap;
     int ck, cv, pk, pv;
     float half_k, half_v;               // (M - 1) / 2: the entries carry centred levels
+    const uint16_t* win_k;              // optional bf16 window [batch][8][win_cap][128]
+    const uint16_t* win_v;
+    const int32_t* win_lens;            // [batch]
+    int win_cap;
     float softmax_scale;
     const uint32_t* entries;            // [2][kTableSlots] decode tables (K then V)
     float* partials;                    // [batch][Hq][slot_count][kPartStride]

@@ -365,11 +365,32 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
 }  // namespace
 
 hipError_t launch_token_attention(const TokAttnArgs& a, hipStream_t s) {
+    if (a.win_k) {
+        // the bf16 window's partial (the same kernel as for per-head caches; it
+        // reads only the queries, the window and the partial layout)
+        AttnArgs w = {};
+        w.q = a.q;
+        w.q_dtype = a.q_dtype;
+        w.batch = a.batch;
+        w.num_q_heads = a.num_q_heads;
+        w.num_kv_heads = kTokHeads;
+        w.group = a.group;
+        w.slot_count = a.slot_count;
+        w.win_k = a.win_k;
+        w.win_v = a.win_v;
+        w.win_lens = a.win_lens;
+        w.win_cap = a.win_cap;
+        w.softmax_scale = a.softmax_scale;
+        w.partials = a.partials;
+        hipError_t e = launch_window(w, a.num_splits, s);
+        if (e != hipSuccess) return e;
+    }
     dim3 grid((unsigned)(a.num_splits * a.batch));
     hipLaunchKernelGGL(token_attn_kernel, grid, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    MergeArgs m = {a.partials, a.slot_count, a.context_lens, a.token_cap, a.split_len, a.num_q_heads, -1, a.out};
+    MergeArgs m = {a.partials, a.slot_count, a.context_lens, a.token_cap, a.split_len, a.num_q_heads,
+                   a.win_k ? a.num_splits : -1, a.out};
     return launch_merge(m, a.batch * a.num_q_heads, true, s);
 }
 

@@ -95,6 +95,8 @@ _sig = {
     "dq_token_decode_attention": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, ctypes.c_float, _i,
                                        _p, _p, ctypes.c_size_t, _p, _p]),
     "dq_token_decode_symbols": (_i, [_p, _i, _p, _i, _p, _p, _p]),
+    "dq_token_decode_attention_ext": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, ctypes.c_float,
+                                           _i, ctypes.POINTER(dq_attention_extras), _p, _p, ctypes.c_size_t, _p, _p]),
     "dq_strerror": (ctypes.c_char_p, [_i]),
     "dq_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -462,8 +464,11 @@ def dq_token_workspace_size(batch: int, num_q_heads: int, max_context: int, num_
 
 def dq_token_decode_attention(tables: Tables, q, k_cache, v_cache, k_meta, v_meta, block_table, context_lens,
                               page_size: int, max_context: int, out, workspace, softmax_scale: float = 0.0,
-                              num_splits: int = 0, err_word=None, stream=None) -> None:
-    """q: [B][Hq][128] float32 or bfloat16 with Hq = 8 G, G <= 4; out: [B][Hq][128] float32."""
+                              num_splits: int = 0, err_word=None, stream=None, window_k=None, window_v=None,
+                              window_lens=None) -> None:
+    """q: [B][Hq][128] float32 or bfloat16 with Hq = 8 G, G <= 4; out: [B][Hq][128] float32.
+    Optional bf16 window of the newest tokens: window_k / window_v [B][8][cap][128],
+    window_lens int32 [B] (dq_token_decode_attention_ext)."""
     import torch
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError("q must be [B][Hq][128]")
@@ -485,12 +490,30 @@ def dq_token_decode_attention(tables: Tables, q, k_cache, v_cache, k_meta, v_met
             raise ValueError(f"{nm} must hold 16-bit elements")
     if err_word is not None:
         _need(err_word, "err_word")
-    _check(_lib.dq_token_decode_attention(tables.handle, _ptr(q), q_dtype, _ptr(k_cache), _ptr(v_cache), _ptr(k_meta),
-                                          _ptr(v_meta), _ptr(block_table), _ptr(context_lens), B, hq,
-                                          int(block_table.shape[1]), int(page_size), int(max_context),
-                                          float(softmax_scale), int(num_splits), _ptr(out), _ptr(workspace),
-                                          int(workspace.numel()), _ptr(err_word), _stream(stream)),
-           "dq_token_decode_attention")
+    if window_k is None:
+        _check(_lib.dq_token_decode_attention(tables.handle, _ptr(q), q_dtype, _ptr(k_cache), _ptr(v_cache),
+                                              _ptr(k_meta), _ptr(v_meta), _ptr(block_table), _ptr(context_lens), B, hq,
+                                              int(block_table.shape[1]), int(page_size), int(max_context),
+                                              float(softmax_scale), int(num_splits), _ptr(out), _ptr(workspace),
+                                              int(workspace.numel()), _ptr(err_word), _stream(stream)),
+               "dq_token_decode_attention")
+        return
+    if window_v is None or window_lens is None:
+        raise ValueError("a window needs window_k, window_v and window_lens")
+    if window_k.dtype != torch.bfloat16 or window_v.dtype != torch.bfloat16 or window_k.shape != window_v.shape:
+        raise ValueError("window_k / window_v must be bfloat16 of one shape")
+    if window_k.dim() != 4 or window_k.shape[0] != B or window_k.shape[1] != TOKEN_HEADS or window_k.shape[3] != HEAD_DIM:
+        raise ValueError("window_k must be [B][8][cap][128]")
+    _need(window_k, "window_k"); _need(window_v, "window_v")
+    _need(window_lens, "window_lens", torch.int32, (B,))
+    ex = dq_attention_extras(_ptr(window_k), _ptr(window_v), _ptr(window_lens), int(window_k.shape[2]), None, None)
+    _check(_lib.dq_token_decode_attention_ext(tables.handle, _ptr(q), q_dtype, _ptr(k_cache), _ptr(v_cache),
+                                              _ptr(k_meta), _ptr(v_meta), _ptr(block_table), _ptr(context_lens), B, hq,
+                                              int(block_table.shape[1]), int(page_size), int(max_context),
+                                              float(softmax_scale), int(num_splits), ctypes.byref(ex), _ptr(out),
+                                              _ptr(workspace), int(workspace.numel()), _ptr(err_word),
+                                              _stream(stream)),
+           "dq_token_decode_attention_ext")
 
 
 def dq_token_decode_symbols(tables: Tables, which: int, containers, symbols_out, err_word=None,

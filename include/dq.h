@@ -396,6 +396,21 @@ int dq_token_decode_attention(const dq_tables* tables, const void* q, int q_dtyp
                               size_t workspace_bytes, uint32_t* err_word, void* stream);
 
 /*
+ * dq_token_decode_attention with a bf16 window of the most recent tokens
+ * (section 5.1): extras->window_k / window_v [batch][8][window_cap][128] in
+ * the original domain with window_lens [batch], merged by log-sum-exp as in
+ * dq_decode_attention_ext. Key block means are not supported for this format
+ * (extras->k_mean set: DQ_ERR_UNSUPPORTED). extras may be NULL.
+ */
+int dq_token_decode_attention_ext(const dq_tables* tables, const void* q, int q_dtype, const uint8_t* k_cache,
+                                  const uint8_t* v_cache, const uint16_t* k_meta, const uint16_t* v_meta,
+                                  const int32_t* block_table, const int32_t* context_lens, int batch,
+                                  int num_q_heads, int max_pages_per_seq, int page_size, int max_context,
+                                  float softmax_scale, int num_splits, const dq_attention_extras* extras,
+                                  float* out, void* workspace, size_t workspace_bytes, uint32_t* err_word,
+                                  void* stream);
+
+/*
  * Test hook: decode n_streams contiguous per-token containers ([n][C] bytes
  * of table `which`) into symbols uint8 [n][1024] by a plain per-thread
  * decoder. Streams failing the integrity check set DQ_DEVERR_DECODE.

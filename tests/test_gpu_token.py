@@ -269,3 +269,61 @@ def test_token_qwen3_layer_sampled(setup):
         ref = oracle.attention(qh[b:b + 1], [kh], [vh])[0]
         e = row_rel_err(out[b], ref)
         assert e.max() <= TOL, (b, e.max())
+
+
+def test_token_attention_with_bf16_window(setup):
+    """The paper's serving layout on the per-token format: compressed tokens
+    plus a bf16 window of the newest ones (section 5.1), merged by log-sum-exp;
+    window with compressed tokens, window only, and an empty sequence."""
+    dq, tk, tv, tabs = setup
+    lens, wl, G, cap = [300, 0, 100, 0], [64, 128, 0, 0], 4, 128
+    dq_, tabs_, d, _, P = _attention_case(setup, lens, G, seed=11, perm_seed=6)
+    rng = np.random.default_rng(12)
+    wk = synth.round_to_bf16(rng.standard_normal((4, 8, cap, 128)).astype(np.float32))
+    wv = synth.round_to_bf16(rng.standard_normal((4, 8, cap, 128)).astype(np.float32))
+    q = d["q"].float().cpu().numpy()
+    ref = np.zeros((4, 8 * G, 128))
+    for b, T in enumerate(lens):
+        if T + wl[b] == 0:
+            continue
+        kh = np.zeros((8, 0, 128)); vh = np.zeros((8, 0, 128))
+        if T:
+            rk = oracle.encode_tokens(_tokens(11, synth.T_K, T, part=b).astype(np.float64), tk)
+            rv = oracle.encode_tokens(_tokens(11, synth.T_V, T, part=b).astype(np.float64), tv)
+            kh = oracle.reconstruct_tokens(rk.symbols, rk.o16, rk.s16).transpose(1, 0, 2)
+            vh = oracle.reconstruct_tokens(rv.symbols, rv.o16, rv.s16).transpose(1, 0, 2)
+        kh = np.concatenate([kh, wk[b, :, :wl[b]].astype(np.float64)], axis=1)
+        vh = np.concatenate([vh, wv[b, :, :wl[b]].astype(np.float64)], axis=1)
+        ref[b] = oracle.attention(q[b:b + 1], [kh], [vh])[0]
+    bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).cuda().view(torch.bfloat16)
+    B, hq = q.shape[:2]
+    max_ctx = max(lens)
+    out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((dq.dq_token_workspace_size(B, hq, max_ctx),), 0xFF, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_token_decode_attention(tabs, d["q"], d["kc"], d["vc"], d["km"], d["vm"], d["bt"], d["lens"], P, max_ctx,
+                                 out, ws, err_word=err, window_k=bf(wk), window_v=bf(wv),
+                                 window_lens=_dev(np.asarray(wl, np.int32)))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert int(err.item()) == 0
+    assert np.all(out[3] == 0)
+    assert row_rel_err(out[:3], ref[:3]).max() <= TOL
+
+
+def test_token_attention_refuses_key_means(setup):
+    """Key block means are not a feature of the per-token format here."""
+    import ctypes
+    dq, tk, tv, tabs = setup
+    lens = [10]
+    dq_, tabs_, d, _, P = _attention_case(setup, lens, 1, seed=13)
+    dummy = torch.zeros(16, dtype=torch.int8, device="cuda")
+    ex = dq.dq_attention_extras(None, None, None, 0, dummy.data_ptr(), dummy.data_ptr())
+    out = torch.zeros((1, 8, 128), dtype=torch.float32, device="cuda")
+    ws = torch.zeros((dq.dq_token_workspace_size(1, 8, 10),), dtype=torch.uint8, device="cuda")
+    rc = dq._lib.dq_token_decode_attention_ext(tabs.handle, d["q"].data_ptr(), dq.DQ_DTYPE_BF16, d["kc"].data_ptr(),
+                                               d["vc"].data_ptr(), d["km"].data_ptr(), d["vm"].data_ptr(),
+                                               d["bt"].data_ptr(), d["lens"].data_ptr(), 1, 8, d["bt"].shape[1], P, 10,
+                                               0.0, 0, ctypes.byref(ex), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                               None, None)
+    assert rc == dq.DQ_ERR_UNSUPPORTED
