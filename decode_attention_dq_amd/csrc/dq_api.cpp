@@ -7,7 +7,7 @@
 #include <new>
 #include <string>
 
-#include "dq_internal.h"
+#include "dq_token.h"
 
 namespace {
 
@@ -610,7 +610,9 @@ int dq_token_decode_attention_ext(const dq_tables* t, const void* q, int q_dtype
         ((uintptr_t)v_meta & 3u))
         return DQ_ERR_INVALID_ARG;
     const bool win = ex && ex->window_k;
-    if (ex && (ex->k_mean || ex->k_mean_scale)) return DQ_ERR_UNSUPPORTED;
+    const bool mk = ex && ex->k_mean;
+    if (ex && !ex->k_mean != !ex->k_mean_scale) return DQ_ERR_INVALID_ARG;
+    if (mk && ((uintptr_t)ex->k_mean & 3u)) return DQ_ERR_INVALID_ARG;
     if (win) {
         if (!ex->window_v || !ex->window_lens || ex->window_cap <= 0 || !aligned16(ex->window_k) ||
             !aligned16(ex->window_v))
@@ -649,6 +651,8 @@ int dq_token_decode_attention_ext(const dq_tables* t, const void* q, int q_dtype
     a.win_v = win ? ex->window_v : nullptr;
     a.win_lens = win ? ex->window_lens : nullptr;
     a.win_cap = win ? ex->window_cap : 0;
+    a.k_mean = mk ? ex->k_mean : nullptr;
+    a.k_mean_scale = mk ? ex->k_mean_scale : nullptr;
     a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
     a.entries = t->d_entries;
     a.partials = (float*)workspace;
@@ -670,9 +674,11 @@ int dq_token_decode_attention(const dq_tables* t, const void* q, int q_dtype, co
                                          err_word, stream);
 }
 
-int dq_encode_tokens(const dq_tables* t, const void* k, const void* v, int dtype, int num_tokens,
-                     int page_size, const int32_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
-                     uint16_t* k_meta, uint16_t* v_meta, uint32_t* drift_stats, uint32_t* err_word, void* stream) {
+namespace {
+int token_encode_impl(const dq_tables* t, const void* k, const void* v, int dtype, int num_tokens, int page_size,
+                      const int32_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache, uint16_t* k_meta,
+                      uint16_t* v_meta, int8_t* k_mean, uint16_t* k_mean_scale, uint32_t* drift_stats,
+                      uint32_t* err_word, void* stream) {
     if (!t || t->format != 1 || num_tokens < 0 || page_size <= 0) return DQ_ERR_INVALID_ARG;
     if (dtype != DQ_DTYPE_F32 && dtype != DQ_DTYPE_BF16) return DQ_ERR_INVALID_ARG;
     if (num_tokens == 0) return DQ_OK;
@@ -692,8 +698,29 @@ int dq_encode_tokens(const dq_tables* t, const void* k, const void* v, int dtype
     a.drift_stats = drift_stats;
     a.err_word = err_word;
     a.tables = t->d_enc;
+    a.k_mean = k_mean;
+    a.k_mean_scale = k_mean_scale;
     hipError_t e = dq::launch_token_encode(a, (hipStream_t)stream);
     return e == hipSuccess ? DQ_OK : hip_fail(e);
+}
+}  // namespace
+
+int dq_encode_tokens(const dq_tables* t, const void* k, const void* v, int dtype, int num_tokens,
+                     int page_size, const int32_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                     uint16_t* k_meta, uint16_t* v_meta, uint32_t* drift_stats, uint32_t* err_word, void* stream) {
+    return token_encode_impl(t, k, v, dtype, num_tokens, page_size, slot_mapping, k_cache, v_cache, k_meta, v_meta,
+                             nullptr, nullptr, drift_stats, err_word, stream);
+}
+
+int dq_encode_tokens_blocks(const dq_tables* t, const void* k, const void* v, int dtype, int num_blocks,
+                            int page_size, const int32_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                            uint16_t* k_meta, uint16_t* v_meta, int8_t* k_mean, uint16_t* k_mean_scale,
+                            uint32_t* drift_stats, uint32_t* err_word, void* stream) {
+    if (!k_mean || !k_mean_scale || num_blocks < 0 || (long)num_blocks * dq::kMeanBlock > INT32_MAX)
+        return DQ_ERR_INVALID_ARG;
+    if (page_size > 0 && (page_size & (page_size - 1))) return DQ_ERR_UNSUPPORTED;
+    return token_encode_impl(t, k, v, dtype, num_blocks * dq::kMeanBlock, page_size, slot_mapping, k_cache, v_cache,
+                             k_meta, v_meta, k_mean, k_mean_scale, drift_stats, err_word, stream);
 }
 
 int dq_token_decode_symbols(const dq_tables* t, int which, const uint8_t* containers, int n_streams,

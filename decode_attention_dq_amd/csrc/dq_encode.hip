@@ -16,7 +16,7 @@
 // A stream that the first drift round cannot fit (no prefix fits, or it needs
 // more extensions than were staged) is redone from scratch by the complete
 // per-stream procedure, which also runs the fallback rounds.
-#include "dq_internal.h"
+#include "dq_token.h"
 
 #include <algorithm>
 
@@ -190,13 +190,18 @@ __device__ __forceinline__ void load_row(const EncArgs& a, const StreamId& s, in
 // Key channel-mean removal (sections 3.2 and 5): the mean row of the
 // 128-token block that starts at call token `first`, found from that token's
 // slot; false when the slot is missing or not where a block starts.
-__device__ __forceinline__ bool mean_row(const EncArgs& a, int first, int head, size_t& row) {
-    const int slot = a.slot_mapping[first];
+__device__ __forceinline__ bool mean_row_at(const int32_t* slot_mapping, int P, int num_kv_heads, int first,
+                                            int head, size_t& row) {
+    const int slot = slot_mapping[first];
     if (slot < 0) return false;
-    const int P = a.page_size, page = slot / P, off = slot - page * P;
+    const int page = slot / P, off = slot - page * P;
     if (off % (P < kMeanBlock ? P : kMeanBlock) != 0) return false;
-    row = ((size_t)page * a.num_kv_heads + head) * (size_t)mean_rows_per_page(P) + (size_t)(off / kMeanBlock);
+    row = ((size_t)page * num_kv_heads + head) * (size_t)mean_rows_per_page(P) + (size_t)(off / kMeanBlock);
     return true;
+}
+
+__device__ __forceinline__ bool mean_row(const EncArgs& a, int first, int head, size_t& row) {
+    return mean_row_at(a.slot_mapping, a.page_size, a.num_kv_heads, first, head, row);
 }
 
 __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
@@ -720,6 +725,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void token_encode_kernel(TokEncArgs
 #pragma unroll
         for (int h = 0; h < 8; ++h) fwht_f64(y[2 * h], y[2 * h + 1], lane);
     }
+    // key block mean: the stream codes y minus the dequantised mean q * s16 of
+    // its 128-row block, head by head; a block without a mean row (flagged by
+    // the mean pass) leaves its key streams unwritten
+    if (kv == 0 && a.k_mean) {
+        const int first = token / kMeanBlock * kMeanBlock;
+#pragma unroll
+        for (int h = 0; h < kTokHeads; ++h) {
+            size_t row;
+            if (!mean_row_at(a.slot_mapping, a.page_size, kTokHeads, first, h, row)) return;
+            const double sd = f16_bits_to_f64(a.k_mean_scale[row]);
+            y[2 * h] = y[2 * h] - (double)a.k_mean[row * kHeadDim + lane] * sd;
+            y[2 * h + 1] = y[2 * h + 1] - (double)a.k_mean[row * kHeadDim + lane + 64] * sd;
+        }
+    }
 
     // token-wise min-max grid: o = min, s = (max - min) / (M - 1), u = (y - o) / s
     double mn = y[0], mx = y[0];
@@ -964,6 +983,23 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_token_encode(const TokEncArgs& a, hipStream_t s) {
+    if (a.k_mean) {
+        // the per-head mean pass over [num_tokens][8][128] key rows
+        EncArgs m = {};
+        m.k = a.k;
+        m.dtype = a.dtype;
+        m.num_tokens = a.num_tokens;
+        m.num_kv_heads = kTokHeads;
+        m.page_size = a.page_size;
+        m.slot_mapping = a.slot_mapping;
+        m.err_word = a.err_word;
+        m.k_mean = a.k_mean;
+        m.k_mean_scale = a.k_mean_scale;
+        const long waves = (long)(a.num_tokens / kMeanBlock) * kTokHeads;
+        hipLaunchKernelGGL(mean_kernel, dim3((unsigned)((waves + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0, s, m);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const long streams = 2l * a.num_tokens;
     dim3 grid((unsigned)((streams + kWaves - 1) / kWaves));
     hipLaunchKernelGGL(token_encode_kernel, grid, dim3(64 * kWaves), 0, s, a);

@@ -109,48 +109,6 @@ struct Bf16Args {
     float* out;
 };
 
-// Per-token format: one stream of the 8 KV heads' 1024 rotated values per
-// token, on a token-wise affine grid (o, s) stored as two fp16 values.
-constexpr int kTokHeads = 8;
-constexpr int kTokN = kTokHeads * kHeadDim;   // symbols per stream
-constexpr int kTokMinC = 16, kTokMaxC = 1024; // container bytes
-
-struct TokEncArgs {
-    const void* k;                      // [num_tokens][8][128], bf16 bits or fp32
-    const void* v;
-    int dtype, num_tokens, page_size;
-    const int32_t* slot_mapping;        // [num_tokens], slot = page * page_size + offset; < 0: skip
-    uint8_t* cache[2];                  // [pages][page_size][C]
-    uint16_t* meta[2];                  // [pages][page_size][2]: o16, s16
-    uint32_t* drift_stats;              // optional [num_tokens][2]: changed | rounds << 16
-    uint32_t* err_word;
-    const EncTable* tables;             // device copy: [0] keys, [1] values
-};
-
-struct TokAttnArgs {
-    const void* q;                      // [batch][Hq][128]
-    int q_dtype;
-    const uint8_t* k_cache;             // [pages][page_size][C_K]
-    const uint8_t* v_cache;
-    const uint16_t* k_meta;             // [pages][page_size][2]
-    const uint16_t* v_meta;
-    const int32_t* block_table;
-    const int32_t* context_lens;
-    int batch, num_q_heads, group, max_pages_per_seq, page_size, log2p;
-    int num_splits, split_len, slot_count, token_cap;
-    int ck, cv, pk, pv;
-    float half_k, half_v;               // (M - 1) / 2: the entries carry centred levels
-    const uint16_t* win_k;              // optional bf16 window [batch][8][win_cap][128]
-    const uint16_t* win_v;
-    const int32_t* win_lens;            // [batch]
-    int win_cap;
-    float softmax_scale;
-    const uint32_t* entries;            // [2][kTableSlots] decode tables (K then V)
-    float* partials;                    // [batch][Hq][slot_count][kPartStride]
-    float* out;
-    uint32_t* err_word;
-};
-
 constexpr int kPartStride = 132;         // m, l, pad, pad, acc[128]
 constexpr int kWindowMax = 256;          // largest bf16 window
 
@@ -173,10 +131,6 @@ struct MergeArgs {
 };
 // `rotated`: the partials are in the rotated domain (inverse rotation applied).
 hipError_t launch_merge(const MergeArgs& a, int rows, bool rotated, hipStream_t s);
-hipError_t launch_token_encode(const TokEncArgs& a, hipStream_t s);
-hipError_t launch_token_attention(const TokAttnArgs& a, hipStream_t s);
-hipError_t launch_token_decode_symbols(const EncTable* table, const uint8_t* containers, int n, uint8_t* out,
-                                       uint32_t* err, hipStream_t s);
 hipError_t launch_decode_symbols(const uint32_t* entries, int prob_bits, int levels, int container,
                                  const uint8_t* containers, int n, uint8_t* out, uint32_t* err,
                                  hipStream_t s);
@@ -186,8 +140,6 @@ hipError_t launch_selftest_fp64(const double* a, const double* b, int n, double*
 // Split rule shared by dq_workspace_size and dq_decode_attention.
 int choose_splits(int batch, int num_kv_heads, int max_context);
 int split_tokens(int max_context, int splits);
-int token_cap(int max_pages_per_seq, int page_size, int splits, int split_len);
-int token_choose_splits(int batch, int max_context);
 
 }  // namespace dq
 

@@ -19,7 +19,7 @@
 // each refill issues the loads for the next one, clamped to the container's
 // last row, so no read leaves the container.
 #include "dq_device.h"
-#include "dq_internal.h"
+#include "dq_token.h"
 #include "dq_sched.h"
 #include "dq_wave.h"
 
@@ -176,6 +176,28 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
         const uint32_t pg = (uint32_t)page * (uint32_t)a.page_size, po = idx - pg;
         const GSrc sk_ = {kbase, pg * ck4 + po, (uint32_t)a.page_size, ck4 - 1u};
         const GSrc sv_ = {vbase, pg * cv4 + po, (uint32_t)a.page_size, cv4 - 1u};
+        // key block means: lane 4g + hh gets q~ . (q * s16) of query head
+        // (g, hh) and the 128-token block the tile lies in
+        float qmu = 0.0f;
+        if (a.k_mean) {
+            const int tb = t0 & ~(kMeanBlock - 1);
+            const int mpage = a.block_table[(size_t)b * a.max_pages_per_seq + (tb >> a.log2p)];
+            const int mg = lane >> 2, mh = lane & 3;
+            if (lane < 4 * kTokHeads && mh < G) {
+                const size_t row = ((size_t)mpage * kTokHeads + mg) * (size_t)mean_rows_per_page(a.page_size) +
+                                   (size_t)((tb & (a.page_size - 1)) / kMeanBlock);
+                const uint32_t* mr = (const uint32_t*)(a.k_mean + row * kHeadDim);
+                float d = 0.0f;
+                for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
+                    const uint32_t w = mr[c4];
+                    const half2_t m0 = {(_Float16)(int8_t)(w & 255u), (_Float16)(int8_t)((w >> 8) & 255u)};
+                    const half2_t m1 = {(_Float16)(int8_t)((w >> 16) & 255u), (_Float16)(int8_t)(w >> 24)};
+                    d = __builtin_amdgcn_fdot2(S.qt[mg][2 * c4][mh], m0, d, false);
+                    d = __builtin_amdgcn_fdot2(S.qt[mg][2 * c4 + 1][mh], m1, d, false);
+                }
+                qmu = d * f16_to_f32(a.k_mean_scale[row]);
+            }
+        }
         RansLane rk, rv;
         GWin gk, gv;
         grans_init(rk, gk, sk_);
@@ -210,7 +232,8 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
 #pragma unroll
             for (int hh = 0; hh < kGrp; ++hh) {
                 const int hl = 4 * g + hh;
-                const float L = valid ? (ok * S.qsum[g][hh] + sk * s4[hh]) * cs : -INFINITY;
+                const float qm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qmu), hl));
+                const float L = valid ? (ok * S.qsum[g][hh] + (sk * s4[hh] + qm)) * cs : -INFINITY;
                 const float mt = wave_max_uniform(L);
                 const float mo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), hl));
                 const float mn = fmaxf(mo, mt);

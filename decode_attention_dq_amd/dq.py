@@ -91,6 +91,7 @@ _sig = {
                                   ctypes.POINTER(dq_table_params)]),
     "dq_token_table_describe": (_i, [ctypes.POINTER(dq_table_params), ctypes.POINTER(dq_table_info)]),
     "dq_encode_tokens": (_i, [_p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "dq_encode_tokens_blocks": (_i, [_p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "dq_token_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "dq_token_decode_attention": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, ctypes.c_float, _i,
                                        _p, _p, ctypes.c_size_t, _p, _p]),
@@ -458,6 +459,42 @@ def dq_encode_tokens(tables: Tables, k, v, slot_mapping, k_cache, v_cache, k_met
                                  _ptr(err_word), _stream(stream)), "dq_encode_tokens")
 
 
+def dq_encode_tokens_blocks(tables: Tables, k, v, slot_mapping, k_cache, v_cache, k_meta, v_meta, k_mean,
+                            k_mean_scale, page_size: int, drift_stats=None, err_word=None, stream=None) -> None:
+    """Per-token cache write with key block means: k, v [128 * blocks][8][128]
+    (block j = rows 128j .. 128j+127), k_mean int8 [pages][8][R][128],
+    k_mean_scale 16-bit [pages][8][R] with R = mean_rows_per_page(page_size);
+    the rest as dq_encode_tokens."""
+    import torch
+    if k.dtype != v.dtype or k.shape != v.shape or k.dim() != 3 or tuple(k.shape[1:]) != (TOKEN_HEADS, HEAD_DIM):
+        raise ValueError("k and v must both be [num_tokens][8][128] of one dtype")
+    if k.shape[0] % MEAN_BLOCK:
+        raise ValueError("the token count must be a multiple of 128")
+    dtype = {torch.float32: DQ_DTYPE_F32, torch.bfloat16: DQ_DTYPE_BF16}.get(k.dtype)
+    if dtype is None:
+        raise ValueError("k/v dtype must be float32 or bfloat16")
+    n = int(k.shape[0])
+    _need(k, "k"); _need(v, "v")
+    _need(slot_mapping, "slot_mapping", torch.int32, (n,))
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, torch.uint8)
+    for t, nm in ((k_meta, "k_meta"), (v_meta, "v_meta"), (k_mean_scale, "k_mean_scale")):
+        _need(t, nm)
+        if t.element_size() != 2:
+            raise ValueError(f"{nm} must hold 16-bit elements")
+    _need(k_mean, "k_mean", torch.int8)
+    if drift_stats is not None:
+        _need(drift_stats, "drift_stats", shape=(n, 2))
+        if drift_stats.element_size() != 4:
+            raise ValueError("drift_stats must hold 32-bit elements")
+    if err_word is not None:
+        _need(err_word, "err_word")
+    _check(_lib.dq_encode_tokens_blocks(tables.handle, _ptr(k), _ptr(v), dtype, n // MEAN_BLOCK, int(page_size),
+                                        _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _ptr(k_meta), _ptr(v_meta),
+                                        _ptr(k_mean), _ptr(k_mean_scale), _ptr(drift_stats), _ptr(err_word),
+                                        _stream(stream)), "dq_encode_tokens_blocks")
+
+
 def dq_token_workspace_size(batch: int, num_q_heads: int, max_context: int, num_splits: int = 0) -> int:
     return int(_lib.dq_token_workspace_size(int(batch), int(num_q_heads), int(max_context), int(num_splits)))
 
@@ -465,10 +502,11 @@ def dq_token_workspace_size(batch: int, num_q_heads: int, max_context: int, num_
 def dq_token_decode_attention(tables: Tables, q, k_cache, v_cache, k_meta, v_meta, block_table, context_lens,
                               page_size: int, max_context: int, out, workspace, softmax_scale: float = 0.0,
                               num_splits: int = 0, err_word=None, stream=None, window_k=None, window_v=None,
-                              window_lens=None) -> None:
+                              window_lens=None, k_mean=None, k_mean_scale=None) -> None:
     """q: [B][Hq][128] float32 or bfloat16 with Hq = 8 G, G <= 4; out: [B][Hq][128] float32.
     Optional bf16 window of the newest tokens: window_k / window_v [B][8][cap][128],
-    window_lens int32 [B] (dq_token_decode_attention_ext)."""
+    window_lens int32 [B]; optional key block means k_mean / k_mean_scale as written by
+    dq_encode_tokens_blocks (both through dq_token_decode_attention_ext)."""
     import torch
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError("q must be [B][Hq][128]")
@@ -490,7 +528,7 @@ def dq_token_decode_attention(tables: Tables, q, k_cache, v_cache, k_meta, v_met
             raise ValueError(f"{nm} must hold 16-bit elements")
     if err_word is not None:
         _need(err_word, "err_word")
-    if window_k is None:
+    if window_k is None and k_mean is None:
         _check(_lib.dq_token_decode_attention(tables.handle, _ptr(q), q_dtype, _ptr(k_cache), _ptr(v_cache),
                                               _ptr(k_meta), _ptr(v_meta), _ptr(block_table), _ptr(context_lens), B, hq,
                                               int(block_table.shape[1]), int(page_size), int(max_context),
@@ -498,15 +536,27 @@ def dq_token_decode_attention(tables: Tables, q, k_cache, v_cache, k_meta, v_met
                                               int(workspace.numel()), _ptr(err_word), _stream(stream)),
                "dq_token_decode_attention")
         return
-    if window_v is None or window_lens is None:
-        raise ValueError("a window needs window_k, window_v and window_lens")
-    if window_k.dtype != torch.bfloat16 or window_v.dtype != torch.bfloat16 or window_k.shape != window_v.shape:
-        raise ValueError("window_k / window_v must be bfloat16 of one shape")
-    if window_k.dim() != 4 or window_k.shape[0] != B or window_k.shape[1] != TOKEN_HEADS or window_k.shape[3] != HEAD_DIM:
-        raise ValueError("window_k must be [B][8][cap][128]")
-    _need(window_k, "window_k"); _need(window_v, "window_v")
-    _need(window_lens, "window_lens", torch.int32, (B,))
-    ex = dq_attention_extras(_ptr(window_k), _ptr(window_v), _ptr(window_lens), int(window_k.shape[2]), None, None)
+    cap = 0
+    if window_k is not None:
+        if window_v is None or window_lens is None:
+            raise ValueError("a window needs window_k, window_v and window_lens")
+        if window_k.dtype != torch.bfloat16 or window_v.dtype != torch.bfloat16 or window_k.shape != window_v.shape:
+            raise ValueError("window_k / window_v must be bfloat16 of one shape")
+        if (window_k.dim() != 4 or window_k.shape[0] != B or window_k.shape[1] != TOKEN_HEADS
+                or window_k.shape[3] != HEAD_DIM):
+            raise ValueError("window_k must be [B][8][cap][128]")
+        _need(window_k, "window_k"); _need(window_v, "window_v")
+        _need(window_lens, "window_lens", torch.int32, (B,))
+        cap = int(window_k.shape[2])
+    if k_mean is not None:
+        if k_mean_scale is None:
+            raise ValueError("key means need k_mean and k_mean_scale")
+        _need(k_mean, "k_mean", torch.int8)
+        _need(k_mean_scale, "k_mean_scale")
+        if k_mean_scale.element_size() != 2:
+            raise ValueError("k_mean_scale must hold 16-bit elements")
+    ex = dq_attention_extras(_ptr(window_k), _ptr(window_v), _ptr(window_lens), cap, _ptr(k_mean),
+                             _ptr(k_mean_scale))
     _check(_lib.dq_token_decode_attention_ext(tables.handle, _ptr(q), q_dtype, _ptr(k_cache), _ptr(v_cache),
                                               _ptr(k_meta), _ptr(v_meta), _ptr(block_table), _ptr(context_lens), B, hq,
                                               int(block_table.shape[1]), int(page_size), int(max_context),

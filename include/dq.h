@@ -367,6 +367,30 @@ int dq_encode_tokens(const dq_tables* tables, const void* k, const void* v, int 
                      uint16_t* k_meta, uint16_t* v_meta, uint32_t* drift_stats, uint32_t* err_word,
                      void* stream);
 
+/*
+ * Per-token cache write with windowed key channel-mean removal (section 3.2
+ * Table 1, section 5 "windowed INT8 channel means"), the paper's full
+ * per-token configuration: the call's tokens form num_blocks blocks of 128
+ * (block j = rows 128j .. 128j+127 of k and v, 128 consecutive positions of
+ * one sequence starting at a multiple of 128). For every block and each of
+ * the 8 KV heads the mean mu of the rotated key rows H x (token-order fp64
+ * sum / 128) is stored as INT8 with one fp16 scale, s16 = fp16(max|mu| / 127),
+ * q = rint(mu / s16) clamped to +-127; each key stream then codes its rotated
+ * values minus q * s16 of its head. Values are coded as by dq_encode_tokens.
+ * Arguments as for dq_encode_tokens, plus:
+ *   k_mean        int8 [num_pages][8][R][128], R = page_size / 128 when
+ *                 page_size >= 128, else 1: a block's rows live in the page its
+ *                 first token occupies, at index (offset / 128); 4-byte aligned
+ *   k_mean_scale  uint16 (fp16 bits) [num_pages][8][R]
+ * page_size must be a power of two (DQ_ERR_UNSUPPORTED). A block whose first
+ * slot is negative or not at offset 0 mod min(page_size, 128) of its page sets
+ * DQ_DEVERR_MEAN_SLOT and its key streams are not written.
+ */
+int dq_encode_tokens_blocks(const dq_tables* tables, const void* k, const void* v, int dtype, int num_blocks,
+                            int page_size, const int32_t* slot_mapping, uint8_t* k_cache, uint8_t* v_cache,
+                            uint16_t* k_meta, uint16_t* v_meta, int8_t* k_mean, uint16_t* k_mean_scale,
+                            uint32_t* drift_stats, uint32_t* err_word, void* stream);
+
 /* Workspace bytes of dq_token_decode_attention (0 = library split rule). */
 size_t dq_token_workspace_size(int batch, int num_q_heads, int max_context, int num_splits);
 
@@ -396,11 +420,18 @@ int dq_token_decode_attention(const dq_tables* tables, const void* q, int q_dtyp
                               size_t workspace_bytes, uint32_t* err_word, void* stream);
 
 /*
- * dq_token_decode_attention with a bf16 window of the most recent tokens
- * (section 5.1): extras->window_k / window_v [batch][8][window_cap][128] in
- * the original domain with window_lens [batch], merged by log-sum-exp as in
- * dq_decode_attention_ext. Key block means are not supported for this format
- * (extras->k_mean set: DQ_ERR_UNSUPPORTED). extras may be NULL.
+ * dq_token_decode_attention with the optional parts of dq_attention_extras
+ * (sections 3.2, 5 and 5.1); extras may be NULL.
+ *   window_k, window_v, window_lens, window_cap   a bf16 window of the most
+ *                 recent tokens, [batch][8][window_cap][128] in the original
+ *                 domain with window_lens [batch], merged by log-sum-exp as in
+ *                 dq_decode_attention_ext
+ *   k_mean, k_mean_scale   the key block means written by
+ *                 dq_encode_tokens_blocks (k_mean 4-byte aligned): every
+ *                 logit of token t and query head h gains q~_h . (q * s16) / 128
+ *                 of t's block and KV head (a sequence's unfinished last block
+ *                 uses that block's row all the same); one of the two without
+ *                 the other is DQ_ERR_INVALID_ARG
  */
 int dq_token_decode_attention_ext(const dq_tables* tables, const void* q, int q_dtype, const uint8_t* k_cache,
                                   const uint8_t* v_cache, const uint16_t* k_meta, const uint16_t* v_meta,

@@ -88,6 +88,13 @@ def test_invalid_arguments_rejected_on_host(dq):
                                           0, None, None, None, 0, fake, fake, 1 << 20, None, None) == \
         dq.DQ_ERR_INVALID_ARG
     assert lib.dq_decode_symbols(None, 0, fake, 1, fake, None, None) == dq.DQ_ERR_INVALID_ARG
+    # per-token block write: null tables, missing means, non-power-of-two pages
+    assert lib.dq_encode_tokens_blocks(None, fake, fake, 0, 1, 64, fake, fake, fake, fake, fake, fake, fake, None,
+                                       None, None) == dq.DQ_ERR_INVALID_ARG
+    assert lib.dq_encode_tokens_blocks(fake, fake, fake, 0, 1, 64, fake, fake, fake, fake, fake, None, fake, None,
+                                       None, None) == dq.DQ_ERR_INVALID_ARG
+    assert lib.dq_encode_tokens_blocks(fake, fake, fake, 0, 1, 48, fake, fake, fake, fake, fake, fake, fake, None,
+                                       None, None) == dq.DQ_ERR_UNSUPPORTED
     assert lib.dq_selftest_fp64(None, None, -1, None, None, None, None) == dq.DQ_ERR_INVALID_ARG
     assert lib.dq_tables_destroy(None) == dq.DQ_OK
 

@@ -311,19 +311,164 @@ def test_token_attention_with_bf16_window(setup):
     assert row_rel_err(out[:3], ref[:3]).max() <= TOL
 
 
-def test_token_attention_refuses_key_means(setup):
-    """Key block means are not a feature of the per-token format here."""
+BLK = 128
+
+
+def _mean_rows(seed, tensor, T, b, offset):
+    """[T][8][128] rows; keys get a per-(head, channel) offset that also moves
+    from one 128-token block to the next: the mean the block removal takes
+    out, different enough between blocks that a missing share shows."""
+    x = _tokens(seed, tensor, T, part=b).astype(np.float64)
+    if offset is not None:
+        drift = np.random.default_rng([seed, b]).standard_normal((-(-T // BLK), 8, 128))
+        x = x + offset[None] + np.repeat(drift, BLK, axis=0)[:T]
+    return synth.round_to_bf16(x.astype(np.float32))
+
+
+def _oracle_block_means(k):
+    """Oracle means of [128 nb][8][128] key rows: q [nb][8][128], s16 [nb][8]
+    and the per-token rotated mean [128 nb][1024] (head-major)."""
+    nb = k.shape[0] // BLK
+    kb = k.astype(np.float64).reshape(nb, BLK, 8, 128).transpose(0, 2, 1, 3)
+    q, s16, mu_hat, _ = oracle.block_means(kb)
+    return q, s16, np.repeat(mu_hat.reshape(nb, 1024), BLK, axis=0)
+
+
+def _means_cache(dq, tabs, enc_lens, P, seed, perm_seed):
+    """Device cache of whole 128-token blocks per sequence, written by one
+    dq_encode_tokens_blocks call; returns the device buffers and the rows."""
+    bt, pages, slots = _layout(enc_lens, P, perm_seed)
+    R = dq.mean_rows_per_page(P)
+    offset = np.random.default_rng(seed).standard_normal((8, 128)) * 2.0
+    kx = [_mean_rows(seed, synth.T_K, T, b, offset) for b, T in enumerate(enc_lens)]
+    vx = [_mean_rows(seed, synth.T_V, T, b, None) for b, T in enumerate(enc_lens)]
+    d = dict(kc=torch.zeros(dq.token_cache_shape(pages, P, K_CFG[1]), dtype=torch.uint8, device="cuda"),
+             vc=torch.zeros(dq.token_cache_shape(pages, P, V_CFG[1]), dtype=torch.uint8, device="cuda"),
+             km=torch.zeros((pages, P, 2), dtype=torch.int16, device="cuda"),
+             vm=torch.zeros((pages, P, 2), dtype=torch.int16, device="cuda"),
+             kmu=torch.zeros((pages, 8, R, 128), dtype=torch.int8, device="cuda"),
+             ksc=torch.zeros((pages, 8, R), dtype=torch.int16, device="cuda"),
+             bt=_dev(bt))
+    return d, bt, pages, slots, kx, vx
+
+
+@pytest.mark.parametrize("P,bf16", [(64, False), (256, True), (128, False)])
+def test_token_encode_blocks_bit_exact(setup, P, bf16):
+    """Key block means on the per-token format: the INT8 means, their fp16
+    scales, the key containers and (o16, s16) of the residual streams, and the
+    untouched value streams equal the oracle's; a block whose first slot is
+    missing sets the mean flag and leaves its key streams unwritten."""
+    dq, tk, tv, tabs = setup
+    lens = [256, 128, 384, 128]
+    d, bt, pages, slots, kx, vx = _means_cache(dq, tabs, lens, P, seed=21, perm_seed=5)
+    slots[3] = slots[3].copy()
+    slots[3][0] = -1                                  # the last block has no mean row
+    k, v = np.concatenate(kx), np.concatenate(vx)
+    kd, vd = _dev(k), _dev(v)
+    if bf16:
+        kd, vd = kd.to(torch.bfloat16), vd.to(torch.bfloat16)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ds = torch.zeros((k.shape[0], 2), dtype=torch.int32, device="cuda")
+    dq.dq_encode_tokens_blocks(tabs, kd, vd, _dev(np.concatenate(slots)), d["kc"], d["vc"], d["km"], d["vm"],
+                               d["kmu"], d["ksc"], P, drift_stats=ds, err_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == dq.DQ_DEVERR_MEAN_SLOT
+    kc, vc = _from_pages(d["kc"].cpu().numpy(), K_CFG[1]), _from_pages(d["vc"].cpu().numpy(), V_CFG[1])
+    km = d["km"].cpu().numpy().view(np.uint16).reshape(-1, 2)
+    vm = d["vm"].cpu().numpy().view(np.uint16).reshape(-1, 2)
+    kmu, ksc = d["kmu"].cpu().numpy(), d["ksc"].cpu().numpy().view(np.uint16)
+    ds = ds.cpu().numpy().view(np.uint32)
+    row0 = 0
+    for b, T in enumerate(lens):
+        q, s16, mrot = _oracle_block_means(kx[b])
+        rk = oracle.encode_tokens(kx[b].astype(np.float64), tk, mean_rot=mrot)
+        rv = oracle.encode_tokens(vx[b].astype(np.float64), tv)
+        s = slots[b]
+        live = s >= 0
+        assert np.array_equal(vc[s[live], :V_CFG[1]], rv.containers[live]), b
+        assert np.array_equal(vm[s[live], 0], rv.o16[live].view(np.uint16))
+        assert np.array_equal(vm[s[live], 1], rv.s16[live].view(np.uint16))
+        if b == 3:
+            assert not kc[s[1:]].any() and not km[s[1:]].any()    # key streams of the flagged block
+            row0 += T
+            continue
+        assert np.array_equal(kc[s, :K_CFG[1]], rk.containers), b
+        assert not kc[s, K_CFG[1]:].any()
+        assert np.array_equal(km[s, 0], rk.o16.view(np.uint16)) and np.array_equal(km[s, 1], rk.s16.view(np.uint16))
+        st = ds[row0:row0 + T, 0]
+        assert np.array_equal(st & 0xFFFF, rk.changed) and np.array_equal(st >> 16, rk.rounds)
+        first = s[::BLK]
+        rp, ri = first // P, (first % P) // BLK
+        for h in range(8):
+            assert np.array_equal(kmu[rp, h, ri], q[:, h]), (b, h)
+            assert np.array_equal(ksc[rp, h, ri], s16[:, h].view(np.uint16)), (b, h)
+        row0 += T
+
+
+@pytest.mark.parametrize("P,G,window", [(64, 4, False), (256, 2, True), (128, 1, False), (16, 4, True)])
+def test_token_attention_with_key_means(setup, P, G, window):
+    """The paper's full per-token configuration: per-token streams of the key
+    residuals after block-mean removal, the means' share added to every logit,
+    and (with `window`) a bf16 window of the newest tokens. Context lengths end
+    inside a block (its tokens use the block's mean row all the same); the
+    reference is the oracle's fp64 attention over its reconstructions plus the
+    dequantised means."""
+    dq, tk, tv, tabs = setup
+    lens = [3 * BLK + 50, BLK, 77, 0, 5 * BLK]
+    enc = [max(BLK, -(-T // BLK) * BLK) for T in lens]
+    d, bt, pages, slots, kx, vx = _means_cache(dq, tabs, enc, P, seed=23, perm_seed=8)
+    dq.dq_encode_tokens_blocks(tabs, _dev(np.concatenate(kx)), _dev(np.concatenate(vx)), _dev(np.concatenate(slots)),
+                               d["kc"], d["vc"], d["km"], d["vm"], d["kmu"], d["ksc"], P)
+    B, hq, cap = len(lens), 8 * G, 128
+    q = synth.queries(830, B, hq, bf16=True)
+    rng = np.random.default_rng(24)
+    wl = [40, 0, 128, 9, 0] if window else [0] * B
+    wk = synth.round_to_bf16(rng.standard_normal((B, 8, cap, 128)).astype(np.float32))
+    wv = synth.round_to_bf16(rng.standard_normal((B, 8, cap, 128)).astype(np.float32))
+    ref = np.zeros((B, hq, 128))
+    for b, T in enumerate(lens):
+        _, _, mrot = _oracle_block_means(kx[b])
+        rk = oracle.encode_tokens(kx[b].astype(np.float64), tk, mean_rot=mrot)
+        rv = oracle.encode_tokens(vx[b].astype(np.float64), tv)
+        kh = oracle.reconstruct_tokens(rk.symbols, rk.o16, rk.s16, mean_rot=mrot).transpose(1, 0, 2)[:, :T]
+        vh = oracle.reconstruct_tokens(rv.symbols, rv.o16, rv.s16).transpose(1, 0, 2)[:, :T]
+        kh = np.concatenate([kh, wk[b, :, :wl[b]].astype(np.float64)], axis=1)
+        vh = np.concatenate([vh, wv[b, :, :wl[b]].astype(np.float64)], axis=1)
+        if kh.shape[1]:
+            ref[b] = oracle.attention(q[b:b + 1], [kh], [vh])[0]
+    bf = lambda a: torch.from_numpy(synth.f32_to_bf16_bits(a).view(np.int16)).cuda().view(torch.bfloat16)
+    kw = dict(window_k=bf(wk), window_v=bf(wv), window_lens=_dev(np.asarray(wl, np.int32))) if window else {}
+    max_ctx = max(lens)
+    out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((dq.dq_token_workspace_size(B, hq, max_ctx),), 0xFF, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_token_decode_attention(tabs, _dev(q).to(torch.bfloat16), d["kc"], d["vc"], d["km"], d["vm"], d["bt"],
+                                 _dev(np.asarray(lens, np.int32)), P, max_ctx, out, ws, err_word=err,
+                                 k_mean=d["kmu"], k_mean_scale=d["ksc"], **kw)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert int(err.item()) == 0
+    live = [b for b in range(B) if lens[b] + wl[b] > 0]
+    dead = [b for b in range(B) if lens[b] + wl[b] == 0]
+    assert all(np.all(out[b] == 0) for b in dead)
+    e = row_rel_err(out[live], ref[live])
+    assert e.max() <= TOL, e.max()
+
+
+def test_token_attention_needs_both_mean_buffers(setup):
+    """k_mean without k_mean_scale (or the reverse) is an argument error."""
     import ctypes
     dq, tk, tv, tabs = setup
     lens = [10]
     dq_, tabs_, d, _, P = _attention_case(setup, lens, 1, seed=13)
     dummy = torch.zeros(16, dtype=torch.int8, device="cuda")
-    ex = dq.dq_attention_extras(None, None, None, 0, dummy.data_ptr(), dummy.data_ptr())
     out = torch.zeros((1, 8, 128), dtype=torch.float32, device="cuda")
     ws = torch.zeros((dq.dq_token_workspace_size(1, 8, 10),), dtype=torch.uint8, device="cuda")
-    rc = dq._lib.dq_token_decode_attention_ext(tabs.handle, d["q"].data_ptr(), dq.DQ_DTYPE_BF16, d["kc"].data_ptr(),
-                                               d["vc"].data_ptr(), d["km"].data_ptr(), d["vm"].data_ptr(),
-                                               d["bt"].data_ptr(), d["lens"].data_ptr(), 1, 8, d["bt"].shape[1], P, 10,
-                                               0.0, 0, ctypes.byref(ex), out.data_ptr(), ws.data_ptr(), ws.numel(),
-                                               None, None)
-    assert rc == dq.DQ_ERR_UNSUPPORTED
+    for a, b in ((dummy.data_ptr(), None), (None, dummy.data_ptr())):
+        ex = dq.dq_attention_extras(None, None, None, 0, a, b)
+        rc = dq._lib.dq_token_decode_attention_ext(tabs.handle, d["q"].data_ptr(), dq.DQ_DTYPE_BF16,
+                                                   d["kc"].data_ptr(), d["vc"].data_ptr(), d["km"].data_ptr(),
+                                                   d["vm"].data_ptr(), d["bt"].data_ptr(), d["lens"].data_ptr(), 1, 8,
+                                                   d["bt"].shape[1], P, 10, 0.0, 0, ctypes.byref(ex), out.data_ptr(),
+                                                   ws.data_ptr(), ws.numel(), None, None)
+        assert rc == dq.DQ_ERR_INVALID_ARG
