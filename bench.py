@@ -203,19 +203,15 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
     return res
 
 
-def token_measurement(dq, torch, workloads, name: str = "token_qwen3_8b", copies: int = 2, reps: int = 5,
-                      enc_seqs: int = 16) -> dict:
-    """The per-token format on the Qwen3-8B layer (one 1024-value stream per
-    token over the 8 KV heads, 331 / 231-byte containers, 8 / 6 levels):
-    decode attention rotating through `copies` caches (each above the MALL),
-    and the cache write of `enc_seqs` sequences in one call."""
-    from decode_attention_dq_amd import synth
+def token_attention_time(dq, torch, workloads, tables, name: str, copies: int, reps: int):
+    """Mean HIP-event time of one per-token decode attention call on workload
+    `name`, rotating through `copies` caches (each above the MALL), with the
+    workload's bf16 window and key block means when it has them. Returns
+    (seconds, compressed tokens, bytes read per call, device error word)."""
     w = workloads.WORKLOADS[name]
-    tables = dq.dq_token_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.cv))
     caches = [workloads.build_token_cache(dq, tables, w, layer=l) for l in range(copies)]
     qs = [workloads.query_rows(w, l) for l in range(copies)]
     B, hq, P = w.batch, w.num_q_heads, w.page_size
-    lens = caches[0].lens
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
     ws = torch.empty(dq.dq_token_workspace_size(B, hq, w.context), dtype=torch.uint8, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -224,18 +220,47 @@ def token_measurement(dq, torch, workloads, name: str = "token_qwen3_8b", copies
     for it in range(reps + 2):
         for l in range(copies):
             c = caches[l]
+            kw = {}
+            if w.window:
+                kw.update(window_k=c.win_k, window_v=c.win_v, window_lens=c.win_lens)
+            if w.means:
+                kw.update(k_mean=c.k_mean, k_mean_scale=c.k_mean_scale)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             dq.dq_token_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
-                                         c.context_lens, P, w.context, out, ws, err_word=err, stream=stream)
+                                         c.context_lens, P, w.context, out, ws, err_word=err, stream=stream, **kw)
             e1.record(stream)
             if it >= 2:
                 ev.append((e0, e1))
     torch.cuda.synchronize()
     t = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
-    ntok = int(np.sum(lens))
+    ntok = int(np.sum(caches[0].lens))
     nbytes = ntok * (w.container + 4 + w.cv + 4)
+    if w.means:
+        nbytes += int(np.sum(-(-caches[0].lens // 128))) * w.num_kv_heads * (128 + 2)
+    if w.window:
+        nbytes += int(caches[0].win_lens.sum().item()) * w.num_kv_heads * 128 * 2 * 2
     del caches
+    return t, ntok, nbytes, int(err.item())
+
+
+def token_measurement(dq, torch, workloads, name: str = "token_qwen3_8b", full_name: str = "token_full_qwen3_8b",
+                      copies: int = 2, reps: int = 5, enc_seqs: int = 16) -> dict:
+    """The per-token format on the Qwen3-8B layer (one 1024-value stream per
+    token over the 8 KV heads, 331 / 231-byte containers, 8 / 6 levels):
+    decode attention rotating through `copies` caches (each above the MALL),
+    the same with the paper's full configuration (key block means and a bf16
+    window of the newest 128 tokens), and the cache write of `enc_seqs`
+    sequences in one call."""
+    from decode_attention_dq_amd import synth
+    w = workloads.WORKLOADS[name]
+    tables = dq.dq_token_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.cv))
+    B, hq, P = w.batch, w.num_q_heads, w.page_size
+    t, ntok, nbytes, derr = token_attention_time(dq, torch, workloads, tables, name, copies, reps)
+    full = workloads.WORKLOADS[full_name]
+    tf, ntok_f, nbytes_f, derr_f = token_attention_time(dq, torch, workloads, tables, full_name, copies, reps)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
     # cache write of enc_seqs sequences in one call
     n = enc_seqs * w.context
     k = torch.cat([workloads.kv_rows(w, 0, synth.T_K, b, w.context) for b in range(enc_seqs)])
@@ -260,7 +285,10 @@ def token_measurement(dq, torch, workloads, name: str = "token_qwen3_8b", copies
             "levels": [w.k_levels, w.v_levels], "kv_heads_per_stream": 8, "cache_copies": copies,
             "us_per_call": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 2),
             "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes,
-            "symbols_per_s": round(ntok * 2048 / t, 1), "device_errors": int(err.item()),
+            "symbols_per_s": round(ntok * 2048 / t, 1), "device_errors": derr | derr_f | int(err.item()),
+            "full_config": {"workload": full_name, "window": full.window, "key_means": True,
+                            "us_per_call": round(tf * 1e6, 2), "compressed_tokens": ntok_f,
+                            "bytes_per_call": nbytes_f, "GBps": round(nbytes_f / tf / 1e9, 2)},
             "encode": {"streams": 2 * n, "ms": round(te * 1e3, 3), "streams_per_s": round(2 * n / te, 1),
                        "drift_rate_symbols": {"K": round(float(changed[:, 0].sum()) / (n * 1024), 5),
                                               "V": round(float(changed[:, 1].sum()) / (n * 1024), 5)},

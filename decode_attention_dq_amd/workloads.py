@@ -61,6 +61,10 @@ WORKLOADS = {
     # the paper's default format: 331 / 231-byte per-token containers, 8 / 6 levels
     "token_qwen3_8b": Workload("token_qwen3_8b", 128, 32, 8, 8192, container=331, container_v=231, token=True,
                                config_id=8),
+    # the paper's full per-token configuration: 331 / 231-byte containers, key block means,
+    # the last 128 tokens in bf16
+    "token_full_qwen3_8b": Workload("token_full_qwen3_8b", 128, 32, 8, 8192, container=331, container_v=231,
+                                    token=True, window=128, key_offset=2.0, means=True, config_id=9),
 }
 
 
@@ -192,29 +196,55 @@ def build_cache(dq, tables, w: Workload, layer: int = 0, keep_stats: bool = Fals
 def build_token_cache(dq, tables, w: Workload, layer: int = 0, keep_stats: bool = False, device="cuda") -> Cache:
     """Encode every sequence of one layer into a per-token cache: containers
     [pages][ceil(C/4)][P][4] (dword-interleaved across a page's slots), and
-    (o16, s16) metadata [pages][P][2] in the norm fields."""
+    (o16, s16) metadata [pages][P][2] in the norm fields. With a window, the
+    last `w.window` tokens of each sequence stay in bf16 ([B][8][window][128]);
+    with means, the keys are written in 128-token blocks with their block means
+    ([pages][8][R][128] int8 and [pages][8][R] fp16 scales)."""
     import torch
-    lens = context_lengths(w)
+    full = context_lengths(w)
+    lens = np.maximum(full - w.window, 0).astype(np.int32)
     bt, total = page_plan(w, lens)
-    P = w.page_size
+    P, H = w.page_size, w.num_kv_heads
     kc = torch.zeros(dq.token_cache_shape(total, P, w.container), dtype=torch.uint8, device=device)
     vc = torch.zeros(dq.token_cache_shape(total, P, w.cv), dtype=torch.uint8, device=device)
     km = torch.zeros((total, P, 2), dtype=torch.int16, device=device)
     vm = torch.zeros((total, P, 2), dtype=torch.int16, device=device)
+    if w.window:
+        wk = torch.zeros((w.batch, H, w.window, 128), dtype=torch.bfloat16, device=device)
+        wv = torch.zeros_like(wk)
+    if w.means:
+        R = dq.mean_rows_per_page(P)
+        kmu = torch.zeros((total, H, R, 128), dtype=torch.int8, device=device)
+        ksc = torch.zeros((total, H, R), dtype=torch.int16, device=device)
     stats = []
     for b in range(w.batch):
         T = int(lens[b])
         slots = torch.as_tensor(slot_mapping(bt[b:b + 1], lens[b:b + 1], P), device=device)
-        k = kv_rows(w, layer, synth.T_K, b, T, device)
-        v = kv_rows(w, layer, synth.T_V, b, T, device)
+        k = kv_rows(w, layer, synth.T_K, b, int(full[b]), device)
+        v = kv_rows(w, layer, synth.T_V, b, int(full[b]), device)
+        if w.window:
+            nw = int(full[b]) - T
+            wk[b, :, :nw] = k[T:].transpose(0, 1).to(torch.bfloat16)
+            wv[b, :, :nw] = v[T:].transpose(0, 1).to(torch.bfloat16)
+            k, v = k[:T].contiguous(), v[:T].contiguous()
         st = torch.zeros((T, 2), dtype=torch.int32, device=device) if keep_stats else None
-        if T:
+        if T and w.means:
+            if T % 128:
+                raise ValueError("block writes need whole 128-token blocks")
+            dq.dq_encode_tokens_blocks(tables, k, v, slots, kc, vc, km, vm, kmu, ksc, P, drift_stats=st)
+        elif T:
             dq.dq_encode_tokens(tables, k, v, slots, kc, vc, km, vm, P, drift_stats=st)
         if keep_stats:
             stats.append(st)
         del k, v
-    return Cache(kc, vc, km, vm, torch.as_tensor(bt, device=device), torch.as_tensor(lens, device=device), lens,
-                 torch.cat(stats) if keep_stats else None)
+    c = Cache(kc, vc, km, vm, torch.as_tensor(bt, device=device), torch.as_tensor(lens, device=device), lens,
+              torch.cat(stats) if keep_stats else None)
+    if w.means:
+        c.k_mean, c.k_mean_scale = kmu, ksc
+    if w.window:
+        c.win_k, c.win_v = wk, wv
+        c.win_lens = torch.as_tensor((full - lens).astype(np.int32), device=device)
+    return c
 
 
 def build_bf16_cache(w: Workload, layer: int = 0, device="cuda"):

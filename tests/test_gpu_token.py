@@ -472,3 +472,60 @@ def test_token_attention_needs_both_mean_buffers(setup):
                                                    d["bt"].shape[1], P, 10, 0.0, 0, ctypes.byref(ex), out.data_ptr(),
                                                    ws.data_ptr(), ws.numel(), None, None)
         assert rc == dq.DQ_ERR_INVALID_ARG
+
+
+def test_token_full_config_layer_sampled(setup):
+    """The paper's full per-token configuration on the benchmark's layer
+    (128 x 8192: key block means, the newest 128 tokens in bf16, the library's
+    split rule), built by the device cache write: for a sampled sequence the
+    containers, (o16, s16), INT8 means and scales equal the oracle's byte for
+    byte, and its 32 attention rows meet the bar."""
+    from decode_attention_dq_amd import workloads
+    dq, tk, tv, tabs = setup
+    w = workloads.WORKLOADS["token_full_qwen3_8b"]
+    cache = workloads.build_token_cache(dq, tabs, w)
+    q = workloads.query_rows(w)
+    B, hq, P = w.batch, w.num_q_heads, w.page_size
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dq.dq_token_workspace_size(B, hq, w.context), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_token_decode_attention(tabs, q, cache.k_cache, cache.v_cache, cache.k_norm, cache.v_norm,
+                                 cache.block_table, cache.context_lens, P, w.context, out, ws, err_word=err,
+                                 window_k=cache.win_k, window_v=cache.win_v, window_lens=cache.win_lens,
+                                 k_mean=cache.k_mean, k_mean_scale=cache.k_mean_scale)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    out = out.cpu().numpy()
+    qh = q.float().cpu().numpy()
+    bt = cache.block_table.cpu().numpy()
+    b = 77
+    T = int(cache.lens[b])
+    full = T + w.window
+    k = workloads.kv_rows(w, 0, synth.T_K, b, full).float().cpu().numpy().astype(np.float64)
+    v = workloads.kv_rows(w, 0, synth.T_V, b, full).float().cpu().numpy().astype(np.float64)
+    qm, s16, mrot = _oracle_block_means(k[:T])
+    rk, rv = oracle.encode_tokens(k[:T], tk, mean_rot=mrot), oracle.encode_tokens(v[:T], tv)
+    slots = workloads.slot_mapping(bt[b:b + 1], cache.lens[b:b + 1], P)
+    pg = torch.as_tensor(slots // P, device="cuda", dtype=torch.long)
+    off = torch.as_tensor(slots % P, device="cuda", dtype=torch.long)
+    for c, r, C, meta in ((cache.k_cache, rk, w.container, cache.k_norm), (cache.v_cache, rv, w.cv, cache.v_norm)):
+        got = c.permute(0, 2, 1, 3)[pg, off].reshape(T, -1).cpu().numpy()
+        assert np.array_equal(got[:, :C], r.containers) and not got[:, C:].any()
+        mt = meta[pg, off].cpu().numpy().view(np.uint16)
+        assert np.array_equal(mt[:, 0], r.o16.view(np.uint16)) and np.array_equal(mt[:, 1], r.s16.view(np.uint16))
+    first = slots[::BLK]
+    kmu, ksc = cache.k_mean.cpu().numpy(), cache.k_mean_scale.cpu().numpy().view(np.uint16)
+    R = dq.mean_rows_per_page(P)
+    rp, ri = first // P, (first % P) // BLK
+    assert R == P // BLK
+    for h in range(8):
+        assert np.array_equal(kmu[rp, h, ri], qm[:, h]) and np.array_equal(ksc[rp, h, ri], s16[:, h].view(np.uint16))
+    # the window holds the sequence's newest rows in bf16
+    wk = synth.round_to_bf16(k[T:].astype(np.float32)).astype(np.float64).transpose(1, 0, 2)
+    wv = synth.round_to_bf16(v[T:].astype(np.float32)).astype(np.float64).transpose(1, 0, 2)
+    kh = np.concatenate([oracle.reconstruct_tokens(rk.symbols, rk.o16, rk.s16, mean_rot=mrot).transpose(1, 0, 2), wk],
+                        axis=1)
+    vh = np.concatenate([oracle.reconstruct_tokens(rv.symbols, rv.o16, rv.s16).transpose(1, 0, 2), wv], axis=1)
+    ref = oracle.attention(qh[b:b + 1], [kh], [vh])[0]
+    e = row_rel_err(out[b], ref)
+    assert e.max() <= TOL, e.max()
