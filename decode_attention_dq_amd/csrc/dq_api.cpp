@@ -604,7 +604,8 @@ int dq_token_decode_attention_ext(const dq_tables* t, const void* q, int q_dtype
     if (batch <= 0 || num_q_heads <= 0 || max_pages_per_seq <= 0 || page_size <= 0 || max_context < 0 ||
         num_splits < 0 || (long)max_pages_per_seq * page_size < max_context)
         return DQ_ERR_INVALID_ARG;
-    if (num_q_heads % dq::kTokHeads || num_q_heads / dq::kTokHeads > 4 || (page_size & (page_size - 1)))
+    if (num_q_heads % dq::kTokHeads || num_q_heads / dq::kTokHeads > 4 || (page_size & (page_size - 1)) ||
+        page_size > dq::kTokMaxPage)
         return DQ_ERR_UNSUPPORTED;
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) || ((uintptr_t)k_meta & 3u) ||
         ((uintptr_t)v_meta & 3u))

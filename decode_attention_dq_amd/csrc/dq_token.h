@@ -10,6 +10,7 @@ namespace dq {
 constexpr int kTokHeads = 8;
 constexpr int kTokN = kTokHeads * kHeadDim;   // symbols per stream
 constexpr int kTokMinC = 16, kTokMaxC = 1024; // container bytes
+constexpr int kTokMaxPage = 65536;            // largest page (the attention kernel's 24-bit row offsets)
 
 struct TokEncArgs {
     const void* k;                      // [num_tokens][8][128], bf16 bits or fp32

@@ -61,42 +61,53 @@ struct TokShared {
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-// The three container dwords from byte a (aligned) on, the next refill's
-// source. Row r of a container is dword row0 + r * P of the cache.
+// The three container dwords from byte a (aligned) on: rows a/4 .. a/4 + 2,
+// the next refill's source. Row r of a container is the dword at byte
+// row0 + r * stride of the cache, read through a buffer resource with 32-bit
+// byte offsets (a cache stays under 4 GiB), so a load costs one clamp and one
+// 24-bit multiply-add. Rows past the container's last are read as the last
+// row; a valid stream never consumes their bytes.
 struct GWin {
     uint32_t a, d0, d1, d2;
 };
 struct GSrc {
-    const uint32_t* base;   // the cache as dwords
-    uint32_t row0;          // dword index of the container's first dword
-    uint32_t stride;        // dwords between rows (the page size)
+    uint32_t row0;          // byte offset of the container's first dword
+    uint32_t stride;        // bytes between rows (4 x the page size)
     uint32_t last;          // index of the container's last row
 };
-__device__ __forceinline__ void gwin_load(GWin& g, const GSrc& src, uint32_t ptr) {
-    g.a = ptr & ~3u;
-    const uint32_t r = g.a >> 2;
-    g.d0 = src.base[src.row0 + min(r, src.last) * src.stride];
-    g.d1 = src.base[src.row0 + min(r + 1u, src.last) * src.stride];
-    g.d2 = src.base[src.row0 + min(r + 2u, src.last) * src.stride];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t cache_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFFu, 0x00020000);
 }
-// Move the window past the consumed bytes (ptr - g.a is at most 7, so the
-// window's 4 bytes lie in g's dwords), then start the next dwords' loads.
-__device__ __forceinline__ void grans_refill(RansLane& r, GWin& g, const GSrc& src) {
+__device__ __forceinline__ uint32_t row_load(__amdgpu_buffer_rsrc_t rs, const GSrc& src, uint32_t r) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, __umul24(min(r, src.last), src.stride) + src.row0,
+                                                0, 0);
+}
+// Move the window past the consumed bytes. At most 4 bytes went since the
+// last refill, so ptr - g.a is at most 7: the window's 4 bytes lie in rows
+// a/4 + up and a/4 + up + 1, and the new a is g.a + 4 up. Those two rows stay
+// as the new first two; only the third is loaded, for the next refill.
+__device__ __forceinline__ void grans_refill(RansLane& r, GWin& g, __amdgpu_buffer_rsrc_t rs, const GSrc& src) {
     r.ptr += r.sel - kSel0;
     const bool up = r.ptr - g.a >= 4u;
     const uint32_t lo = up ? g.d1 : g.d0, hi = up ? g.d2 : g.d1;
     r.win = __builtin_amdgcn_alignbyte(hi, lo, r.ptr);
     r.sel = kSel0;
-    gwin_load(g, src, r.ptr);
+    g.a = r.ptr & ~3u;
+    g.d0 = lo;
+    g.d1 = hi;
+    g.d2 = row_load(rs, src, (r.ptr >> 2) + 2u);
 }
 // Stream state from the 3-byte flush at the container's start, then the
 // window at byte 3 (byte offsets count from the container's start).
-__device__ __forceinline__ void grans_init(RansLane& r, GWin& g, const GSrc& src) {
-    gwin_load(g, src, 0u);
+__device__ __forceinline__ void grans_init(RansLane& r, GWin& g, __amdgpu_buffer_rsrc_t rs, const GSrc& src) {
+    g.a = 0u;
+    g.d0 = row_load(rs, src, 0u);
+    g.d1 = row_load(rs, src, 1u);
+    g.d2 = row_load(rs, src, 2u);
     r.ptr = 0u;
     r.x = g.d0 & 0xFFFFFFu;
     r.sel = kSel0 + (uint32_t)kStateBytes;
-    grans_refill(r, g, src);
+    grans_refill(r, g, rs, src);
 }
 
 __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) {
@@ -142,8 +153,7 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
     const uint32_t tabK = (uint32_t)(size_t)(__attribute__((address_space(3))) uint32_t*)&S.tab[0][0];
     const uint32_t tabV = tabK + kTableSlots * 4u;
     const uint32_t maskK = (1u << a.pk) - 1u, maskV = (1u << a.pv) - 1u;
-    const uint32_t* kbase = (const uint32_t*)a.k_cache;
-    const uint32_t* vbase = (const uint32_t*)a.v_cache;
+    const __amdgpu_buffer_rsrc_t kres = cache_rsrc(a.k_cache), vres = cache_rsrc(a.v_cache);
     const float cs = a.softmax_scale * kLog2e / (float)kHeadDim;
 
     float acc[kTokHeads][kGrp][2];
@@ -174,8 +184,9 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
         const float ov = f16_to_f32((uint16_t)(vm & 0xFFFFu)) + sv * a.half_v;
         const uint32_t ck4 = ((uint32_t)a.ck + 3u) >> 2, cv4 = ((uint32_t)a.cv + 3u) >> 2;
         const uint32_t pg = (uint32_t)page * (uint32_t)a.page_size, po = idx - pg;
-        const GSrc sk_ = {kbase, pg * ck4 + po, (uint32_t)a.page_size, ck4 - 1u};
-        const GSrc sv_ = {vbase, pg * cv4 + po, (uint32_t)a.page_size, cv4 - 1u};
+        const uint32_t stride = 4u * (uint32_t)a.page_size;
+        const GSrc sk_ = {4u * (pg * ck4 + po), stride, ck4 - 1u};
+        const GSrc sv_ = {4u * (pg * cv4 + po), stride, cv4 - 1u};
         // key block means: lane 4g + hh gets q~ . (q * s16) of query head
         // (g, hh) and the 128-token block the tile lies in
         float qmu = 0.0f;
@@ -200,13 +211,13 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
         }
         RansLane rk, rv;
         GWin gk, gv;
-        grans_init(rk, gk, sk_);
-        grans_init(rv, gv, sv_);
+        grans_init(rk, gk, kres, sk_);
+        grans_init(rv, gv, vres, sv_);
 
         // K head 0 alone
         float s4[kGrp] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
-            if (c4) grans_refill(rk, gk, sk_);
+            if (c4) grans_refill(rk, gk, kres, sk_);
 #pragma unroll
             for (int i = 0; i < 4; i += 2) {
                 const uint32_t e0 = rans_lookup(rk, tabK, maskK);
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                 for (int hh = 0; hh < kGrp; ++hh) s4[hh] = __builtin_amdgcn_fdot2(q[hh], mm, s4[hh], false);
             }
         }
-        grans_refill(rk, gk, sk_);
+        grans_refill(rk, gk, kres, sk_);
 
         // KV heads in order: the softmax of group g, V head g (fused with K
         // head g + 1 while there is one), the group's p.v. The loop is not
@@ -260,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
 #pragma unroll 1
                 for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
                     if (c4) {
-                        grans_refill(rv, gv, sv_);
-                        grans_refill(rk, gk, sk_);
+                        grans_refill(rv, gv, vres, sv_);
+                        grans_refill(rk, gk, kres, sk_);
                     }
                     uint32_t ev[4];
 #pragma unroll
@@ -283,11 +294,11 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                                                             __builtin_amdgcn_perm(ev[1], ev[0], 0x0C0C0400u),
                                                             0x05040100u);
                 }
-                grans_refill(rk, gk, sk_);
+                grans_refill(rk, gk, kres, sk_);
             } else {
 #pragma unroll 1
                 for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
-                    if (c4) grans_refill(rv, gv, sv_);
+                    if (c4) grans_refill(rv, gv, vres, sv_);
                     uint32_t ev[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -299,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                                                             0x05040100u);
                 }
             }
-            grans_refill(rv, gv, sv_);
+            grans_refill(rv, gv, vres, sv_);
             wave_lds_sync();
 
             // p.v of V head g over token pairs: lane owns channels 2 lane and 2 lane + 1

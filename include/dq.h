@@ -406,6 +406,7 @@ size_t dq_token_workspace_size(int batch, int num_q_heads, int max_context, int 
  *                 caches 16-byte aligned and under 4 GiB each, the metadata
  *                 4-byte aligned
  *   block_table   int32 [batch][max_pages_per_seq]; page_size a power of two
+ *                 of at most 65536 (else DQ_ERR_UNSUPPORTED)
  *   context_lens  int32 [batch], 0 <= len <= max_context (0 gives zeros)
  *   workspace     dq_token_workspace_size bytes, 16-byte aligned
  *   err_word      optional; DQ_DEVERR_DECODE when a stream does not end in
