@@ -36,15 +36,20 @@ constexpr int kVtRowDw = kTile + 1; // dwords per row of the V level transpose (
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-// Products run on v_dot2_f32_f16 (two fp16 products added into fp32): the
-// logits over channel pairs (queries x key levels), p.v over token pairs
-// (weights x value levels). Levels enter centred, m - (M-1)/2, as fp16 whose
-// high byte is the decode entry's level byte (the low byte is zero); the
-// centre joins the offset, so the offset is near the values' mean and the
-// products carry only the centred part.
+// The logits run on v_mfma_f32_16x16x32_f16: after 8 key channels a lane
+// holds 8 fp16 levels of its own token, the B operand for column lane % 16
+// and k-group lane / 16; a block-diagonal A operand (query head h of the
+// group in row 4 (lane / 16) + h, non-zero only in k-group lane / 16) lands
+// the 4 head logits of the lane's own token in its accumulator, so no
+// transpose is needed. p.v runs on v_dot2_f32_f16 (two fp16 products added
+// into fp32) over token pairs (weights x value levels). Levels enter centred,
+// m - (M-1)/2, as fp16 whose high byte is the decode entry's level byte (the
+// low byte is zero); the centre joins the offset, so the offset is near the
+// values' mean and the products carry only the centred part.
 struct TokShared {
     uint32_t tab[2][kTableSlots];                 // decode tables, K then V
-    half2_t qt[kTokHeads][kHeadDim / 2][kGrp];    // rotated queries [KV head][channel pair][head in group]
+    _Float16 qa[kTokHeads][kGrp][kHeadDim];       // rotated queries [KV head][head in group][channel]
+    uint32_t zero[64];                            // A operand of the rows without a head (16 blocks of 16 bytes)
     float qsum[kTokHeads][kGrp];                  // their sums over the channels (fp32)
     union {
         struct {
@@ -122,7 +127,8 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
 
     // ---- prologue: decode tables, rotated queries q~ = H q and their sums
     for (int i = tid; i < 2 * kTableSlots; i += kThreads) (&S.tab[0][0])[i] = a.entries[i];
-    for (int i = tid; i < kTokHeads * kHeadDim / 2 * kGrp; i += kThreads) (&S.qt[0][0][0])[i] = half2_t{0, 0};
+    for (int i = tid; i < kTokHeads * kGrp * kHeadDim / 2; i += kThreads) ((uint32_t*)&S.qa[0][0][0])[i] = 0u;
+    if (tid < 64) S.zero[tid] = 0u;
     if (tid < kTokHeads * kGrp) (&S.qsum[0][0])[tid] = 0.0f;
     __syncthreads();
     for (int h = wave; h < a.num_q_heads; h += kWaves) {
@@ -139,12 +145,8 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
         }
         fwht128_f32(v0, v1, lane);
         const int g = h / G, hh = h - g * G;
-        // lanes 2k, 2k + 1 hold channels 2k, 2k + 1: one half2 per even lane
-        const float o0 = __shfl_xor(v0, 1), o1 = __shfl_xor(v1, 1);
-        if ((lane & 1) == 0) {
-            S.qt[g][lane >> 1][hh] = half2_t{(_Float16)v0, (_Float16)o0};
-            S.qt[g][(lane + 64) >> 1][hh] = half2_t{(_Float16)v1, (_Float16)o1};
-        }
+        S.qa[g][hh][lane] = (_Float16)v0;
+        S.qa[g][hh][lane + 64] = (_Float16)v1;
         const float sum = wave_sum(v0 + v1);
         if (lane == 0) S.qsum[g][hh] = sum;
     }
@@ -155,6 +157,15 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
     const uint32_t maskK = (1u << a.pk) - 1u, maskV = (1u << a.pv) - 1u;
     const __amdgpu_buffer_rsrc_t kres = cache_rsrc(a.k_cache), vres = cache_rsrc(a.v_cache);
     const float cs = a.softmax_scale * kLog2e / (float)kHeadDim;
+    // A operand of the logit MFMA: lane l supplies row l % 16 in k-group
+    // l / 16, the query head (l % 16) & 3 of the group when l / 16 is
+    // (l % 16) / 4, else zeros (16 blocks of 8 channels, 16 bytes each)
+    const char* Sb = (const char*)&S;
+    const int r16 = lane & 15;
+    const bool qrow = (lane >> 4) == (r16 >> 2) && (r16 & 3) < G;
+    const uint32_t qa0 = (uint32_t)((const char*)&S.qa[0][r16 & 3][0] - Sb);
+    const uint32_t qz = (uint32_t)((const char*)&S.zero[0] - Sb);
+    auto q_off = [&](int g) -> uint32_t { return qrow ? qa0 + (uint32_t)g * (kGrp * kHeadDim * 2u) : qz; };
 
     float acc[kTokHeads][kGrp][2];
 #pragma unroll
@@ -203,8 +214,12 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                     const uint32_t w = mr[c4];
                     const half2_t m0 = {(_Float16)(int8_t)(w & 255u), (_Float16)(int8_t)((w >> 8) & 255u)};
                     const half2_t m1 = {(_Float16)(int8_t)((w >> 16) & 255u), (_Float16)(int8_t)(w >> 24)};
-                    d = __builtin_amdgcn_fdot2(S.qt[mg][2 * c4][mh], m0, d, false);
-                    d = __builtin_amdgcn_fdot2(S.qt[mg][2 * c4 + 1][mh], m1, d, false);
+                    // the address is formed here (hoisted, the 32 addresses would take registers)
+                    uint32_t qo = (uint32_t)((const char*)&S.qa[mg][mh][4 * c4] - Sb);
+                    asm volatile("" : "+v"(qo));
+                    const half2_t* qp = (const half2_t*)(Sb + qo);
+                    d = __builtin_amdgcn_fdot2(qp[0], m0, d, false);
+                    d = __builtin_amdgcn_fdot2(qp[1], m1, d, false);
                 }
                 qmu = d * f16_to_f32(a.k_mean_scale[row]);
             }
@@ -214,20 +229,29 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
         grans_init(rk, gk, kres, sk_);
         grans_init(rv, gv, vres, sv_);
 
-        // K head 0 alone
-        float s4[kGrp] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
-            if (c4) grans_refill(rk, gk, kres, sk_);
+        // K head 0 alone; dk[h] ends as the raw logit of head h of the group
+        float4_t dk = {0.0f, 0.0f, 0.0f, 0.0f};
+        {
+            const uint32_t qo = q_off(0);
+#pragma unroll 1
+            for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
+                u32x4 kw;
 #pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-                const uint32_t e0 = rans_lookup(rk, tabK, maskK);
-                rans_advance(rk, e0, (uint32_t)a.pk);
-                const uint32_t e1 = rans_lookup(rk, tabK, maskK);
-                rans_advance(rk, e1, (uint32_t)a.pk);
-                const half2_t mm = __builtin_bit_cast(half2_t, pack_levels(e0, e1));
-                const half2_t* q = &S.qt[0][(4 * c4 + i) >> 1][0];
+                for (int hf = 0; hf < 2; ++hf) {
+                    if (c8 | hf) grans_refill(rk, gk, kres, sk_);
 #pragma unroll
-                for (int hh = 0; hh < kGrp; ++hh) s4[hh] = __builtin_amdgcn_fdot2(q[hh], mm, s4[hh], false);
+                    for (int i = 0; i < 4; i += 2) {
+                        const uint32_t e0 = rans_lookup(rk, tabK, maskK);
+                        rans_advance(rk, e0, (uint32_t)a.pk);
+                        const uint32_t e1 = rans_lookup(rk, tabK, maskK);
+                        rans_advance(rk, e1, (uint32_t)a.pk);
+                        kw[2 * hf + i / 2] = pack_levels(e0, e1);
+                    }
+                }
+                uint32_t qa = qo + 16u * (uint32_t)c8;
+                asm volatile("" : "+v"(qa));
+                const half8 aq = *(const half8*)(Sb + qa);
+                dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, __builtin_bit_cast(half8, kw), dk, 0, 0, 0);
             }
         }
         grans_refill(rk, gk, kres, sk_);
@@ -244,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
             for (int hh = 0; hh < kGrp; ++hh) {
                 const int hl = 4 * g + hh;
                 const float qm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qmu), hl));
-                const float L = valid ? (ok * S.qsum[g][hh] + (sk * s4[hh] + qm)) * cs : -INFINITY;
+                const float L = valid ? (ok * S.qsum[g][hh] + (sk * dk[hh] + qm)) * cs : -INFINITY;
                 const float mt = wave_max_uniform(L);
                 const float mo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), hl));
                 const float mn = fmaxf(mo, mt);
@@ -265,34 +289,40 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                 if ((lane & 1) == 0) Wv.w[lane >> 1][hh] = half2_t{(_Float16)wv[hh], (_Float16)wn};
             }
 
-            s4[0] = s4[1] = s4[2] = s4[3] = 0.0f;
+            dk = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
             if (g + 1 < kTokHeads) {
-                const half2_t* qn = &S.qt[g + 1][0][0];
+                const uint32_t qo = q_off(g + 1);
 #pragma unroll 1
-                for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
-                    if (c4) {
-                        grans_refill(rv, gv, vres, sv_);
-                        grans_refill(rk, gk, kres, sk_);
-                    }
-                    uint32_t ev[4];
+                for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
+                    u32x4 kw;
 #pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        ev[i] = rans_lookup(rv, tabV, maskV);
-                        const uint32_t e0 = rans_lookup(rk, tabK, maskK);
-                        rans_advance(rv, ev[i], (uint32_t)a.pv);
-                        rans_advance(rk, e0, (uint32_t)a.pk);
-                        ev[i + 1] = rans_lookup(rv, tabV, maskV);
-                        const uint32_t e1 = rans_lookup(rk, tabK, maskK);
-                        rans_advance(rv, ev[i + 1], (uint32_t)a.pv);
-                        rans_advance(rk, e1, (uint32_t)a.pk);
-                        const half2_t mm = __builtin_bit_cast(half2_t, pack_levels(e0, e1));
-                        const half2_t* q = qn + ((4 * c4 + i) >> 1) * kGrp;
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int c4 = 2 * c8 + hf;
+                        if (c4) {
+                            grans_refill(rv, gv, vres, sv_);
+                            grans_refill(rk, gk, kres, sk_);
+                        }
+                        uint32_t ev[4];
 #pragma unroll
-                        for (int hh = 0; hh < kGrp; ++hh) s4[hh] = __builtin_amdgcn_fdot2(q[hh], mm, s4[hh], false);
+                        for (int i = 0; i < 4; i += 2) {
+                            ev[i] = rans_lookup(rv, tabV, maskV);
+                            const uint32_t e0 = rans_lookup(rk, tabK, maskK);
+                            rans_advance(rv, ev[i], (uint32_t)a.pv);
+                            rans_advance(rk, e0, (uint32_t)a.pk);
+                            ev[i + 1] = rans_lookup(rv, tabV, maskV);
+                            const uint32_t e1 = rans_lookup(rk, tabK, maskK);
+                            rans_advance(rv, ev[i + 1], (uint32_t)a.pv);
+                            rans_advance(rk, e1, (uint32_t)a.pk);
+                            kw[2 * hf + i / 2] = pack_levels(e0, e1);
+                        }
+                        Wv.vt[c4][lane] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(ev[3], ev[2], 0x0C0C0400u),
+                                                                __builtin_amdgcn_perm(ev[1], ev[0], 0x0C0C0400u),
+                                                                0x05040100u);
                     }
-                    Wv.vt[c4][lane] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(ev[3], ev[2], 0x0C0C0400u),
-                                                            __builtin_amdgcn_perm(ev[1], ev[0], 0x0C0C0400u),
-                                                            0x05040100u);
+                    uint32_t qa = qo + 16u * (uint32_t)c8;
+                    asm volatile("" : "+v"(qa));
+                    const half8 aq = *(const half8*)(Sb + qa);
+                    dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, __builtin_bit_cast(half8, kw), dk, 0, 0, 0);
                 }
                 grans_refill(rk, gk, kres, sk_);
             } else {
