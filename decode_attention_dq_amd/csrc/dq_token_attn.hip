@@ -32,17 +32,21 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;           // tokens per wave tile, one per lane
 constexpr int kGrp = 4;             // query heads per KV head held (GQA group <= 4)
-constexpr int kVtRowDw = kTile + 1; // dwords per row of the V level transpose (padded)
+constexpr int kVtRowDw = kTile + 4; // dwords per row of the V level transpose (16-byte rows, padded)
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // The logits run on v_mfma_f32_16x16x32_f16: after 8 key channels a lane
 // holds 8 fp16 levels of its own token, the B operand for column lane % 16
 // and k-group lane / 16; a block-diagonal A operand (query head h of the
 // group in row 4 (lane / 16) + h, non-zero only in k-group lane / 16) lands
 // the 4 head logits of the lane's own token in its accumulator, so no
-// transpose is needed. p.v runs on v_dot2_f32_f16 (two fp16 products added
-// into fp32) over token pairs (weights x value levels). Levels enter centred,
+// transpose is needed. p.v runs on v_mfma_f32_4x4x4f16 (16 blocks of 4x4x4):
+// block b of the MFMA takes channels 4b..4b+3 and 4 tokens, the same weights
+// in every block, so lane l ends with the 4 query heads of channel l (and of
+// l + 64 in a second accumulator). Levels enter centred,
 // m - (M-1)/2, as fp16 whose high byte is the decode entry's level byte (the
 // low byte is zero); the centre joins the offset, so the offset is near the
 // values' mean and the products carry only the centred part.
@@ -51,10 +55,10 @@ struct TokShared {
     _Float16 qa[kTokHeads][kGrp][kHeadDim];       // rotated queries [KV head][head in group][channel]
     uint32_t zero[64];                            // A operand of the rows without a head (16 blocks of 16 bytes)
     float qsum[kTokHeads][kGrp];                  // their sums over the channels (fp32)
-    union {
+    union alignas(16) {
         struct {
             uint32_t vt[kHeadDim / 4][kVtRowDw];  // V level bytes: row k holds channels 4k..4k+3, column = token
-            half2_t w[kTile / 2][kGrp];           // p * s_v per token pair and head
+            _Float16 w[kGrp][kTile];              // p * s_v per head and token
         } wave[kWaves];
         struct {
             float acc[kWaves][kGrp][kHeadDim];
@@ -167,20 +171,19 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
     const uint32_t qz = (uint32_t)((const char*)&S.zero[0] - Sb);
     auto q_off = [&](int g) -> uint32_t { return qrow ? qa0 + (uint32_t)g * (kGrp * kHeadDim * 2u) : qz; };
 
-    float acc[kTokHeads][kGrp][2];
+    // acc[g][c][h]: query head h of group g at channel lane + 64 c
+    float4_t acc[kTokHeads][2];
 #pragma unroll
-    for (int g = 0; g < kTokHeads; ++g)
-#pragma unroll
-        for (int hh = 0; hh < kGrp; ++hh) acc[g][hh][0] = acc[g][hh][1] = 0.0f;
+    for (int g = 0; g < kTokHeads; ++g) acc[g][0] = acc[g][1] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     float mrun = -INFINITY, lrun = 0.0f;   // lane 4g + hh: running max and sum of head (g, hh)
     bool bad = false;
     auto& Wv = S.u.wave[wave];
-    // p.v operands: channel 2 lane sits in byte 2 (lane & 1) of row lane / 2 of
-    // the transpose; the selectors pair that byte of tokens t and t + 1 into
-    // the high bytes of an fp16 pair
-    const uint32_t vrow = (uint32_t)lane >> 1, vb = ((uint32_t)lane & 1u) * 2u;
-    const uint32_t vsel0 = 0x000C000Cu | (vb << 8) | ((vb + 4u) << 24);
-    const uint32_t vsel1 = vsel0 + 0x01000100u;
+    // p.v B operand: channel lane (lane + 64) is byte lane & 3 of row lane / 4
+    // (16 + lane / 4) of the transpose; the selector puts that byte of two
+    // tokens' dwords into the high bytes of an fp16 pair
+    const uint32_t vb = (uint32_t)lane & 3u;
+    const uint32_t vsel = 0x000C000Cu | (vb << 8) | ((vb + 4u) << 24);
+    const uint32_t vrow = (uint32_t)lane >> 2;
 
     for (int t0 = start + wave * kTile; t0 < end; t0 += kWaves * kTile) {
         const int t = t0 + lane;
@@ -277,8 +280,8 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                 const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lrun), hl));
                 const float ln = lo * fac + wave_sum_uniform(p);
                 const float os = wave_sum_uniform(p * ov);
-                acc[0][hh][0] = acc[0][hh][0] * fac + os;
-                acc[0][hh][1] = acc[0][hh][1] * fac + os;
+                acc[0][0][hh] = acc[0][0][hh] * fac + os;
+                acc[0][1][hh] = acc[0][1][hh] * fac + os;
                 mrun = lane == hl ? mn : mrun;
                 lrun = lane == hl ? ln : lrun;
                 wv[hh] = p * sv;
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
 #pragma unroll
             for (int hh = 0; hh < kGrp; ++hh) {
                 const float wn = __shfl_xor(wv[hh], 1);   // the pair partner's weight (token lane ^ 1)
-                if ((lane & 1) == 0) Wv.w[lane >> 1][hh] = half2_t{(_Float16)wv[hh], (_Float16)wn};
+                if ((lane & 1) == 0) *(half2_t*)&Wv.w[hh][lane] = half2_t{(_Float16)wv[hh], (_Float16)wn};
             }
 
             dk = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -343,31 +346,26 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
             grans_refill(rv, gv, vres, sv_);
             wave_lds_sync();
 
-            // p.v of V head g over token pairs: lane owns channels 2 lane and 2 lane + 1
+            // p.v of V head g, 4 tokens per MFMA: the A operand is head lane & 3's
+            // weights of the 4 tokens, the B operand channel lane's (lane + 64's)
+            // levels of the same tokens
 #pragma unroll 4
-            for (int j = 0; j < kTile; j += 2) {
-                const uint32_t d0 = Wv.vt[vrow][j], d1 = Wv.vt[vrow][j + 1];
-                const half2_t m0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(d1, d0, vsel0));
-                const half2_t m1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(d1, d0, vsel1));
-                const half2_t* w2 = &Wv.w[j >> 1][0];
-#pragma unroll
-                for (int hh = 0; hh < kGrp; ++hh) {
-                    const half2_t wp = w2[hh];
-                    acc[0][hh][0] = __builtin_amdgcn_fdot2(wp, m0, acc[0][hh][0], false);
-                    acc[0][hh][1] = __builtin_amdgcn_fdot2(wp, m1, acc[0][hh][1], false);
-                }
+            for (int j = 0; j < kTile; j += 4) {
+                const u32x4 d0 = *(const u32x4*)&Wv.vt[vrow][j];
+                const u32x4 d1 = *(const u32x4*)&Wv.vt[16 + vrow][j];
+                const half4_t aw = *(const half4_t*)&Wv.w[lane & 3][j];
+                const u32x2 b0 = {__builtin_amdgcn_perm(d0[1], d0[0], vsel), __builtin_amdgcn_perm(d0[3], d0[2], vsel)};
+                const u32x2 b1 = {__builtin_amdgcn_perm(d1[1], d1[0], vsel), __builtin_amdgcn_perm(d1[3], d1[2], vsel)};
+                acc[0][0] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw, __builtin_bit_cast(half4_t, b0), acc[0][0], 0, 0, 0);
+                acc[0][1] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw, __builtin_bit_cast(half4_t, b1), acc[0][1], 0, 0, 0);
             }
             wave_lds_sync();
             // rotate: the next group's accumulators to the front
-            float first[kGrp][2];
+            const float4_t first0 = acc[0][0], first1 = acc[0][1];
 #pragma unroll
-            for (int hh = 0; hh < kGrp; ++hh) first[hh][0] = acc[0][hh][0], first[hh][1] = acc[0][hh][1];
-#pragma unroll
-            for (int gg = 0; gg + 1 < kTokHeads; ++gg)
-#pragma unroll
-                for (int hh = 0; hh < kGrp; ++hh) acc[gg][hh][0] = acc[gg + 1][hh][0], acc[gg][hh][1] = acc[gg + 1][hh][1];
-#pragma unroll
-            for (int hh = 0; hh < kGrp; ++hh) acc[kTokHeads - 1][hh][0] = first[hh][0], acc[kTokHeads - 1][hh][1] = first[hh][1];
+            for (int gg = 0; gg + 1 < kTokHeads; ++gg) acc[gg][0] = acc[gg + 1][0], acc[gg][1] = acc[gg + 1][1];
+            acc[kTokHeads - 1][0] = first0;
+            acc[kTokHeads - 1][1] = first1;
         }
         // both streams must end in the initial state having read no byte past C
         const bool okk = rk.x == kStateLow && rk.ptr + (rk.sel - kSel0) <= (uint32_t)a.ck;
@@ -378,12 +376,12 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
 
     // ---- combine the 4 waves' partials per KV head and write them
     __syncthreads();
-    auto combine = [&](auto gtag, const float (&ag)[kGrp][2]) {
+    auto combine = [&](auto gtag, const float4_t (&ag)[2]) {
         constexpr int g = decltype(gtag)::value;
 #pragma unroll
         for (int hh = 0; hh < kGrp; ++hh) {
-            S.u.red.acc[wave][hh][2 * lane] = ag[hh][0];
-            S.u.red.acc[wave][hh][2 * lane + 1] = ag[hh][1];
+            S.u.red.acc[wave][hh][lane] = ag[0][hh];
+            S.u.red.acc[wave][hh][lane + 64] = ag[1][hh];
         }
         const float mg = __shfl(mrun, 4 * g + (lane & 3)), lg = __shfl(lrun, 4 * g + (lane & 3));
         if (lane < kGrp) {
