@@ -70,6 +70,36 @@ struct TokShared {
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// Wave-wide max and sum as wave-uniform values: the butterflies and row
+// broadcasts of the DPP reduction each as one v_max/v_add with a DPP source
+// (the compiler's forms add a move, and for the max a canonicalisation, per
+// stage). Each stage reads the previous one's result, so two wait states
+// precede it. Every lane must be active; the values are never NaN.
+__device__ __forceinline__ float tok_wave_max(float v) {
+    asm volatile(
+        "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+v"(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float tok_wave_sum(float v) {
+    asm volatile(
+        "s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+v"(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // The three container dwords from byte a (aligned) on: rows a/4 .. a/4 + 2,
 // the next refill's source. Row r of a container is the dword at byte
 // row0 + r * stride of the cache, read through a buffer resource with 32-bit
@@ -272,14 +302,15 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                 const int hl = 4 * g + hh;
                 const float qm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qmu), hl));
                 const float L = valid ? (ok * S.qsum[g][hh] + (sk * dk[hh] + qm)) * cs : -INFINITY;
-                const float mt = wave_max_uniform(L);
+                const float mt = tok_wave_max(L);
                 const float mo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), hl));
                 const float mn = fmaxf(mo, mt);
-                const float fac = exp2f(mo - mn);
-                const float p = valid ? exp2f(L - mn) : 0.0f;
+                // both arguments are <= 0 (or -inf): v_exp_f32 as it stands
+                const float fac = __builtin_amdgcn_exp2f(mo - mn);
+                const float p = valid ? __builtin_amdgcn_exp2f(L - mn) : 0.0f;
                 const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lrun), hl));
-                const float ln = lo * fac + wave_sum_uniform(p);
-                const float os = wave_sum_uniform(p * ov);
+                const float ln = lo * fac + tok_wave_sum(p);
+                const float os = tok_wave_sum(p * ov);
                 acc[0][0][hh] = acc[0][0][hh] * fac + os;
                 acc[0][1][hh] = acc[0][1][hh] * fac + os;
                 mrun = lane == hl ? mn : mrun;
@@ -287,10 +318,7 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                 wv[hh] = p * sv;
             }
 #pragma unroll
-            for (int hh = 0; hh < kGrp; ++hh) {
-                const float wn = __shfl_xor(wv[hh], 1);   // the pair partner's weight (token lane ^ 1)
-                if ((lane & 1) == 0) *(half2_t*)&Wv.w[hh][lane] = half2_t{(_Float16)wv[hh], (_Float16)wn};
-            }
+            for (int hh = 0; hh < kGrp; ++hh) Wv.w[hh][lane] = (_Float16)wv[hh];
 
             dk = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
             if (g + 1 < kTokHeads) {
