@@ -224,6 +224,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     // (do_v): two independent decode chains per lane, the q.k MFMA after each
     // 8 key channels, the p.v MFMAs after each 16 value channels.
     auto pass = [&](bool do_k, bool do_v, RansLane& kr, RansLane& vr, float4v& dk) {
+        // the weights are the same A operand for every 16 channels of the tile
+        half8 av[2];
+        if (do_v) {
+            av[0] = *(const half8*)(lds + ap_off);
+            av[1] = *(const half8*)(lds + ap_off + 64u);
+        }
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
 #pragma unroll
@@ -272,12 +278,11 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
                 wave_lds_sync();
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
-                    const half8 av = *(const half8*)(lds + ap_off + 64u * hf);
                     const uint32_t src = tr0 + (uint32_t)hf * 32u * kVtRow;
                     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_base + src));
                     const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_base + src + 4u * kVtRow));
                     const half8 bv = __builtin_bit_cast(half8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[blk], 0, 0, 0);
+                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[hf], bv, acc[blk], 0, 0, 0);
                 }
                 wave_lds_sync();
             }

@@ -76,6 +76,7 @@ __device__ __forceinline__ void rans_advance(RansLane& r, uint32_t e, uint32_t p
     const bool need = xn < kStateLow;
     r.x = need ? t : xn;
     r.sel += need ? 1u : 0u;
+    asm volatile("" : "+v"(r.sel));   // one carry-in add per step (no 0/1 temporaries summed in a tree)
 }
 __device__ __forceinline__ uint32_t rans_dec_step(RansLane& r, uint32_t tab, uint32_t mask, uint32_t p) {
     const uint32_t e = *(lds_u32*)(size_t)(tab + ((r.x & mask) << 2));
@@ -86,6 +87,7 @@ __device__ __forceinline__ uint32_t rans_dec_step(RansLane& r, uint32_t tab, uin
     const bool need = xn < kStateLow;
     r.x = need ? t : xn;
     r.sel += need ? 1u : 0u;
+    asm volatile("" : "+v"(r.sel));   // one carry-in add per step (no 0/1 temporaries summed in a tree)
     return e;
 }
 
