@@ -72,6 +72,16 @@ __device__ __forceinline__ int wave_sum_i(int v) {
     return v;
 }
 
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -310,21 +320,57 @@ __device__ __forceinline__ Cands rank_candidates(const EncTable* T, double z0, d
     r.pos0 = __popcll(bal0 & lt_mask);
     r.pos1 = __popcll(bal0) + __popcll(bal1 & lt_mask);
     r.nc = __popcll(bal0) + __popcll(bal1);
-    if (r.c0) { W.key[r.pos0] = k0; W.dr[r.pos0] = r.dr0; }
-    if (r.c1) { W.key[r.pos1] = k1; W.dr[r.pos1] = r.dr1; }
+    if (r.c0) W.key[r.pos0] = k0;
+    if (r.c1) W.key[r.pos1] = k1;
     wave_sync();
+    // Ranks by key alone. Distinct keys give distinct ranks; candidates with
+    // equal keys share one, and only then is the channel order needed.
     r.rank0 = 0; r.rank1 = 0; r.cb0 = 0; r.cb1 = 0; r.tot = 0;
     for (int j = 0; j < r.nc; ++j) {
         const uint64_t kj = W.key[j];
-        const int dj = W.dr[j];
-        r.tot += dj;
-        const bool a0 = kj < k0 || (kj == k0 && j < r.pos0);
-        const bool a1 = kj < k1 || (kj == k1 && j < r.pos1);
-        r.rank0 += a0;
-        r.cb0 += a0 ? dj : 0;
-        r.rank1 += a1;
-        r.cb1 += a1 ? dj : 0;
+        r.rank0 += kj < k0 ? 1 : 0;
+        r.rank1 += kj < k1 ? 1 : 0;
     }
+    if (r.c0) W.dr[r.rank0] = r.pos0;
+    if (r.c1) W.dr[r.rank1] = r.pos1;
+    wave_sync();
+    const bool clash = (r.c0 && W.dr[r.rank0] != r.pos0) || (r.c1 && W.dr[r.rank1] != r.pos1);
+    wave_sync();
+    if (__ballot(clash)) {
+        // equal keys: (key, channel) order, counted against every candidate
+        if (r.c0) W.dr[r.pos0] = r.dr0;
+        if (r.c1) W.dr[r.pos1] = r.dr1;
+        wave_sync();
+        r.rank0 = 0; r.rank1 = 0;
+        for (int j = 0; j < r.nc; ++j) {
+            const uint64_t kj = W.key[j];
+            const int dj = W.dr[j];
+            r.tot += dj;
+            const bool a0 = kj < k0 || (kj == k0 && j < r.pos0);
+            const bool a1 = kj < k1 || (kj == k1 && j < r.pos1);
+            r.rank0 += a0;
+            r.cb0 += a0 ? dj : 0;
+            r.rank1 += a1;
+            r.cb1 += a1 ? dj : 0;
+        }
+        wave_sync();
+        return r;
+    }
+    // the rate removed ahead of each candidate: exclusive prefix sums of the
+    // rates in rank order (lane holds ranks lane and lane + 64)
+    if (r.c0) W.dr[r.rank0] = r.dr0;
+    if (r.c1) W.dr[r.rank1] = r.dr1;
+    wave_sync();
+    const int d0 = lane < r.nc ? W.dr[lane] : 0, d1 = lane + 64 < r.nc ? W.dr[lane + 64] : 0;
+    const int s0 = wave_incl_scan_i(d0, lane), s1 = wave_incl_scan_i(d1, lane);
+    const int t0 = __shfl(s0, 63), t1 = __shfl(s1, 63);
+    wave_sync();
+    W.dr[lane] = s0 - d0;
+    W.dr[lane + 64] = t0 + s1 - d1;
+    wave_sync();
+    r.tot = t0 + t1;
+    if (r.c0) r.cb0 = W.dr[r.rank0];
+    if (r.c1) r.cb1 = W.dr[r.rank1];
     wave_sync();
     return r;
 }

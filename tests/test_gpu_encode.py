@@ -97,6 +97,50 @@ def test_encode_edge_rows(gpu_lib):
     _check(dq, tabs, tk, tv, k, v, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
 
 
+def _tied_rows(n, seed, tables):
+    """n rows whose rotation is a small-integer vector y (x = H y / 128 is exact
+    in fp32 and H x gives y back exactly), so that many channels share one
+    unit-RMS value; kept are rows that drift under every table and whose drift
+    candidates share keys (checked with the oracle's own quantities)."""
+    rng = np.random.default_rng(seed)
+    y = rng.integers(-3, 4, size=(4 * n, 128)).astype(np.float64)
+    keep = np.ones(len(y), dtype=bool)
+    _, _, z = oracle.normalize(y)
+    for t in tables:
+        m = oracle.nearest_level(z, t)
+        keep &= t.cost[m].sum(axis=-1) > t.budget_fx
+        inner = t.inner[m]
+        has = inner >= 0
+        inner = np.where(has, inner, m)
+        dr = np.where(has, t.cost[m] - t.cost[inner], 0)
+        cand = has & (dr > 0)
+        dd = (z - t.recon[inner]) ** 2 - (z - t.recon[m]) ** 2
+        for s in np.flatnonzero(keep):
+            keys = dd[s][cand[s]] / dr[s][cand[s]]
+            keep[s] = np.unique(keys).size < keys.size
+    y = y[keep][:n]
+    assert len(y) == n, "too few rows with tied drift keys"
+    x = oracle.fwht(y) / 128.0
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    return x.astype(np.float32)
+
+
+def test_encode_equal_drift_keys(gpu_lib):
+    """Drift candidates with equal keys take the (key, channel) order; rows with
+    and without such ties share each wave."""
+    dq = gpu_lib
+    tk, tv = oracle.make_table(8, 37), oracle.make_table(6, 37)
+    tabs = dq.dq_tables_init(dq.make_params(8, 37), dq.make_params(6, 37))
+    tied = _tied_rows(96, 11, (tk, tv))
+    gauss = synth.gaussian_kv(3, synth.T_K, 96, 1).reshape(96, 128)
+    rows = np.empty((192, 128), dtype=np.float32)
+    rows[0::2] = tied
+    rows[1::2] = gauss
+    k = np.ascontiguousarray(rows.reshape(-1, 1, 128))
+    v = np.ascontiguousarray(rows[::-1].reshape(-1, 1, 128))
+    _check(dq, tabs, tk, tv, k, v, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+
+
 def test_encode_fallback_rounds(gpu_lib):
     """A budget so tight that one drift round is not always enough."""
     dq = gpu_lib
