@@ -4,13 +4,13 @@
 // floating-point decision is an IEEE fp64 operation in a fixed order with no
 // contraction (this file is compiled with -ffp-contract=off).
 //
-// Work decomposition: a wave takes up to 64 consecutive streams.
+// Work decomposition: a wave takes up to kPerWave (32) consecutive streams.
 //   1. lane = channel, one stream after another (the next stream's inputs are
 //      already in flight): rotation, norm, nearest level, the drift candidates
 //      and their (key, channel) ranks. What stays in LDS per stream is the
 //      symbol row of the minimal candidate prefix and the channels of the
 //      next candidates in order.
-//   2. lane = stream: the 64 serial rANS encodes run side by side. A stream
+//   2. lane = stream: the serial rANS encodes run side by side. A stream
 //      whose encoding overflows takes the next candidate and encodes again.
 //   3. lane = stream: a last encode writes each container.
 // A stream that the first drift round cannot fit (no prefix fits, or it needs
@@ -28,6 +28,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kMaxRounds = 64;
 constexpr int kTail = 16;         // candidates staged per stream beyond the minimal prefix
+constexpr int kPerWave = 32;      // most streams a wave takes (lanes of the serial phase)
 constexpr int kRow = 132;         // LDS bytes per stream symbol row (an odd number of dwords)
 
 // fp64 -> fp16 bits with a single rounding to nearest even; overflow gives inf.
@@ -103,11 +104,11 @@ struct Scratch {
 
 struct WaveLds {
     Scratch sc;
-    uint8_t sym[64][kRow];        // symbol row of each stream
-    uint8_t ord[64][kTail];       // channels of the staged candidates, in (key, channel) order
-    int32_t kmin[64];             // candidates in the minimal prefix
-    int32_t staged[64];           // staged candidates; -1: redo with the per-stream procedure
-    int32_t meta[64];             // bit 0: over budget before drift; bits 16..31: rho16
+    uint8_t sym[kPerWave][kRow];  // symbol row of each stream
+    uint8_t ord[kPerWave][kTail]; // channels of the staged candidates, in (key, channel) order
+    int32_t kmin[kPerWave];       // candidates in the minimal prefix
+    int32_t staged[kPerWave];     // staged candidates; -1: redo with the per-stream procedure
+    int32_t meta[kPerWave];       // bit 0: over budget before drift; bits 16..31: rho16
 };
 
 // rANS encode of sym[127..0] (section 3.1, Enc) by one lane: before each
@@ -527,7 +528,7 @@ __global__ __launch_bounds__(64 * kWaves) void mean_kernel(EncArgs a) {
     if (lane == 0) a.k_mean_scale[row] = s16;
 }
 
-__global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a, int per_wave) {
+__global__ __launch_bounds__(64 * kWaves, 5) void encode_kernel(EncArgs a, int per_wave) {
     __shared__ WaveLds wl_all[kWaves];
     __shared__ SymConst sconst[2][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -550,7 +551,7 @@ __global__ __launch_bounds__(64 * kWaves) void encode_kernel(EncArgs a, int per_
     const long total = 2l * a.num_tokens * a.num_kv_heads;
     const long sid0 = ((long)blockIdx.x * kWaves + wave) * per_wave;
     if (sid0 >= total) return;
-    const int nb = (int)min((long)per_wave, total - sid0);   // streams of this wave, <= 64
+    const int nb = (int)min((long)per_wave, total - sid0);   // streams of this wave, <= kPerWave
 
     // ---- phase 1: lane = channel, one stream at a time
     int slot_n = -1;
@@ -1009,9 +1010,12 @@ __global__ void token_decode_symbols_kernel(const EncTable* __restrict__ T, cons
 
 }  // namespace
 
-// Streams per wave: 64 (one per lane in the serial phase) for large writes;
-// fewer when that would leave the chip short of waves (about 3072 fit at
-// once: 256 CUs x 12), since a wave walks its streams one at a time first.
+// Streams per wave: kPerWave (one per lane in the serial phase) for large
+// writes; fewer when that would leave the chip short of waves (about 5120 fit
+// at once: 256 CUs x 20), since a wave walks its streams one at a time first.
+// Waves stalled on fp64 divide chains and cross-lane moves are hidden by
+// occupancy: 32 streams per wave keep the LDS at 28 KB per work-group, and
+// the launch bound holds the registers to 96, so 5 waves share a SIMD.
 hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
     if (a.k_mean) {
         const long waves = (long)(a.num_tokens / kMeanBlock) * a.num_kv_heads;
@@ -1020,8 +1024,8 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     const long streams = 2l * a.num_tokens * a.num_kv_heads;
-    const long waves_wanted = 3072;
-    const int per_wave = (int)std::min(64l, std::max(1l, (streams + waves_wanted - 1) / waves_wanted));
+    const long waves_wanted = 5120;
+    const int per_wave = (int)std::min((long)kPerWave, std::max(1l, (streams + waves_wanted - 1) / waves_wanted));
     const long per_block = (long)per_wave * kWaves;
     dim3 grid((unsigned)((streams + per_block - 1) / per_block));
     hipLaunchKernelGGL(encode_kernel, grid, dim3(64 * kWaves), 0, s, a, per_wave);
