@@ -727,7 +727,10 @@ struct Nib16 {
     }
 };
 
-__global__ __launch_bounds__(64 * kWaves, 2) void token_encode_kernel(TokEncArgs a) {
+// 6 waves per SIMD: the serial rANS of one lane per wave is latency bound, so
+// more waves in flight pay for the registers the bound spills (16.5 ms at 2
+// waves per SIMD, 10.3 ms at 4, 9.4 ms at 6, 13.5 ms at 8 for 262,144 streams).
+__global__ __launch_bounds__(64 * kWaves, 6) void token_encode_kernel(TokEncArgs a) {
     __shared__ TokLds tl_all[kWaves];
     __shared__ SymConst sconst[2][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
