@@ -699,6 +699,7 @@ int token_encode_impl(const dq_tables* t, const void* k, const void* v, int dtyp
     a.drift_stats = drift_stats;
     a.err_word = err_word;
     a.tables = t->d_enc;
+    a.max_c = std::max(t->enc[0].container, t->enc[1].container);
     a.k_mean = k_mean;
     a.k_mean_scale = k_mean_scale;
     hipError_t e = dq::launch_token_encode(a, (hipStream_t)stream);

@@ -22,6 +22,7 @@ struct TokEncArgs {
     uint32_t* drift_stats;              // optional [num_tokens][2]: changed | rounds << 16
     uint32_t* err_word;
     const EncTable* tables;             // device copy: [0] keys, [1] values
+    int max_c;                          // the larger of the two container sizes (sizes the kernel's LDS)
     // key block means (blocks of 128 rows of the call, as for the per-head
     // format with 8 KV heads), written by a pass before the streams; null when off
     int8_t* k_mean;                     // [pages][8][mean_rows_per_page][128]

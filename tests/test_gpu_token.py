@@ -113,6 +113,42 @@ def test_token_encode_bit_exact(setup, bf16):
     assert not kc[unused].any() and not km[unused].any()
 
 
+def test_token_encode_later_rounds(gpu_lib):
+    """Key streams whose first drift round cannot bring the rate under a tight
+    budget (several rounds, the per-stream procedure) next to value streams that
+    fit in the first round, in the same waves: all bit-exact."""
+    dq = gpu_lib
+    kcfg = (8, 200)
+    tk, tv = oracle.make_token_table(*kcfg), oracle.make_token_table(*V_CFG)
+    tabs = dq.dq_token_tables_init(dq.make_params(*kcfg), dq.make_params(*V_CFG))
+    n, P = 96, 16
+    k = _tokens(5, synth.T_K, n)
+    v = _tokens(5, synth.T_V, n)
+    rk = oracle.encode_tokens(k.astype(np.float64), tk)
+    rv = oracle.encode_tokens(v.astype(np.float64), tv)
+    assert (rk.rounds > 1).sum() > n // 2 and (rv.rounds <= 1).all(), "case no longer exercises both paths"
+    slots = np.random.default_rng(4).permutation(n).astype(np.int32)
+    pages = n // P
+    kc = torch.zeros(dq.token_cache_shape(pages, P, kcfg[1]), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros(dq.token_cache_shape(pages, P, V_CFG[1]), dtype=torch.uint8, device="cuda")
+    km = torch.zeros((pages, P, 2), dtype=torch.int16, device="cuda")
+    vm = torch.zeros_like(km)
+    ds = torch.zeros((n, 2), dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_encode_tokens(tabs, _dev(k), _dev(v), _dev(slots), kc, vc, km, vm, P, drift_stats=ds, err_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    kc = _from_pages(kc.cpu().numpy(), kcfg[1])[:, :kcfg[1]]
+    vc = _from_pages(vc.cpu().numpy(), V_CFG[1])[:, :V_CFG[1]]
+    km, vm = km.cpu().numpy().view(np.uint16).reshape(-1, 2), vm.cpu().numpy().view(np.uint16).reshape(-1, 2)
+    ds = ds.cpu().numpy().view(np.uint32)
+    assert np.array_equal(kc[slots], rk.containers) and np.array_equal(vc[slots], rv.containers)
+    assert np.array_equal(km[slots, 0], rk.o16.view(np.uint16)) and np.array_equal(km[slots, 1], rk.s16.view(np.uint16))
+    assert np.array_equal(vm[slots, 0], rv.o16.view(np.uint16)) and np.array_equal(vm[slots, 1], rv.s16.view(np.uint16))
+    assert np.array_equal(ds[:, 0] & 0xFFFF, rk.changed) and np.array_equal(ds[:, 0] >> 16, rk.rounds)
+    assert np.array_equal(ds[:, 1] & 0xFFFF, rv.changed) and np.array_equal(ds[:, 1] >> 16, rv.rounds)
+
+
 def test_token_decode_symbols(setup):
     """Oracle containers decode to the oracle's symbols; a corrupted container
     sets the decode flag."""
