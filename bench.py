@@ -337,6 +337,29 @@ ATTN_SOURCES = ("dq_attn.hip", "dq_device.h", "dq_wave.h", "dq_sched.h", "dq_int
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def copy_measurement(torch, nbytes: int = 1 << 30, reps: int = 7) -> dict:
+    """The box's achievable HBM rate for a plain device-to-device copy of
+    `nbytes` (read + write bytes over the median copy time), the reference the
+    compressed-byte rate is also quoted against."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    del src, dst
+    t = float(np.median(times))
+    return {"bytes": nbytes, "read_plus_write_GBps": round(2 * nbytes / t / 1e9, 1),
+            "frac_of_peak": round(2 * nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def attn_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
@@ -519,6 +542,7 @@ def main() -> int:
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
         "us_per_layer_call": round(per_call_s * 1e6, 2),
+        "us_per_layer_call_p10_p50_p90": [round(float(np.percentile(call_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
         "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
                      "unit": "Tops/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
                      "traffic": recorded_traffic("attn_kernel", w.name),
@@ -529,6 +553,9 @@ def main() -> int:
     if not args.layers:
         del caches, qs
         torch.cuda.empty_cache()
+        cp = copy_measurement(torch)
+        cp["compressed_frac_of_copy"] = round(gbs / cp["read_plus_write_GBps"], 4)
+        result["copy_reference"] = cp
         result["encode"] = encode_measurement(dq, torch, workloads)
         result["other_workloads"] = {
             "long_llama_b4": config_measurement(dq, torch, workloads, "long_llama_b4", copies=4),
