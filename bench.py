@@ -33,7 +33,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12      # int32 lane-ops per second, in T
-OPS_PER_SYMBOL = 8                            # lane-ops of one rANS decode step
+OPS_PER_SYMBOL = 8                            # least lane-ops of one rANS decode step: slot mask, x >> p, one
+                                              # 24-bit multiply-add, renorm compare, shift-in, select, pointer
+                                              # advance, one field extraction
 METRIC = "decode-attn compressed-KV GB/s (% HBM peak) and tokens/s at B=128, 8K ctx"
 
 
@@ -433,8 +435,8 @@ def main() -> int:
         print(json.dumps(record_traffic(*args.record_traffic)), flush=True)
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode-attention path has no "
-              f"multi-GPU mode in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode-attention path runs on "
+              f"one GPU and has no multi-GPU mode.", file=sys.stderr)
         return 2
 
     import torch

@@ -15,7 +15,7 @@ Paper anchors (D-Quant, arXiv 2609.19880):
 * section 5.4 / appendix "Drift makes only sparse, local corrections": no
   changed symbol moves by more than one reconstruction level.
 
-Readings (listed in the design doc): one stream is the 128 channels of one
+Readings: one stream is the 128 channels of one
 (token, KV head); the per-token scale is the L2 norm stored as fp16; the
 drift candidates are the one-level inward moves; the Lagrangian solution is
 computed exactly as the minimal prefix of candidates sorted by

@@ -12,7 +12,7 @@ Paper anchors (D-Quant, arXiv 2609.19880):
 * section 4.4 "Distribution sharpening": p'_m proportional to p_m^alpha,
   alpha > 1 (alpha = 1.4, section 5.1).
 
-Readings where the paper is silent (each also listed in the design doc):
+Readings where the paper is silent:
 * grid: symmetric and uniform in unit-RMS units, level m at
   delta * (m - (M-1)/2); that is the paper's affine grid with o = -delta*(M-1)/2
   and s = delta, the per-token scale being the stored norm;

@@ -15,7 +15,7 @@ Paper anchors (D-Quant, arXiv 2609.19880):
 * section 5.5: token-wise min-max affine grids, per-token grouping,
   least-squares refitting and FP16 metadata.
 
-Readings (each also listed in the design doc):
+Readings:
 * the stream is the 8 heads' rotated values in head-major order, each head
   rotated by its own 128-point Hadamard (y = H x, unnormalised);
 * the grid is min-max over the stream: o = min y, s = (max y - min y)/(M-1),
