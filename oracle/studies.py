@@ -8,7 +8,8 @@ the normalisation the paper's preprocessed KV rows are close to this, section
 1. Reconstruction error against the number of levels at fixed key and value
    budgets (the analysis of the paper's Table 2): for each M, the NMSE at the
    grid step that minimises it, with the fraction of drifted symbols, or "-"
-   when no step gives a table every stream fits (R23).
+   when no step gives a feasible table (one where every stream fits once all
+   its symbols sit at the ends of their drift chains, with a byte of slack).
 2. Largest alphabet against the container size (the analysis of Figure 6
    left): the largest M whose grid, at its MSE-optimal uniform step for
    N(0,1), has a mean coded length that fits the container (drift absorbs the
