@@ -545,6 +545,7 @@ def main() -> int:
         "tokens_per_s": round(B / (ms_per_step / 1e3), 1),
         "us_per_layer_call": round(per_call_s * 1e6, 2),
         "us_per_layer_call_p10_p50_p90": [round(float(np.percentile(call_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "symbols_per_s": round(symbols / per_call_s, 1),
         "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
                      "unit": "Tops/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
                      "traffic": recorded_traffic("attn_kernel", w.name),
