@@ -149,6 +149,36 @@ def test_token_encode_later_rounds(gpu_lib):
     assert np.array_equal(ds[:, 1] & 0xFFFF, rv.changed) and np.array_equal(ds[:, 1] >> 16, rv.rounds)
 
 
+def test_token_encode_large_containers(gpu_lib):
+    """The largest containers (1024-byte keys, 900-byte values): fewer streams
+    share a wave so that their rows and emission buffers fit the LDS; bit-exact."""
+    dq = gpu_lib
+    kcfg, vcfg = (8, 1024), (6, 900)
+    tk, tv = oracle.make_token_table(*kcfg), oracle.make_token_table(*vcfg)
+    tabs = dq.dq_token_tables_init(dq.make_params(*kcfg), dq.make_params(*vcfg))
+    n, P = 45, 16
+    k = _tokens(6, synth.T_K, n)
+    v = _tokens(6, synth.T_V, n)
+    slots = np.random.default_rng(6).permutation(48)[:n].astype(np.int32)
+    pages = 3
+    kc = torch.zeros(dq.token_cache_shape(pages, P, kcfg[1]), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros(dq.token_cache_shape(pages, P, vcfg[1]), dtype=torch.uint8, device="cuda")
+    km = torch.zeros((pages, P, 2), dtype=torch.int16, device="cuda")
+    vm = torch.zeros_like(km)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_encode_tokens(tabs, _dev(k), _dev(v), _dev(slots), kc, vc, km, vm, P, err_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    rk = oracle.encode_tokens(k.astype(np.float64), tk)
+    rv = oracle.encode_tokens(v.astype(np.float64), tv)
+    kc = _from_pages(kc.cpu().numpy(), kcfg[1])[:, :kcfg[1]]
+    vc = _from_pages(vc.cpu().numpy(), vcfg[1])[:, :vcfg[1]]
+    km, vm = km.cpu().numpy().view(np.uint16).reshape(-1, 2), vm.cpu().numpy().view(np.uint16).reshape(-1, 2)
+    assert np.array_equal(kc[slots], rk.containers) and np.array_equal(vc[slots], rv.containers)
+    assert np.array_equal(km[slots, 0], rk.o16.view(np.uint16)) and np.array_equal(km[slots, 1], rk.s16.view(np.uint16))
+    assert np.array_equal(vm[slots, 0], rv.o16.view(np.uint16)) and np.array_equal(vm[slots, 1], rv.s16.view(np.uint16))
+
+
 def test_token_decode_symbols(setup):
     """Oracle containers decode to the oracle's symbols; a corrupted container
     sets the decode flag."""
