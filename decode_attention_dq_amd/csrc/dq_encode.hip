@@ -695,6 +695,7 @@ struct TokWave {
 constexpr int kTokWgLds = 39 * 1024;           // dynamic LDS of a work-group: 4 fit on a CU
 __host__ __device__ inline int tok_buf_stride(int max_c) { return (max_c + 3) & ~3; }
 __host__ __device__ inline int tok_stream_bytes(int max_c) { return kTokRow + tok_buf_stride(max_c) + 12; }
+static_assert(kTokWgLds / kWaves >= kTokRow + kTokMaxC + 12, "a wave must hold at least one stream");
 // streams per wave: kTokBatch, fewer when the LDS of kTokBatch would not fit
 __host__ __device__ inline int tok_per_wave(int max_c) {
     const int n = kTokWgLds / kWaves / tok_stream_bytes(max_c);
