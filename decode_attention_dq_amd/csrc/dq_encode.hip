@@ -4,7 +4,7 @@
 // floating-point decision is an IEEE fp64 operation in a fixed order with no
 // contraction (this file is compiled with -ffp-contract=off).
 //
-// Work decomposition: a wave takes up to kPerWave (32) consecutive streams.
+// Work decomposition: a wave takes up to kPerWave (24) consecutive streams.
 //   1. lane = channel, one stream after another (the next stream's inputs are
 //      already in flight): rotation, norm, nearest level, the drift candidates
 //      and their (key, channel) ranks. What stays in LDS per stream is the
@@ -28,7 +28,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kMaxRounds = 64;
 constexpr int kTail = 16;         // candidates staged per stream beyond the minimal prefix
-constexpr int kPerWave = 32;      // most streams a wave takes (lanes of the serial phase)
+constexpr int kPerWave = 24;      // most streams a wave takes (lanes of the serial phase)
 constexpr int kRow = 132;         // LDS bytes per stream symbol row (an odd number of dwords)
 
 // fp64 -> fp16 bits with a single rounding to nearest even; overflow gives inf.
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(64 * kWaves) void mean_kernel(EncArgs a) {
     if (lane == 0) a.k_mean_scale[row] = s16;
 }
 
-__global__ __launch_bounds__(64 * kWaves, 5) void encode_kernel(EncArgs a, int per_wave) {
+__global__ __launch_bounds__(64 * kWaves, 6) void encode_kernel(EncArgs a, int per_wave) {
     __shared__ WaveLds wl_all[kWaves];
     __shared__ SymConst sconst[2][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1178,11 +1178,12 @@ __global__ void token_decode_symbols_kernel(const EncTable* __restrict__ T, cons
 }  // namespace
 
 // Streams per wave: kPerWave (one per lane in the serial phase) for large
-// writes; fewer when that would leave the chip short of waves (about 5120 fit
-// at once: 256 CUs x 20), since a wave walks its streams one at a time first.
+// writes; fewer when that would leave the chip short of waves (about 6144 fit
+// at once: 256 CUs x 24), since a wave walks its streams one at a time first.
 // Waves stalled on fp64 divide chains and cross-lane moves are hidden by
-// occupancy: 32 streams per wave keep the LDS at 28 KB per work-group, and
-// the launch bound holds the registers to 96, so 5 waves share a SIMD.
+// occupancy: 24 streams per wave keep the LDS at 24 KB per work-group and the
+// launch bound holds the registers to 80 (a few spill), so 6 waves share a
+// SIMD (Llama-shaped write: 4.07 ms at 32 streams and 5 waves, 3.98 ms here).
 hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
     if (a.k_mean) {
         const long waves = (long)(a.num_tokens / kMeanBlock) * a.num_kv_heads;
@@ -1191,7 +1192,7 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     const long streams = 2l * a.num_tokens * a.num_kv_heads;
-    const long waves_wanted = 5120;
+    const long waves_wanted = 6144;
     const int per_wave = (int)std::min((long)kPerWave, std::max(1l, (streams + waves_wanted - 1) / waves_wanted));
     const long per_block = (long)per_wave * kWaves;
     dim3 grid((unsigned)((streams + per_block - 1) / per_block));
