@@ -370,6 +370,46 @@ def attn_source_hash() -> str:
     return h.hexdigest()
 
 
+def recorded_issue(kernel: str, workload: str):
+    """The decode kernel's measured VALU-issue and LDS-active fractions of its
+    busy CU cycles (SQ counters of one rocprofv3 pass), or None when the kernel
+    sources changed since those counters were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_JSON))[kernel]
+        sq = rec["sq"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if sq.get("source_sha256") != attn_source_hash() or sq.get("workload") != workload:
+        return None
+    return {"valu_issue_frac": sq["valu_issue_frac"], "lds_active_frac": sq["lds_active_frac"]}
+
+
+def record_issue(sq_csv: str, workload: str = "decode_qwen3_8b", cus: int = 256, simds: int = 1024) -> dict:
+    """Host only: from a rocprofv3 --pmc CSV holding SQ_INSTS_VALU,
+    SQ_BUSY_CU_CYCLES and SQ_LDS_IDX_ACTIVE for the headline kernel, the VALU
+    issue cycles per SIMD (4 per wave instruction) and the LDS-active cycles as
+    fractions of the busy cycles per CU, written to profiles/traffic.json with
+    the hash of the current kernel sources."""
+    import csv
+    sums = {}
+    for r in csv.DictReader(open(sq_csv)):
+        if "attn_kernel<false, false, false>" in r["Kernel_Name"]:
+            sums.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            sums[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    mean = {c: sum(v.values()) / len(v) for c, v in sums.items()}
+    busy_per_cu = mean["SQ_BUSY_CU_CYCLES"] / cus
+    sq = {"workload": workload, "source_sha256": attn_source_hash(),
+          "valu_issue_frac": round(mean["SQ_INSTS_VALU"] * 4 / simds / busy_per_cu, 4),
+          "lds_active_frac": round(mean["SQ_LDS_IDX_ACTIVE"] / mean["SQ_BUSY_CU_CYCLES"], 4),
+          "dispatches": len(sums["SQ_INSTS_VALU"])}
+    allrec = json.load(open(TRAFFIC_JSON))
+    allrec["attn_kernel"]["sq"] = sq
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(allrec, f, indent=1)
+        f.write("\n")
+    return sq
+
+
 def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None when
     the kernel sources changed since those counters were taken."""
@@ -428,11 +468,16 @@ def main() -> int:
                     help="profiling only: run just this measurement and print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (reference for HBM byte counters)")
+    ap.add_argument("--record-issue", metavar="SQ_CSV", default=None,
+                    help="host only: write the VALU-issue and LDS-active fractions to profiles/traffic.json")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: write profiles/traffic.json from two rocprofv3 --pmc counter CSVs")
     args = ap.parse_args()
     if args.record_traffic:
         print(json.dumps(record_traffic(*args.record_traffic)), flush=True)
+        return 0
+    if args.record_issue:
+        print(json.dumps(record_issue(args.record_issue)), flush=True)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode-attention path runs on "
@@ -549,6 +594,7 @@ def main() -> int:
         "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
                      "unit": "Tops/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
                      "traffic": recorded_traffic("attn_kernel", w.name),
+                     "measured_issue": recorded_issue("attn_kernel", w.name),
                      "algorithmic_bytes_per_call": nbytes, "symbols_per_call": symbols,
                      "hbm_GBps": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)},
         "cpu_baseline": None,

@@ -55,6 +55,20 @@ def test_traffic_record_follows_sources(monkeypatch):
     assert bench.recorded_traffic("attn_kernel", "decode_qwen3_8b") is None
 
 
+def test_issue_record_follows_sources(monkeypatch):
+    """The measured VALU-issue and LDS-active fractions are reported only while
+    their record carries the current sources' hash."""
+    sq = json.load(open(bench.TRAFFIC_JSON))["attn_kernel"].get("sq")
+    got = bench.recorded_issue("attn_kernel", "decode_qwen3_8b")
+    if sq is not None and sq["source_sha256"] == bench.attn_source_hash():
+        assert got == {"valu_issue_frac": sq["valu_issue_frac"], "lds_active_frac": sq["lds_active_frac"]}
+        assert 0.0 < got["valu_issue_frac"] <= 1.0 and 0.0 < got["lds_active_frac"] <= 1.0
+    else:
+        assert got is None
+    monkeypatch.setattr(bench, "attn_source_hash", lambda: "0" * 64)
+    assert bench.recorded_issue("attn_kernel", "decode_qwen3_8b") is None
+
+
 def test_record_traffic_scales_by_copy(tmp_path, monkeypatch):
     """Traffic = FETCH_SIZE and WRITE_SIZE (KiB, mean over the headline
     kernel's dispatches) times the copy calibration's bytes-per-KiB factors."""
