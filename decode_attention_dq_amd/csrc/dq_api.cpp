@@ -130,11 +130,15 @@ int describe(const dq_table_params* in, dq_table_info* t, bool token = false) {
     for (int m = 0; m < M; ++m) w[m] = pow(t->mass[m], alpha);
     for (int m = 0; m < M; ++m) s += w[m];
 
+    // Rounding and the floor keep the model's order: going inward, a level
+    // whose cell is strictly more probable than its outer neighbour's gets at
+    // least one more unit, so its cost is strictly lower.
     int64_t sum = 0;
     for (int m = 0; m < M / 2; ++m) {
         double r = nearbyint((w[m] / s) * (double)total);   // round half to even
         int64_t f = (int64_t)r;
         if (f < (int64_t)f_min) f = f_min;
+        if (m > 0 && t->mass[m] > t->mass[m - 1] && f <= (int64_t)t->freq[m - 1]) f = (int64_t)t->freq[m - 1] + 1;
         t->freq[m] = (uint32_t)f;
         t->freq[M - 1 - m] = (uint32_t)f;
         sum += 2 * f;
@@ -161,8 +165,10 @@ int describe(const dq_table_params* in, dq_table_info* t, bool token = false) {
         t->cost[m] = (int64_t)nearbyint(((double)p - log2((double)t->freq[m])) * (double)(1 << dq::kCostFracBits));
     }
     // drift target: the nearest level toward zero with a strictly lower cost
-    // (expensive symbols drift to nearby cheaper ones, section 4.3); the walk
-    // ends after the first level at or across zero
+    // (expensive symbols drift to nearby cheaper ones, section 4.3); with the
+    // model's order kept above this is the adjacent inner level wherever the
+    // cells get less probable outward; the walk ends after the first level at
+    // or across zero
     for (int m = 0; m < M; ++m) {
         t->inner[m] = -1;
         const int d = t->recon[m] > 0 ? -1 : (t->recon[m] < 0 ? 1 : 0);
@@ -265,11 +271,6 @@ int token_choose_splits(int batch, int max_context) {
     return (int)s;
 }
 
-int token_cap(int max_pages_per_seq, int page_size, int splits, int split_len) {
-    long cap = std::min((long)max_pages_per_seq * page_size, (long)splits * split_len);
-    return (int)std::min(cap, (long)INT32_MAX);
-}
-
 int split_tokens(int max_context, int splits) {
     const int tile = 256;
     int per = (max_context + splits - 1) / splits;
@@ -314,6 +315,7 @@ static int tables_init(dq_tables** out, const dq_table_params* keys, const dq_ta
     fill_entries(t->info[0], host);
     fill_entries(t->info[1], host + dq::kTableSlots);
     hipError_t e = hipGetDevice(&t->device);
+    if (e == hipSuccess) e = dq::prepare_attention_kernels();
     if (e != hipSuccess) { delete t; return hip_fail(e); }
     const size_t ent_bytes = sizeof(uint32_t) * 2 * dq::kTableSlots;
     const size_t total = ent_bytes + sizeof(dq::EncTable) * 2;
@@ -463,7 +465,7 @@ static int decode_attention_impl(const dq_tables* t, const void* q, int q_dtype,
     a.num_splits = splits;
     a.split_len = dq::split_tokens(max_context, splits);
     a.slot_count = splits + 1;
-    a.token_cap = dq::token_cap(max_pages_per_seq, page_size, splits, a.split_len);
+    a.token_cap = max_context;   // within the pages and the splits (checked above / by construction)
     a.win_k = window_k;
     a.win_v = window_v;
     a.win_lens = window_lens;
@@ -531,7 +533,7 @@ int dq_bf16_decode_attention(const uint16_t* q, const uint16_t* k_cache, const u
     a.num_splits = splits;
     a.split_len = dq::split_tokens(max_context, splits);
     a.slot_count = splits + 1;
-    a.token_cap = dq::token_cap(max_pages_per_seq, page_size, splits, a.split_len);
+    a.token_cap = max_context;   // within the pages and the splits (checked above / by construction)
     a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
     a.partials = (float*)workspace;
     a.out = out;
@@ -641,7 +643,7 @@ int dq_token_decode_attention_ext(const dq_tables* t, const void* q, int q_dtype
     a.num_splits = splits;
     a.split_len = dq::split_tokens(max_context, splits);
     a.slot_count = splits + 1;
-    a.token_cap = dq::token_cap(max_pages_per_seq, page_size, splits, a.split_len);
+    a.token_cap = max_context;   // within the pages and the splits (checked above / by construction)
     a.ck = t->info[0].container;
     a.cv = t->info[1].container;
     a.pk = t->info[0].prob_bits;

@@ -543,7 +543,24 @@ __global__ __launch_bounds__(kThreads) void decode_symbols_kernel(const uint32_t
         atomicOr(err, DQ_DEVERR_DECODE);
 }
 
+typedef void (*AttnKernel)(AttnLaunch);
+const AttnKernel kAttnKernels[8] = {
+    attn_kernel<false, false, false>, attn_kernel<false, true, false>, attn_kernel<true, false, false>,
+    attn_kernel<true, true, false>,   attn_kernel<false, false, true>, attn_kernel<false, true, true>,
+    attn_kernel<true, false, true>,   attn_kernel<true, true, true>};
+
 }  // namespace
+
+// Large containers need more than the default 64 KB of dynamic LDS. Set once
+// per device when its tables are created (a set-up call), so that the launch
+// path writes no shared state.
+hipError_t prepare_attention_kernels() {
+    for (const AttnKernel fn : kAttnKernels) {
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     AttnLaunch L;
@@ -555,19 +572,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     L.magic_v = ((1u << 21) + (uint32_t)a.cv - 1u) / (uint32_t)a.cv;
     const bool pk = lds_stride(a.ck) != (uint32_t)a.ck, pv = lds_stride(a.cv) != (uint32_t)a.cv;
     const bool mk = a.k_mean != nullptr;
-    typedef void (*Kernel)(AttnLaunch);
-    static const Kernel kernels[8] = {
-        attn_kernel<false, false, false>, attn_kernel<false, true, false>, attn_kernel<true, false, false>,
-        attn_kernel<true, true, false>,   attn_kernel<false, false, true>, attn_kernel<false, true, true>,
-        attn_kernel<true, false, true>,   attn_kernel<true, true, true>};
     const int which = (mk ? 4 : 0) + (pk ? 2 : 0) + (pv ? 1 : 0);
-    const Kernel fn = kernels[which];
-    static bool attr_set[8] = {false, false, false, false, false, false, false, false};
-    if (!attr_set[which]) {
-        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set[which] = true;
-    }
+    const AttnKernel fn = kAttnKernels[which];
     if (a.win_k) {
         hipError_t e = launch_window(a, a.num_splits, s);
         if (e != hipSuccess) return e;
@@ -577,7 +583,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     MergeArgs m = {a.partials, a.slot_count, a.context_lens, a.token_cap, a.split_len, a.num_q_heads,
-                   a.win_k ? a.num_splits : -1, a.out};
+                   a.win_k ? a.num_splits : -1, a.out, a.err_word};
     return launch_merge(m, a.batch * a.num_q_heads, true, s);
 }
 

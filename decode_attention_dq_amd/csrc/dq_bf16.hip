@@ -200,7 +200,8 @@ hipError_t launch_bf16_attention(const Bf16Args& a, hipStream_t s) {
     hipLaunchKernelGGL(bf16_attn_kernel, grid, dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    MergeArgs m = {a.partials, a.slot_count, a.context_lens, a.token_cap, a.split_len, a.num_q_heads, -1, a.out};
+    MergeArgs m = {a.partials, a.slot_count, a.context_lens, a.token_cap, a.split_len, a.num_q_heads, -1, a.out,
+                   nullptr};
     return launch_merge(m, a.batch * a.num_q_heads, false, s);
 }
 

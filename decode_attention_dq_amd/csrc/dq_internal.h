@@ -77,7 +77,7 @@ struct AttnArgs {
     int batch, num_q_heads, num_kv_heads, group, max_pages_per_seq, page_size;
     int num_splits, split_len;          // tokens per split (multiple of the work-group tile)
     int slot_count;                     // partial slots per (sequence, query head): splits + 1
-    int token_cap;                      // tokens a sequence can cover: min(pages * page_size, splits * split_len)
+    int token_cap;                      // tokens a sequence covers at most: max_context
     const uint16_t* win_k;              // optional bf16 window [batch][Hkv][win_cap][128]
     const uint16_t* win_v;
     const int32_t* win_lens;            // [batch]
@@ -115,6 +115,7 @@ constexpr int kWindowMax = 256;          // largest bf16 window
 // Launchers (defined next to their kernels).
 hipError_t launch_encode(const EncArgs& a, hipStream_t s);   // runs the mean pass first when a.k_mean
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t prepare_attention_kernels();   // per device, from dq_tables_init
 hipError_t launch_bf16_attention(const Bf16Args& a, hipStream_t s);
 // Partial of the bf16 window, written to partial slot `slot`.
 hipError_t launch_window(const AttnArgs& a, int slot, hipStream_t s);
@@ -124,10 +125,11 @@ struct MergeArgs {
     const float* partials;              // [batch][Hq][slot_count][kPartStride]
     int slot_count;
     const int32_t* context_lens;
-    int cap;                            // tokens a sequence can cover (see covered_tokens)
+    int cap;                            // tokens a sequence covers at most (max_context)
     int split_len, num_q_heads;
     int window_slot;                    // slot of the bf16 window partial, or -1
     float* out;
+    uint32_t* err_word;                 // optional: DQ_DEVERR_CONTEXT for a length outside [0, cap]
 };
 // `rotated`: the partials are in the rotated domain (inverse rotation applied).
 hipError_t launch_merge(const MergeArgs& a, int rows, bool rotated, hipStream_t s);

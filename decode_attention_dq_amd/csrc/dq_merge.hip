@@ -22,7 +22,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
     __shared__ float red[kMergeWaves][132];
     const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* p = a.partials + (size_t)bh * a.slot_count * kPartStride;
-    const int T = covered_tokens(a.context_lens[bh / a.num_q_heads], a.cap);
+    const int len = a.context_lens[bh / a.num_q_heads];
+    const int T = covered_tokens(len, a.cap);
+    if (tid == 0 && a.err_word && (len < 0 || len > a.cap)) atomicOr(a.err_word, DQ_DEVERR_CONTEXT);
     const int n = (T + a.split_len - 1) / a.split_len;
     const int slots = n + (a.window_slot >= 0 ? 1 : 0);
     auto slot = [&](int i) { return i < n ? i : a.window_slot; };

@@ -22,8 +22,9 @@ namespace dq {
 
 constexpr int kJobTile = 256;
 
-// Tokens of sequence b that the call covers: the length clamped to the paged
-// capacity and to the tokens the splits cover.
+// Tokens of sequence b that the call covers: its length clamped to
+// [0, max_context] (max_context fits the pages and the splits; the merge
+// flags a length outside that range).
 __host__ __device__ inline int covered_tokens(int len, int cap) { return len < 0 ? 0 : (len < cap ? len : cap); }
 
 // Inclusive prefix sum over the wave (every lane active).

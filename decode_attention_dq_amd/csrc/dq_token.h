@@ -63,7 +63,6 @@ hipError_t launch_token_decode_symbols(const EncTable* table, const uint8_t* con
                                        uint32_t* err, hipStream_t s);
 
 // Split rule shared by dq_token_workspace_size and the attention call.
-int token_cap(int max_pages_per_seq, int page_size, int splits, int split_len);
 int token_choose_splits(int batch, int max_context);
 
 }  // namespace dq

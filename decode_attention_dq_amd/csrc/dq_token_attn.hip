@@ -480,7 +480,7 @@ hipError_t launch_token_attention(const TokAttnArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     MergeArgs m = {a.partials, a.slot_count, a.context_lens, a.token_cap, a.split_len, a.num_q_heads,
-                   a.win_k ? a.num_splits : -1, a.out};
+                   a.win_k ? a.num_splits : -1, a.out, a.err_word};
     return launch_merge(m, a.batch * a.num_q_heads, true, s);
 }
 

@@ -23,7 +23,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 DQ_OK, DQ_ERR_INVALID_ARG, DQ_ERR_UNSUPPORTED, DQ_ERR_INFEASIBLE, DQ_ERR_WORKSPACE, DQ_ERR_HIP = range(6)
 DQ_DTYPE_F32, DQ_DTYPE_BF16 = 0, 1
 DQ_KEYS, DQ_VALUES = 0, 1
-DQ_DEVERR_DECODE, DQ_DEVERR_ENCODE, DQ_DEVERR_MEAN_SLOT = 1, 2, 4
+DQ_DEVERR_DECODE, DQ_DEVERR_ENCODE, DQ_DEVERR_MEAN_SLOT, DQ_DEVERR_CONTEXT = 1, 2, 4, 8
 HEAD_DIM = 128
 
 

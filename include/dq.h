@@ -12,8 +12,13 @@
  * table derived from the standard normal and sharpened by p' ~ p^alpha
  * (section 3.1 Enc/Dec equations; section 4.4 "Distribution sharpening"), and
  * drift: the length-constrained assignment of section 4.3 that moves a few
- * expensive symbols to an adjacent cheaper level until sum r(m_i) <= 8C - sigma
- * (section 4.2 container equation). Decoding feeds the decoded levels straight
+ * expensive symbols inward, each to the nearest strictly cheaper level toward
+ * zero, until sum r(m_i) <= 8C - sigma (section 4.2 container equation). The
+ * frequency quantisation keeps the strict outward order of the N(0,1) cell
+ * masses, so for every table whose cells get less probable outward (all the
+ * defaults) that target is the adjacent level and no symbol moves by more
+ * than one level. Decoding feeds
+ * the decoded levels straight
  * into the attention contraction with the affine map folded in (section 4.5
  * "Decoding").
  *
@@ -39,6 +44,9 @@
  *     dq_tables_destroy);
  *   - calls are asynchronous on the HIP stream passed as `stream` (a
  *     hipStream_t; NULL means the default stream) and never synchronise;
+ *     calls on different streams may be made from several host threads at
+ *     once (the launch path keeps no mutable shared state; dq_tables_init,
+ *     a set-up call, prepares the kernels of its device);
  *   - return value 0 (DQ_OK) or one of the DQ_ERR_* codes below; no C++
  *     exception crosses this interface; dq_strerror() names a code and
  *     dq_last_hip_error() gives the text of the last HIP failure seen by the
@@ -75,6 +83,8 @@ enum { DQ_KEYS = 0, DQ_VALUES = 1 };
 #define DQ_DEVERR_DECODE 1u   /* a decoded stream did not return to state 2^16 or overran C */
 #define DQ_DEVERR_ENCODE 2u   /* a stream could not be made to fit its container */
 #define DQ_DEVERR_MEAN_SLOT 4u /* a key block's first slot is not where a 128-token block starts */
+#define DQ_DEVERR_CONTEXT 8u   /* a context length is negative or above max_context: the sequence is
+                                  attended over its length clamped to [0, max_context] */
 
 /*
  * Parameters of one static entropy table (keys and values each have one).
@@ -118,9 +128,12 @@ typedef struct dq_tables dq_tables;   /* opaque */
  * Derive one table on the host (no device work): N(0,1) cell masses of the
  * nearest-level cells (section 1, section 3.2: the model comes straight from
  * the standard normal), sharpening (section 4.4), integer frequencies (round
- * half even, floor 2^(p-8), mirrored, residual to the central level(s)), costs
- * and the feasibility check (the all-central stream must fit with one byte of
- * slack). Returns DQ_ERR_UNSUPPORTED / DQ_ERR_INFEASIBLE as dq_tables_init.
+ * half even, floor 2^(p-8), one unit more than the outer neighbour where the
+ * model makes a level strictly more probable, mirrored, residual to the
+ * central level(s)), costs, drift targets, and the feasibility check: a
+ * stream whose symbols all sit at the ends of their drift chains (the
+ * central levels, for the default tables) must fit with one byte of slack.
+ * Returns DQ_ERR_UNSUPPORTED / DQ_ERR_INFEASIBLE as dq_tables_init.
  */
 int dq_table_describe(const dq_table_params* params, dq_table_info* out);
 
@@ -201,7 +214,9 @@ size_t dq_workspace_size(int batch, int num_q_heads, int num_kv_heads, int max_c
  *   q             [batch][num_q_heads][128], DQ_DTYPE_F32 or DQ_DTYPE_BF16
  *   block_table   int32 [batch][max_pages_per_seq]: physical page of each
  *                 logical page; entries past the context are not read
- *   context_lens  int32 [batch], 0 <= len <= max_context (0 gives zeros)
+ *   context_lens  int32 [batch], 0 <= len <= max_context (0 gives zeros); a
+ *                 length outside that range is clamped to it and sets
+ *                 DQ_DEVERR_CONTEXT in *err_word
  *   max_context   host-side upper bound of context_lens (sizes the split)
  *   softmax_scale <= 0 selects 1/sqrt(128)
  *   num_splits    0 = chosen by the library; otherwise the number of token
@@ -407,7 +422,9 @@ size_t dq_token_workspace_size(int batch, int num_q_heads, int max_context, int 
  *                 4-byte aligned
  *   block_table   int32 [batch][max_pages_per_seq]; page_size a power of two
  *                 of at most 65536 (else DQ_ERR_UNSUPPORTED)
- *   context_lens  int32 [batch], 0 <= len <= max_context (0 gives zeros)
+ *   context_lens  int32 [batch], 0 <= len <= max_context (0 gives zeros); a
+ *                 length outside that range is clamped to it and sets
+ *                 DQ_DEVERR_CONTEXT in *err_word
  *   workspace     dq_token_workspace_size bytes, 16-byte aligned
  *   err_word      optional; DQ_DEVERR_DECODE when a stream does not end in
  *                 the initial state or reads past its container

@@ -6,7 +6,7 @@ values (``default_rng(0)``), alpha = 1.4, p = 10; the minimiser is printed as
 the entry to freeze in ``oracle/tables.py`` (DEFAULT_STEP) and in the C
 header's documented defaults.
 
-    python -m oracle.sweep_step [--lo 0.70 --hi 1.40]
+    python -m oracle.sweep_step [--lo 0.70 --hi 1.40] [--pairs 8:37,6:37]
 """
 from __future__ import annotations
 
@@ -32,11 +32,14 @@ def main() -> None:
     ap.add_argument("--lo", type=float, default=0.70)
     ap.add_argument("--hi", type=float, default=1.40)
     ap.add_argument("--rows", type=int, default=20000)
+    ap.add_argument("--pairs", default="8:37,6:37,8:32,6:32,8:41,6:27",
+                    help="comma-separated levels:container pairs to sweep")
     args = ap.parse_args()
     x = np.random.default_rng(0).standard_normal((args.rows, 128))
     steps = np.round(np.arange(args.lo, args.hi + 1e-9, 0.01), 2)
     best = {}
-    for M, C in [(8, 37), (6, 37), (8, 32), (6, 32), (8, 41), (6, 27)]:
+    pairs = [tuple(int(v) for v in pc.split(":")) for pc in args.pairs.split(",")]
+    for M, C in pairs:
         res = [(s, *score(M, C, float(s), x)) for s in steps]
         s_best, e_best, d_best = min(res, key=lambda r: r[1])
         best[(M, C)] = float(s_best)

@@ -19,7 +19,9 @@ Readings where the paper is silent:
 * p_m is the N(0,1) mass of level m's nearest-neighbour cell (boundaries
   halfway between adjacent levels);
 * frequencies: round-half-even of q_m * 2^p for the lower half, floored at
-  f_min = 2^(p-8), mirrored, the (even) residual split equally over the two
+  f_min = 2^(p-8), raised where needed so that a cell the model makes
+  strictly more probable than its outer neighbour keeps a strictly larger
+  frequency, mirrored, the (even) residual split equally over the two
   central levels (or given to the single central level when M is odd);
 * costs are fixed point with 16 fractional bits, cost(m) = rint((p - log2 f_m) * 2^16);
 * the rANS state lives in [2^16, 2^24) with byte renormalisation, flushed as
@@ -126,10 +128,14 @@ def make_table(levels: int, container: int, step: float | None = None, alpha: fl
         s += v
     sharpened = np.array([v / s for v in w])
 
-    # integer frequencies at precision 2^p
+    # integer frequencies at precision 2^p. Rounding and the floor must not
+    # erase the model's order: going inward, a level whose cell is strictly
+    # more probable than its outer neighbour's keeps at least one more unit.
     freq = np.zeros(M, dtype=np.int64)
     for m in range(M // 2):
         f = max(f_min, int(round(sharpened[m] * total)))   # round() is half-even
+        if m > 0 and mass[m] > mass[m - 1]:
+            f = max(f, int(freq[m - 1]) + 1)
         freq[m] = f
         freq[M - 1 - m] = f
     notes = []
@@ -153,10 +159,11 @@ def make_table(levels: int, container: int, step: float | None = None, alpha: fl
         sym[cum[m]:cum[m + 1]] = m
 
     # drift target: the nearest level toward zero whose cost is strictly lower
-    # (section 4.3: expensive symbols drift to nearby cheaper ones). Where the
-    # costs grow outward this is the adjacent inner level; a tie (tail levels
-    # both at f_min) is skipped over. The walk stops after the first level at
-    # or across zero; -1 means the level never drifts.
+    # (section 4.3: expensive symbols drift to nearby cheaper ones). The
+    # frequencies keep the model's strict order, so wherever the N(0,1) cells
+    # get less probable outward (every configured table) this is the adjacent
+    # inner level. The walk stops after the first level at or across zero; -1
+    # means the level never drifts.
     inner = np.full(M, -1, dtype=np.int64)
     for m in range(M):
         d = -1 if recon[m] > 0 else (1 if recon[m] < 0 else 0)

@@ -2,8 +2,10 @@
 reconstructions of the same seeded K/V: max relative error per (sequence,
 query head) row <= 2e-3. Cases: the tiny check, GQA with ragged lengths and
 shuffled 16-token pages, split-count invariance, an empty context, extreme
-value norms, and sampled rows of the full Qwen3-8B-layer and 128K
-long-context workloads in the benchmark's launch configuration."""
+value norms, context lengths outside the range, and sampled units of every
+full-size workload (the Qwen3-8B layer, 4 x 64K and 1 x 128K contexts at two
+split counts each, every sequence of the ragged 1.96-bit batch, the
+bf16-window layer) in the benchmark's launch configuration."""
 import numpy as np
 import pytest
 import torch
@@ -186,62 +188,103 @@ def test_corrupt_container_sets_error(gpu_lib):
     assert err & dq.DQ_DEVERR_DECODE
 
 
-def _full_size_sampled(dq, w, samples):
+def _oracle_unit(tk, tv, k, v, T, kdev, vdev, q_rows):
+    """Oracle side of one (sequence, KV head) unit of a full-size layer:
+    containers compared with the device's, and the fp64 attention rows of its
+    query heads. k, v: [T + W][1][128] host rows; the last W enter attention as
+    their bf16 values (the window)."""
+    kc_, vc_, kn_, vn_, kh, vh = sequence_case(tk, tv, k[:T], v[:T])
+    W = k.shape[0] - T
+    if W:
+        kh = np.concatenate([kh, synth.round_to_bf16(k[T:]).transpose(1, 0, 2).astype(np.float64)], axis=1)
+        vh = np.concatenate([vh, synth.round_to_bf16(v[T:]).transpose(1, 0, 2).astype(np.float64)], axis=1)
+    same = np.array_equal(kdev, kc_[:, 0]) and np.array_equal(vdev, vc_[:, 0])
+    return same, oracle.attention(q_rows, [kh], [vh])[0]
+
+
+def _full_size_sampled(dq, w, samples, splits=(0,)):
+    """The full layer in the benchmark's launch configuration (and at each
+    extra split count), checked on sampled (sequence, KV head) units: their
+    containers byte for byte, and the attention rows of their query heads
+    within TOL of the oracle's fp64 attention. The oracle side of the units
+    runs in a thread pool (NumPy releases the GIL in its array operations)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
     tk, tv = oracle.make_table(w.k_levels, w.container), oracle.make_table(w.v_levels, w.cv)
     tabs = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.cv))
     cache = workloads.build_cache(dq, tabs, w)
     q = workloads.query_rows(w)
     B, hq, hkv = w.batch, w.num_q_heads, w.num_kv_heads
-    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
-    ws = torch.empty(dq.dq_workspace_size(B, hq, hkv, w.context), dtype=torch.uint8, device="cuda")
-    err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    if w.window:
-        dq.dq_decode_attention_window(tabs, q, cache.k_cache, cache.v_cache, cache.k_norm, cache.v_norm,
-                                      cache.block_table, cache.context_lens, cache.win_k, cache.win_v,
-                                      cache.win_lens, hkv, w.page_size, w.context, out, ws, err_word=err)
-    else:
-        dq.dq_decode_attention(tabs, q, cache.k_cache, cache.v_cache, cache.k_norm, cache.v_norm, cache.block_table,
-                               cache.context_lens, hkv, w.page_size, w.context, out, ws, err_word=err)
-    torch.cuda.synchronize()
-    assert int(err.item()) == 0
-    out = out.cpu().numpy()
+    outs = {}
+    for ns in splits:
+        out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.full((dq.dq_workspace_size(B, hq, hkv, w.context, ns),), 0xFF, dtype=torch.uint8,
+                        device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if w.window:
+            dq.dq_decode_attention_window(tabs, q, cache.k_cache, cache.v_cache, cache.k_norm, cache.v_norm,
+                                          cache.block_table, cache.context_lens, cache.win_k, cache.win_v,
+                                          cache.win_lens, hkv, w.page_size, w.context, out, ws, num_splits=ns,
+                                          err_word=err)
+        else:
+            dq.dq_decode_attention(tabs, q, cache.k_cache, cache.v_cache, cache.k_norm, cache.v_norm,
+                                   cache.block_table, cache.context_lens, hkv, w.page_size, w.context, out, ws,
+                                   num_splits=ns, err_word=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0, ns
+        outs[ns] = out.cpu().numpy()
     qh = q.float().cpu().numpy()
     bt = cache.block_table.cpu().numpy()
     G = hq // hkv
+    tasks = []
     for b, g in samples:
         T = int(cache.lens[b])
         W = int(cache.win_lens[b]) if w.window else 0
         k = workloads.kv_rows(w, 0, synth.T_K, b, T + W)[:, g:g + 1].float().cpu().numpy()
         v = workloads.kv_rows(w, 0, synth.T_V, b, T + W)[:, g:g + 1].float().cpu().numpy()
-        kc_, vc_, kn_, vn_, kh, vh = sequence_case(tk, tv, k[:T], v[:T])
-        if W:   # the window rows enter attention as their bf16 values
-            kh = np.concatenate([kh, synth.round_to_bf16(k[T:]).transpose(1, 0, 2).astype(np.float64)], axis=1)
-            vh = np.concatenate([vh, synth.round_to_bf16(v[T:]).transpose(1, 0, 2).astype(np.float64)], axis=1)
         slots = workloads.slot_mapping(bt[b:b + 1], cache.lens[b:b + 1], w.page_size)
         pg = torch.as_tensor(slots // w.page_size, device="cuda", dtype=torch.long)
         off = torch.as_tensor(slots % w.page_size, device="cuda", dtype=torch.long)
-        assert np.array_equal(cache.k_cache[pg, g, off].cpu().numpy(), kc_[:, 0])
-        assert np.array_equal(cache.v_cache[pg, g, off].cpu().numpy(), vc_[:, 0])
-        ref = oracle.attention(qh[b:b + 1, g * G:(g + 1) * G], [kh], [vh])[0]
-        e = row_rel_err(out[b, g * G:(g + 1) * G], ref)
-        assert e.max() <= TOL, (b, g, e)
+        tasks.append((tk, tv, k, v, T, cache.k_cache[pg, g, off].cpu().numpy(),
+                      cache.v_cache[pg, g, off].cpu().numpy(), qh[b:b + 1, g * G:(g + 1) * G]))
+    del cache
+    with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
+        results = list(ex.map(lambda t: _oracle_unit(*t), tasks))
+    for (b, g), (same, ref) in zip(samples, results):
+        assert same, ("containers differ", b, g)
+        for ns, out in outs.items():
+            e = row_rel_err(out[b, g * G:(g + 1) * G], ref)
+            assert e.max() <= TOL, (b, g, ns, e)
 
 
 def test_full_qwen3_layer_sampled(gpu_lib):
+    """Eight (sequence, KV head) units over the batch and every KV head."""
     dq = gpu_lib
-    _full_size_sampled(dq, workloads.WORKLOADS["decode_qwen3_8b"], [(0, 0), (57, 3), (127, 7)])
+    _full_size_sampled(dq, workloads.WORKLOADS["decode_qwen3_8b"],
+                       [(0, 0), (17, 1), (33, 2), (57, 3), (70, 4), (91, 5), (110, 6), (127, 7)])
+
+
+def test_long_context_4x64k_sampled(gpu_lib):
+    """Batch 4 at 65,536 tokens: two units of every sequence, at the library's
+    split count and at a forced 13 (a count that leaves a short last split)."""
+    dq = gpu_lib
+    _full_size_sampled(dq, workloads.WORKLOADS["long_llama_b4"],
+                       [(0, 0), (0, 5), (1, 1), (1, 6), (2, 2), (2, 7), (3, 3), (3, 4)], splits=(0, 13))
 
 
 def test_long_context_128k_sampled(gpu_lib):
+    """One sequence of 131,072 tokens, two KV heads, at the library's split
+    count (128 splits, 129 partials per merge) and at a forced 37."""
     dq = gpu_lib
-    _full_size_sampled(dq, workloads.WORKLOADS["long_llama_b1"], [(0, 5)])
+    _full_size_sampled(dq, workloads.WORKLOADS["long_llama_b1"], [(0, 5), (0, 2)], splits=(0, 37))
 
 
 def test_ragged_low_budget_sampled(gpu_lib):
+    """Every sequence of the ragged 1.96-bit batch, the KV head rotating with
+    the sequence."""
     dq = gpu_lib
     w = workloads.WORKLOADS["ragged_1p96"]
-    lens = workloads.context_lengths(w)
-    _full_size_sampled(dq, w, [(int(np.argmin(lens)), 1), (int(np.argmax(lens)), 6), (31, 2)])
+    _full_size_sampled(dq, w, [(b, b % w.num_kv_heads) for b in range(w.batch)])
 
 
 def test_window_split_budget_layer_sampled(gpu_lib):
@@ -280,3 +323,19 @@ def test_decode_step_with_append(gpu_lib):
     assert np.array_equal(dkc.cpu().numpy(), kc) and np.array_equal(dvc.cpu().numpy(), vc)
     assert np.array_equal(dkn.cpu().numpy().view(np.uint16), kn) and np.array_equal(dvn.cpu().numpy().view(np.uint16), vn)
     assert row_rel_err(out.cpu().numpy(), ref).max() <= TOL
+
+
+def test_context_length_outside_range_is_flagged(gpu_lib):
+    """A length above max_context is attended as max_context, a negative one
+    as 0, and either sets DQ_DEVERR_CONTEXT; lengths inside the range do not."""
+    dq = gpu_lib
+    tk, tv, tabs = _tables(dq)
+    q, kc, vc, kn, vn, bt, ref = _case(tk, tv, [100, 200], 1, 4, 16, True, seed=9, perm_seed=9)
+    out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, [100, 200], 1, 16, 200)
+    assert err == 0 and row_rel_err(out, ref).max() <= TOL
+    out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, [100, 300], 1, 16, 200)
+    assert err == dq.DQ_DEVERR_CONTEXT
+    assert row_rel_err(out, ref).max() <= TOL
+    out, err = _run(dq, tabs, q, kc, vc, kn, vn, bt, [-3, 200], 1, 16, 200)
+    assert err == dq.DQ_DEVERR_CONTEXT
+    assert np.all(out[0] == 0) and row_rel_err(out[1:], ref[1:]).max() <= TOL

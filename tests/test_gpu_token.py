@@ -271,6 +271,23 @@ def test_token_attention_flags_corrupt_stream(setup):
     assert err & dq.DQ_DEVERR_DECODE
 
 
+def test_token_attention_context_length_outside_range_is_flagged(setup):
+    """A length above max_context is attended as max_context and sets
+    DQ_DEVERR_CONTEXT."""
+    lens = [90, 200]
+    dq, tabs, d, ref, P = _attention_case(setup, lens, 2, seed=11, perm_seed=4)
+    d["lens"] = _dev(np.asarray([90, 260], np.int32))
+    B, hq = d["q"].shape[:2]
+    out = torch.full((B, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((dq.dq_token_workspace_size(B, hq, 200, 0),), 0xFF, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dq.dq_token_decode_attention(tabs, d["q"], d["kc"], d["vc"], d["km"], d["vm"], d["bt"], d["lens"], P, 200,
+                                 out, ws, err_word=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == dq.DQ_DEVERR_CONTEXT
+    assert row_rel_err(out.cpu().numpy(), ref).max() <= TOL
+
+
 def test_token_encode_then_attend(setup):
     """The device cache write feeding the device attention: the same output as
     attention over the oracle's containers, within the bar of the oracle."""

@@ -80,10 +80,8 @@ def test_drift_moves_to_the_nearest_cheaper_inner_level(M, C):
     ch = d != 0
     # one drift move per changed symbol, to its drift target
     assert np.array_equal(r.symbols[ch], t.inner[r.nearest[ch]])
-    # where every drift target is the adjacent inner level, no symbol moves by more than one level
-    tgt = t.inner >= 0
-    if np.all(np.abs(t.inner[tgt] - np.arange(M)[tgt]) == 1):
-        assert np.abs(d).max() <= 1
+    # no symbol moves by more than one level (the paper's drift analysis in the appendix)
+    assert np.abs(d).max() <= 1
     # moves go toward zero and to a strictly cheaper level
     assert np.all(np.abs(t.recon[r.symbols[ch]]) < np.abs(t.recon[r.nearest[ch]]))
     assert np.all(t.cost[r.symbols[ch]] < t.cost[r.nearest[ch]])
@@ -93,6 +91,54 @@ def test_drift_moves_to_the_nearest_cheaper_inner_level(M, C):
     untouched = (R0 <= t.budget_fx) & (ln0 <= C)
     assert np.all(r.changed[untouched] == 0)
     assert np.all(r.rounds[untouched] == 0)
+
+
+DEFAULT_TABLES = [(8, 37), (6, 37), (8, 32), (6, 32), (8, 41), (6, 27)]
+
+
+@pytest.mark.parametrize("M,C", DEFAULT_TABLES)
+def test_every_drift_target_is_the_adjacent_inner_level(M, C):
+    """Table property behind the one-level invariant: the quantised
+    frequencies keep the strict outward order of the N(0,1) cell masses, so
+    each non-central level's adjacent inner neighbour is strictly cheaper and
+    is its drift target; the central level(s) never drift."""
+    t = oracle.make_table(M, C)
+    half = M // 2
+    assert np.all(np.diff(t.mass[:half]) > 0)
+    assert np.all(np.diff(t.freq[:half + (M % 2)]) > 0)
+    for m in range(M):
+        if t.recon[m] < 0 and m + 1 < M and t.recon[m + 1] < 0 or (M % 2 and m == half - 1):
+            assert t.inner[m] == m + 1 and t.cost[m + 1] < t.cost[m]
+        elif t.recon[m] > 0 and t.recon[m - 1] > 0 or (M % 2 and m == half + 1):
+            assert t.inner[m] == m - 1 and t.cost[m - 1] < t.cost[m]
+        else:
+            assert t.inner[m] == -1
+
+
+def test_tied_tail_frequencies_are_separated():
+    """At 32 bytes and 8 levels the two outermost key cells both round below
+    the floor 2^(p-8) = 4; the second one, strictly more probable, gets one
+    unit more, so its cost is strictly lower (a tie would send level 0 two
+    levels inward)."""
+    t = oracle.make_table(8, 32)
+    assert t.mass[1] > t.mass[0] and t.sharpened[1] * 1024 < 4 and t.sharpened[0] * 1024 < 4
+    assert t.freq[0] == 4 and t.freq[1] == 5 and t.cost[1] < t.cost[0]
+    assert t.inner.tolist() == [1, 2, 3, -1, -1, 4, 5, 6]
+
+
+@pytest.mark.parametrize("M,C", DEFAULT_TABLES)
+def test_gaussian_drift_never_moves_more_than_one_level(M, C):
+    """Seeded N(0,1) streams on every default table, outermost levels
+    included: every changed symbol moves exactly one level inward."""
+    t = oracle.make_table(M, C)
+    x = np.random.default_rng(1000 + 7 * M + C).standard_normal((20000, 128))
+    r = oracle.encode_streams(x, t)
+    assert not r.fallback.any()
+    d = r.symbols - r.nearest
+    assert np.abs(d).max() <= 1
+    assert np.all(np.abs(t.recon[r.symbols[d != 0]]) < np.abs(t.recon[r.nearest[d != 0]]))
+    if (M, C) == (8, 32):   # the sample reaches the outermost levels, so the pin covers them
+        assert np.count_nonzero((d != 0) & ((r.nearest == 0) | (r.nearest == M - 1))) > 0
 
 
 @pytest.mark.parametrize("M,C", CONFIGS)
