@@ -233,6 +233,8 @@ void fill_entries(const dq_table_info& t, uint32_t* ent) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+static_assert(DQ_NOALLOC_SCRATCH == dq::kScratchBytes, "the header states the scratch size");
+
 }  // namespace
 
 namespace dq {
@@ -316,6 +318,7 @@ static int tables_init(dq_tables** out, const dq_table_params* keys, const dq_ta
     fill_entries(t->info[1], host + dq::kTableSlots);
     hipError_t e = hipGetDevice(&t->device);
     if (e == hipSuccess) e = dq::prepare_attention_kernels();
+    if (e == hipSuccess) e = dq::scratch_device_address(&t->d_scratch);
     if (e != hipSuccess) { delete t; return hip_fail(e); }
     const size_t ent_bytes = sizeof(uint32_t) * 2 * dq::kTableSlots;
     const size_t total = ent_bytes + sizeof(dq::EncTable) * 2;
@@ -497,6 +500,19 @@ int dq_decode_attention(const dq_tables* t, const void* q, int q_dtype, const ui
                                  batch, num_q_heads, num_kv_heads, max_pages_per_seq, page_size, max_context,
                                  softmax_scale, num_splits, nullptr, nullptr, nullptr, 0, nullptr, nullptr, out,
                                  workspace, workspace_bytes, err_word, stream);
+}
+
+int dq_decode_attention_noalloc(const dq_tables* t, const void* q, int q_dtype, const uint8_t* k_cache,
+                                const uint8_t* v_cache, const uint16_t* k_norm, const uint16_t* v_norm,
+                                const int32_t* block_table, const int32_t* context_lens, int batch,
+                                int num_q_heads, int num_kv_heads, int max_pages_per_seq, int page_size,
+                                int max_context, float softmax_scale, int num_splits, float* out,
+                                uint32_t* err_word, void* stream) {
+    if (!t || !t->d_scratch) return DQ_ERR_INVALID_ARG;
+    return decode_attention_impl(t, q, q_dtype, k_cache, v_cache, k_norm, v_norm, block_table, context_lens,
+                                 batch, num_q_heads, num_kv_heads, max_pages_per_seq, page_size, max_context,
+                                 softmax_scale, num_splits, nullptr, nullptr, nullptr, 0, nullptr, nullptr, out,
+                                 t->d_scratch, dq::kScratchBytes, err_word, stream);
 }
 
 int dq_bf16_decode_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,

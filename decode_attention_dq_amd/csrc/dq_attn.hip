@@ -543,6 +543,12 @@ __global__ __launch_bounds__(kThreads) void decode_symbols_kernel(const uint32_t
         atomicOr(err, DQ_DEVERR_DECODE);
 }
 
+// Split partials of dq_decode_attention_noalloc, for callers that cannot
+// allocate. Every device the library runs on holds its own copy until the
+// process ends. In host code `scratch` is only a host-side stand-in for the
+// symbol: its device address comes from scratch_device_address().
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 typedef void (*AttnKernel)(AttnLaunch);
 const AttnKernel kAttnKernels[8] = {
     attn_kernel<false, false, false>, attn_kernel<false, true, false>, attn_kernel<true, false, false>,
@@ -560,6 +566,14 @@ hipError_t prepare_attention_kernels() {
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// Address of the current device's copy of `scratch`; called once per device
+// with that device current (by dq_tables_init), the result kept with the
+// device's tables.
+hipError_t scratch_device_address(void** out) {
+    *out = nullptr;
+    return hipGetSymbolAddress(out, HIP_SYMBOL(scratch));
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {

@@ -116,6 +116,10 @@ constexpr int kWindowMax = 256;          // largest bf16 window
 hipError_t launch_encode(const EncArgs& a, hipStream_t s);   // runs the mean pass first when a.k_mean
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t prepare_attention_kernels();   // per device, from dq_tables_init
+// Fixed device scratch of dq_decode_attention_noalloc: the split partials of
+// one call. Its device address on the current device (see dq_attn.hip).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+hipError_t scratch_device_address(void** out);
 hipError_t launch_bf16_attention(const Bf16Args& a, hipStream_t s);
 // Partial of the bf16 window, written to partial slot `slot`.
 hipError_t launch_window(const AttnArgs& a, int slot, hipStream_t s);
@@ -152,4 +156,5 @@ struct dq_tables {
     dq::EncTable enc[2];
     uint32_t* d_entries;      // [2][kTableSlots] decode tables, then the two EncTables
     dq::EncTable* d_enc;
+    void* d_scratch;          // this device's copy of the fixed attention scratch (not owned)
 };

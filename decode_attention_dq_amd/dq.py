@@ -78,6 +78,8 @@ _sig = {
     "dq_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "dq_decode_attention": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                  ctypes.c_float, _i, _p, _p, ctypes.c_size_t, _p, _p]),
+    "dq_decode_attention_noalloc": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
+                                         ctypes.c_float, _i, _p, _p, _p]),
     "dq_decode_attention_window": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                         ctypes.c_float, _i, _p, _p, _p, _i, _p, _p, ctypes.c_size_t, _p, _p]),
     "dq_decode_attention_ext": (_i, [_p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
@@ -296,6 +298,39 @@ def dq_decode_attention_ext(tables: Tables, q, k_cache, v_cache, k_norm, v_norm,
                                         int(max_context), float(softmax_scale), int(num_splits),
                                         ctypes.byref(ex), _ptr(out), _ptr(workspace), nbytes, _ptr(err_word),
                                         _stream(stream)), "dq_decode_attention_ext")
+
+
+DQ_NOALLOC_SCRATCH = 32 << 20
+
+
+def dq_decode_attention_noalloc(tables: Tables, q, k_cache, v_cache, k_norm, v_norm, block_table, context_lens,
+                                num_kv_heads: int, page_size: int, max_context: int, out, softmax_scale: float = 0.0,
+                                num_splits: int = 0, err_word=None, stream=None) -> None:
+    """dq_decode_attention without a workspace argument: the library's fixed
+    per-device scratch holds the split partials (calls overlapping on one
+    device race)."""
+    import torch
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [B][Hq][128]")
+    qd = {torch.float32: DQ_DTYPE_F32, torch.bfloat16: DQ_DTYPE_BF16}.get(q.dtype)
+    if qd is None:
+        raise ValueError("q dtype must be float32 or bfloat16")
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    _need(q, "q")
+    _need(out, "out", torch.float32, (B, hq, HEAD_DIM))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B][max_pages_per_seq]")
+    _need(context_lens, "context_lens", torch.int32, (B,))
+    _need(k_cache, "k_cache", torch.uint8); _need(v_cache, "v_cache", torch.uint8)
+    _need(k_norm, "k_norm"); _need(v_norm, "v_norm")
+    if err_word is not None:
+        _need(err_word, "err_word")
+    _check(_lib.dq_decode_attention_noalloc(tables.handle, _ptr(q), qd, _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(k_norm), _ptr(v_norm), _ptr(block_table), _ptr(context_lens), B,
+                                            hq, int(num_kv_heads), int(block_table.shape[1]), int(page_size),
+                                            int(max_context), float(softmax_scale), int(num_splits), _ptr(out),
+                                            _ptr(err_word), _stream(stream)), "dq_decode_attention_noalloc")
 
 
 def dq_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_context: int,

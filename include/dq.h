@@ -239,6 +239,29 @@ int dq_decode_attention(const dq_tables* tables, const void* q, int q_dtype,
                         uint32_t* err_word, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * dq_decode_attention, same arguments and results, without the workspace
+ * arguments. The split partials go to a fixed scratch of DQ_NOALLOC_SCRATCH
+ * bytes that the library holds on each device until the process ends (its
+ * address is resolved by dq_tables_init); the call allocates nothing. Returns
+ * DQ_ERR_WORKSPACE when the sizes need more, i.e. when
+ * dq_workspace_size(batch, num_q_heads, num_kv_heads, max_context, num_splits)
+ * exceeds DQ_NOALLOC_SCRATCH. Every call on one device shares that scratch:
+ * calls that overlap in time on one device (different streams, or different
+ * host threads) race and give undefined results; calls ordered on one stream
+ * are safe. No part of the scratch has to start at any particular value.
+ */
+#define DQ_NOALLOC_SCRATCH (32u << 20)
+int dq_decode_attention_noalloc(const dq_tables* tables, const void* q, int q_dtype,
+                                const uint8_t* k_cache, const uint8_t* v_cache,
+                                const uint16_t* k_norm, const uint16_t* v_norm,
+                                const int32_t* block_table, const int32_t* context_lens,
+                                int batch, int num_q_heads, int num_kv_heads, int max_pages_per_seq,
+                                int page_size, int max_context, float softmax_scale, int num_splits,
+                                float* out, uint32_t* err_word, void* stream);
+
+/*
  * Decode attention over the compressed cache plus an uncompressed window of
  * each sequence's most recent tokens (the paper keeps the latest tokens in
  * BF16 and compresses older ones, section 5.1). The two parts are combined by
