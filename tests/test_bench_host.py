@@ -99,3 +99,14 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_units_and_host_info():
+    """The CPU baseline's work units run the oracle on the workloads' shapes and
+    report their own work; the host record names the core count and CPU."""
+    info = bench.host_info()
+    assert info["cpu_count"] == os.cpu_count() and isinstance(info["cpu_model"], str)
+    t, nbytes, streams = bench._cpu_decode_unit((0, 3, 1))
+    assert t > 0 and nbytes == 8192 * 2 * 39 and streams == 2 * 8192
+    t, streams = bench._cpu_encode_unit((0, 0, 5))
+    assert t > 0 and streams == 8192
