@@ -657,7 +657,8 @@ __global__ void selftest_kernel(const double* __restrict__ a, const double* __re
 }
 
 // ---------------------------------------------------------------------------
-// Per-token format (sections 4.5 "Encoding", 5.1, 5.5): one stream of the 8
+// Per-token format (sections 4.5 "Encoding", 5.1; appendix "Compared
+// configurations"): one stream of the 8
 // KV heads' 1024 rotated values per token. Lane l holds channels l and l + 64
 // of every head, i.e. stream positions 128h + l and 128h + 64 + l: value i of
 // a lane (i = 2h + j) sits at position tok_pos(i, lane).

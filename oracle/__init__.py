@@ -19,7 +19,8 @@ Modules
   means      O12  windowed INT8 channel-mean removal for keys (sections 3.2, 5)
   token      O13-O17  the per-token format: one 1024-value stream per token over
              all 8 KV heads, min-max affine grid, drift, rANS, least-squares
-             refit with fp16 (o, s) (sections 4.2-4.5, 5.1, 5.5)
+             refit with fp16 (o, s) (sections 4.2-4.5, 5.1; appendix
+             "Compared configurations")
   measures   entropy, cross-entropy, coding gain, normal gap, NMSE (section 3.1/3.2)
 
 Parity status: every function is pinned by the tests in ``tests/`` against

@@ -12,8 +12,9 @@ Paper anchors (D-Quant, arXiv 2609.19880):
 * section 4.3 "Drift": minimise sum_i (x_i - x_hat(m_i))^2 subject to that
   constraint; only a few values move from an expensive symbol to a nearby
   cheaper one; section 1 solves it with a Lagrangian and bisection;
-* section 5.4 / appendix "Drift makes only sparse, local corrections": no
-  changed symbol moves by more than one reconstruction level.
+* appendix, paragraph "Drift makes only sparse, local corrections": the
+  paper observes that every symbol drift changes lands on a neighbouring
+  reconstruction level, never further away.
 
 Readings: one stream is the 128 channels of one
 (token, KV head); the per-token scale is the L2 norm stored as fp16; the

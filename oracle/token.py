@@ -12,8 +12,10 @@ Paper anchors (D-Quant, arXiv 2609.19880):
   rANS encode in the same wave;
 * section 5.1: 331- and 231-byte key / value containers with 8 / 6 levels,
   each token quantised as one group of 1024 values;
-* section 5.5: token-wise min-max affine grids, per-token grouping,
-  least-squares refitting and FP16 metadata.
+* appendix, paragraph "Compared configurations": the format the paper
+  measures groups each token on its own, sets its affine grid from the
+  token's minimum and maximum, refits that grid by least squares and keeps
+  the grid parameters as two fp16 numbers.
 
 Readings:
 * the stream is the 8 heads' rotated values in head-major order, each head

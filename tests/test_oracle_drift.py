@@ -3,8 +3,9 @@
 D-Quant section 4.2: every stream satisfies sum_i r(m_i) <= B = 8C - sigma
 and fits its container; section 4.3: drift solves
 min sum (x - x_hat)^2 s.t. the rate constraint, moving expensive symbols to
-nearby cheaper ones; the paper reports that no changed symbol moves by more
-than one level. Checked here: container length bounds (including
+nearby cheaper ones; the paper's appendix observes every drifted symbol
+landing on a neighbouring level (paragraph "Drift makes only sparse, local
+corrections"). Checked here: container length bounds (including
 adversarial rows), the rANS information identity, the one-level inward
 property, minimality of the move set, and Everett's generalised-Lagrange
 optimality by brute force on short streams.

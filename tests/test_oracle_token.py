@@ -1,6 +1,7 @@
 """Pins of O13-O17, the per-token stream format (one 1024-value stream per
 token over all 8 KV heads, token-wise min-max affine grid, drift, rANS, least-
-squares refit with fp16 metadata; sections 4.2, 4.3, 4.5, 5.1, 5.5): closed
+squares refit with fp16 metadata; sections 4.2, 4.3, 4.5, 5.1 and the
+appendix paragraph "Compared configurations"): closed
 forms of the expected maximum, brute force for the nearest level, a library
 least-squares solve for the refit, exact invariances of the min-max grid, and
 the container and drift invariants the paper states."""
