@@ -221,19 +221,25 @@ void fill_enc_table(const dq_table_info& t, dq::EncTable* e) {
 // Decode entries; bits 0..7 hold the fp16 high byte of the centred level
 // m - (M-1)/2 (its low byte is zero for M <= 9). The per-token kernel folds
 // the centre into the grid offset: o + s m = (o + s (M-1)/2) + s (m - (M-1)/2).
-void fill_entries(const dq_table_info& t, uint32_t* ent) {
+void fill_entries(const dq_table_info& t, uint32_t* ent, uint32_t* wide) {
     const uint32_t total = 1u << t.prob_bits;
     for (int m = 0; m < t.levels; ++m) {
         uint16_t h = host_f64_to_f16((double)m - (t.levels - 1) / 2.0);
-        for (uint32_t s = t.cum[m]; s < t.cum[m + 1]; ++s)
+        for (uint32_t s = t.cum[m]; s < t.cum[m + 1]; ++s) {
             ent[s] = dq::entry_pack(h >> 8, s - t.cum[m], t.freq[m], (uint32_t)m);
+            if (wide) dq::wide_entry_pack(h >> 8, s - t.cum[m], t.freq[m], wide + 2 * s);
+        }
     }
-    for (uint32_t s = total; s < (uint32_t)dq::kTableSlots; ++s) ent[s] = 0;
+    for (uint32_t s = total; s < (uint32_t)dq::kTableSlots; ++s) {
+        ent[s] = 0;
+        if (wide) wide[2 * s] = wide[2 * s + 1] = 0;
+    }
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static_assert(DQ_NOALLOC_SCRATCH == dq::kScratchBytes, "the header states the scratch size");
+static_assert((2 * sizeof(dq::EncTable)) % 16 == 0, "the two-dword key table starts 16-byte aligned");
 
 }  // namespace
 
@@ -313,23 +319,26 @@ static int tables_init(dq_tables** out, const dq_table_params* keys, const dq_ta
     if (rc != DQ_OK) { delete t; return rc; }
     fill_enc_table(t->info[0], &t->enc[0]);
     fill_enc_table(t->info[1], &t->enc[1]);
-    uint32_t host[2 * dq::kTableSlots];
-    fill_entries(t->info[0], host);
-    fill_entries(t->info[1], host + dq::kTableSlots);
+    uint32_t host[2 * dq::kTableSlots], wide_k[2 * dq::kTableSlots];
+    fill_entries(t->info[0], host, wide_k);
+    fill_entries(t->info[1], host + dq::kTableSlots, nullptr);
     hipError_t e = hipGetDevice(&t->device);
     if (e == hipSuccess) e = dq::prepare_attention_kernels();
     if (e == hipSuccess) e = dq::scratch_device_address(&t->d_scratch);
     if (e != hipSuccess) { delete t; return hip_fail(e); }
     const size_t ent_bytes = sizeof(uint32_t) * 2 * dq::kTableSlots;
-    const size_t total = ent_bytes + sizeof(dq::EncTable) * 2;
+    const size_t wide_off = ent_bytes + sizeof(dq::EncTable) * 2;   // a multiple of 16 bytes
+    const size_t total = wide_off + sizeof(wide_k);
     void* d = nullptr;
     e = hipMalloc(&d, total);
     if (e != hipSuccess) { delete t; return hip_fail(e); }
     e = hipMemcpy(d, host, ent_bytes, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy((char*)d + ent_bytes, t->enc, sizeof(dq::EncTable) * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy((char*)d + wide_off, wide_k, sizeof(wide_k), hipMemcpyHostToDevice);
     if (e != hipSuccess) { (void)hipFree(d); delete t; return hip_fail(e); }
     t->d_entries = (uint32_t*)d;
     t->d_enc = (dq::EncTable*)((char*)d + ent_bytes);
+    t->d_wide_k = (uint32_t*)((char*)d + wide_off);
     *out = t;
     return DQ_OK;
 }
@@ -483,6 +492,7 @@ static int decode_attention_impl(const dq_tables* t, const void* q, int q_dtype,
     a.step_v = (float)t->info[1].step;
     a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
     a.entries = t->d_entries;
+    a.wide_k = t->d_wide_k;
     a.partials = (float*)workspace;
     a.out = out;
     a.err_word = err_word;

@@ -32,17 +32,28 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 64;
 constexpr int kRowH = 72;                 // fp16 per LDS row of the level / weight tiles
 constexpr int kRowB = kRowH * 2;          // bytes
-constexpr int kPad = 144;                 // bytes after a container tile: lane 63 of a corrupt tile reads < 63C + 132
+constexpr int kPad = 144;                 // bytes after a container tile of the symbol-decode hook: lane 63 of a
+                                          // corrupt tile reads < 63C + 132
 constexpr int kVtRow = 32;                // bytes per token row of the V level tile (16 fp16 channels)
-constexpr uint32_t kOffTabK = 0;
-constexpr uint32_t kOffTabV = 4096;
-constexpr uint32_t kOffQt = 8192;         // [4][128] fp16 rotated queries
-constexpr uint32_t kOffZero = 9216;       // 256 zero bytes: A operand of rows without a head
-constexpr uint32_t kOffKappa = 9472;      // [4] floats
-constexpr uint32_t kOffWaves = 9488;
+// LDS of attn_kernel. The key table is held in two-dword form (8 KB), the
+// value table in one-dword form (4 KB): that keeps a work-group at 40 KB, four
+// per CU, while the key chain's decode step needs no field extraction.
+constexpr uint32_t kOffTabK = 0;          // [1024][2] two-dword key entries
+constexpr uint32_t kOffTabV = 8192;       // [1024] value entries
+constexpr uint32_t kOffQt = 12288;        // [4][128] fp16 rotated queries
+constexpr uint32_t kOffZero = 13312;      // 256 zero bytes: A operand of rows without a head
+constexpr uint32_t kOffKappa = 13568;     // [4] floats
+constexpr uint32_t kOffWaves = 13584;
 
 __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
 
+// Per-wave LDS: the key container tile, the value container tile, then the
+// value level tile, which also holds the fp16 p.v weights between passes (they
+// are read into registers at the start of a pass, before its first level
+// row is written). No padding separates the regions: the byte window of a
+// corrupt stream can read up to 138 - C bytes past its tile, which stays
+// inside the next region of the same wave (the value container tile, or the
+// 2048-byte level tile).
 // LDS stride of one token's container: C itself unless C is a multiple of 8,
 // in which case C + 4 keeps the stride an odd number of dwords, so that the
 // lanes' byte-window reads spread over the LDS banks (a stride of 8 dwords
@@ -50,9 +61,9 @@ __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15
 __host__ __device__ inline uint32_t lds_stride(int c) { return (c & 7) ? (uint32_t)c : (uint32_t)c + 4u; }
 
 __host__ __device__ inline uint32_t wave_bytes(int ck, int cv) {
-    return align16(kTile * lds_stride(ck) + kPad) + align16(kTile * lds_stride(cv) + kPad) + kTile * kVtRow +
-           4 * kRowB;
+    return align16(kTile * lds_stride(ck)) + align16(kTile * lds_stride(cv)) + kTile * kVtRow;
 }
+static_assert(4 * kRowB <= kTile * kVtRow, "the p.v weights fit in the value level tile");
 
 // Row index ((page * Hkv + g) * P + slot) of the first token of each 16-token
 // group of the tile starting at t0 (< T); a page holds a multiple of 16
@@ -150,15 +161,15 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const size_t head_stride = (size_t)a.slot_count * kPartStride;
     float* part = a.partials + (((size_t)b * a.num_q_heads + (size_t)g * G) * a.slot_count + split) * kPartStride;
 
-    const uint32_t kcB = align16(kTile * lds_stride(a.ck) + kPad), vcB = align16(kTile * lds_stride(a.cv) + kPad);
+    const uint32_t kcB = align16(kTile * lds_stride(a.ck)), vcB = align16(kTile * lds_stride(a.cv));
     const uint32_t oW = kOffWaves + (uint32_t)wave * wave_bytes(a.ck, a.cv);
-    const uint32_t oKc = oW, oVc = oW + kcB, oVt = oVc + vcB, oWl = oVt + kTile * kVtRow;
+    const uint32_t oKc = oW, oVc = oW + kcB, oVt = oVc + vcB, oWl = oVt;
 
     // ---- prologue: tables, zero regions, rotated queries
     {
-        const uint32_t* ent = a.entries;
         uint32_t* tab = (uint32_t*)lds;
-        for (int i = tid; i < 2 * kTableSlots; i += kThreads) tab[i] = ent[i];
+        for (int i = tid; i < 2 * kTableSlots; i += kThreads) tab[i] = a.wide_k[i];
+        for (int i = tid; i < kTableSlots; i += kThreads) tab[2 * kTableSlots + i] = a.entries[kTableSlots + i];
         uint32_t* z = (uint32_t*)(lds + kOffZero);
         if (tid < 64) z[tid] = 0u;
     }
@@ -243,22 +254,27 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
                     }
                     if (do_k && do_v) {
                         // both table reads in flight before either chain advances
-                        ek[jj] = rans_lookup(kr, tabK, maskK);
+                        const u32x2 wk = rans_lookup_wide(kr, tabK, maskK);
                         ev[jj] = rans_lookup(vr, tabV, maskV);
                         __builtin_amdgcn_sched_barrier(0);
-                        rans_advance(kr, ek[jj], pk);
+                        rans_advance_wide(kr, wk, pk);
+                        ek[jj] = wk.x;
                         rans_advance(vr, ev[jj], pv);
                     } else {
-                        if (do_k) ek[jj] = rans_dec_step(kr, tabK, maskK, pk);
+                        if (do_k) {
+                            const u32x2 wk = rans_lookup_wide(kr, tabK, maskK);
+                            rans_advance_wide(kr, wk, pk);
+                            ek[jj] = wk.x;
+                        }
                         if (do_v) ev[jj] = rans_dec_step(vr, tabV, maskV, pv);
                     }
                 }
                 if (do_k) {
                     u32x4 bw;
-                    bw[0] = pack_levels(ek[0], ek[1]);
-                    bw[1] = pack_levels(ek[2], ek[3]);
-                    bw[2] = pack_levels(ek[4], ek[5]);
-                    bw[3] = pack_levels(ek[6], ek[7]);
+                    bw[0] = pack_levels_wide(ek[0], ek[1]);
+                    bw[1] = pack_levels_wide(ek[2], ek[3]);
+                    bw[2] = pack_levels_wide(ek[4], ek[5]);
+                    bw[3] = pack_levels_wide(ek[6], ek[7]);
                     // pinned here: hoisting all 16 query loads to the top of the pass costs 64 VGPRs
                     uint32_t qa = aq_off + 16u * (2 * blk + hh);
                     asm volatile("" : "+v"(qa));
@@ -410,13 +426,15 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 if ((jj & 3) == 0) rans_refill(kr);
-                ek[jj] = rans_dec_step(kr, tabK, maskK, pk);
+                const u32x2 wk = rans_lookup_wide(kr, tabK, maskK);
+                rans_advance_wide(kr, wk, pk);
+                ek[jj] = wk.x;
             }
             u32x4 bw;
-            bw[0] = pack_levels(ek[0], ek[1]);
-            bw[1] = pack_levels(ek[2], ek[3]);
-            bw[2] = pack_levels(ek[4], ek[5]);
-            bw[3] = pack_levels(ek[6], ek[7]);
+            bw[0] = pack_levels_wide(ek[0], ek[1]);
+            bw[1] = pack_levels_wide(ek[2], ek[3]);
+            bw[2] = pack_levels_wide(ek[4], ek[5]);
+            bw[3] = pack_levels_wide(ek[6], ek[7]);
             uint32_t qa = aq_off + 16u * (uint32_t)j;
             asm volatile("" : "+v"(qa));
             const half8 aq = *(const half8*)(lds + qa);

@@ -9,6 +9,7 @@ namespace dq {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Orders this wave's earlier LDS accesses before its later ones as seen by
 // the other lanes of the same wave.
@@ -20,6 +21,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
 
 // Per-lane rANS decoder state. The container bytes are read through a
 // 4-byte window refilled every 4 steps (at most one byte is consumed per
@@ -91,11 +93,30 @@ __device__ __forceinline__ uint32_t rans_dec_step(RansLane& r, uint32_t tab, uin
     return e;
 }
 
+// The same step from a two-dword entry (wide_entry_pack): one 8-byte table
+// read, and the 24-bit multiply-add takes f_m and the bias straight from it.
+// The entry's dword 0 carries the level's fp16 high byte in bits 24..31.
+__device__ __forceinline__ u32x2 rans_lookup_wide(const RansLane& r, uint32_t tab, uint32_t mask) {
+    return *(lds_u32x2*)(size_t)(tab + ((r.x & mask) << 3));
+}
+__device__ __forceinline__ void rans_advance_wide(RansLane& r, u32x2 e, uint32_t p) {
+    const uint32_t xn = __umul24(e.x, r.x >> p) + e.y;      // e.x & 0xFFFFFF = f_m
+    const uint32_t t = __builtin_amdgcn_perm(xn, r.win, r.sel);
+    const bool need = xn < kStateLow;
+    r.x = need ? t : xn;
+    r.sel += need ? 1u : 0u;
+    asm volatile("" : "+v"(r.sel));
+}
+
 // Two fp16 levels (entries e0 for the lower channel, e1 for the upper) packed
 // into one dword: the level's high byte sits in bits 0..7 of an entry and its
 // low byte is zero.
 __device__ __forceinline__ uint32_t pack_levels(uint32_t e0, uint32_t e1) {
     return __builtin_amdgcn_perm(e1, e0, 0x040C000Cu);
+}
+// The same from dword 0 of two-dword entries (level byte in bits 24..31).
+__device__ __forceinline__ uint32_t pack_levels_wide(uint32_t e0, uint32_t e1) {
+    return __builtin_amdgcn_perm(e1, e0, 0x070C030Cu);
 }
 
 }  // namespace dq

@@ -27,6 +27,15 @@ __host__ __device__ inline uint32_t entry_pack(uint32_t lvl_hi, uint32_t bias, u
     return lvl_hi | (bias << 8) | (f << 18) | (m << 28);
 }
 
+// Two-dword form of the same entry, read with one 8-byte LDS load: dword 0 =
+// f_m | lvl_hi << 24 (its low 24 bits are exactly the multiplicand of a 24-bit
+// multiply-add), dword 1 = bias (the addend). The decode step then needs no
+// field extraction.
+__host__ __device__ inline void wide_entry_pack(uint32_t lvl_hi, uint32_t bias, uint32_t f, uint32_t* out) {
+    out[0] = f | (lvl_hi << 24);
+    out[1] = bias;
+}
+
 // Per-table constants the encoder needs (passed by value to kernels).
 struct EncTable {
     int levels, container, prob_bits, pad0;
@@ -89,6 +98,7 @@ struct AttnArgs {
     const int8_t* k_mean;               // optional key block means (see EncArgs)
     const uint16_t* k_mean_scale;
     const uint32_t* entries;            // [2][kTableSlots] decode tables (K then V)
+    const uint32_t* wide_k;             // [kTableSlots][2] the key table in two-dword form
     float* partials;                    // [batch][Hq][slot_count][kPartStride]
     float* out;
     uint32_t* err_word;
@@ -154,7 +164,8 @@ struct dq_tables {
     int format;               // 0: per-head streams, 1: per-token streams
     dq_table_info info[2];
     dq::EncTable enc[2];
-    uint32_t* d_entries;      // [2][kTableSlots] decode tables, then the two EncTables
+    uint32_t* d_entries;      // [2][kTableSlots] decode tables, the two EncTables, the two-dword key table
     dq::EncTable* d_enc;
+    uint32_t* d_wide_k;       // [kTableSlots][2] key decode table in two-dword form (inside d_entries)
     void* d_scratch;          // this device's copy of the fixed attention scratch (not owned)
 };
