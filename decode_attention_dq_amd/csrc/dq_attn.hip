@@ -65,23 +65,31 @@ __host__ __device__ inline uint32_t wave_bytes(int ck, int cv) {
 }
 static_assert(4 * kRowB <= kTile * kVtRow, "the p.v weights fit in the value level tile");
 
-// Row index ((page * Hkv + g) * P + slot) of the first token of each 16-token
-// group of the tile starting at t0 (< T); a page holds a multiple of 16
+// A 64-token tile is four 16-token groups; a page holds a multiple of 16
 // tokens, so each group's containers are 16 * C contiguous bytes and its norms
-// 16 contiguous halves. A group that starts at or past T takes group 0's row:
-// its lanes are masked out of the softmax, and the copy stays inside pages of
-// this sequence. Everything here is uniform over the wave.
-__device__ __forceinline__ void tile_rows(size_t* row, const int32_t* __restrict__ bt_row, int log2p, int P,
-                                          int hkv, int g, int t0, int T) {
+// 16 contiguous halves, at row (page * Hkv + g) * P + slot of its first token.
+// A group that starts at or past T takes group 0's row: its lanes are masked
+// out of the softmax, and the copy stays inside pages of this sequence.
+// Everything here is uniform over the wave.
+//
+// Page ids of the tile's 4 groups, loaded into VGPRs without waiting: issued
+// a tile ahead, their latency hides behind a decode pass.
+__device__ __forceinline__ void tile_pages(int* pg, const int32_t* __restrict__ bt_row, int log2p, int t0, int T) {
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
         const int tok = t0 + 16 * gi;
-        if (gi == 0 || tok < T) {
-            const int page = bt_row[tok >> log2p];
-            row[gi] = ((size_t)page * (size_t)hkv + (size_t)g) * (size_t)P + (size_t)(tok & (P - 1));
-        } else {
-            row[gi] = row[0];
-        }
+        pg[gi] = bt_row[(gi == 0 || tok < T ? tok : t0) >> log2p];
+    }
+}
+
+// Row indices of the tile's 4 token groups from their page ids (uniform).
+__device__ __forceinline__ void rows_from_pages(size_t* row, const int* pg, int P, int hkv, int g, int t0, int T) {
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+        const int tok = t0 + 16 * gi;
+        const int page = __builtin_amdgcn_readfirstlane(pg[gi]);
+        row[gi] = (gi == 0 || tok < T) ? ((size_t)page * (size_t)hkv + (size_t)g) * (size_t)P + (size_t)(tok & (P - 1))
+                                       : row[0];
     }
 }
 
@@ -106,7 +114,10 @@ __device__ __forceinline__ void stage_unit(uint8_t* lds, uint32_t dst, const uin
     }
     u32x4 v[4];
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) v[gi] = *(const u32x4*)(cache + row[gi] * (size_t)C + 16u * u);
+    for (int gi = 0; gi < 4; ++gi) {
+        const uint8_t* gb = cache + row[gi] * (size_t)C;   // uniform
+        v[gi] = *(const u32x4*)(gb + 16u * u);
+    }
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
         const uint32_t base = dst + (uint32_t)gi * 16u * S;
@@ -313,8 +324,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     // tiles, rarely. Value norms enter the p.v weights scaled by a running
     // power of two 2^-e_run (moved on the same condition) so that the fp16
     // weights w * |v| 2^-e_run stay below 2^(kSlack + 1).
-    auto softmax = [&](const float4v& d, bool valid, float rk, float rv, const float* cm) {
+    auto softmax = [&](const float4v& d, bool valid, uint32_t nk, uint32_t nv, const float* cm) {
         constexpr float kSlack = 8.0f;
+        const float rk = f16_to_f32((uint16_t)nk), rv = f16_to_f32((uint16_t)nv);
         float sv[4];
         bool up = false;
 #pragma unroll
@@ -385,15 +397,17 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
                         s16 * (kap[r] / a.step_k);
     };
 
-    // norms of the lane's token: row of its 16-token group plus its place in the group
-    auto load_norms = [&](int t0, const size_t* row, float& rk, float& rv) {
+    // norms of the lane's token (row of its 16-token group plus its place in
+    // the group), kept as fp16 bits: converted only in the softmax after the
+    // pass, so the loads are not waited on before it
+    auto load_norms = [&](int t0, const size_t* row, uint32_t& nk, uint32_t& nv) {
         const int gl = lane >> 4;
         const size_t r = (gl == 0 ? row[0] : gl == 1 ? row[1] : gl == 2 ? row[2] : row[3]) + (size_t)(lane & 15);
-        rk = 0.0f;
-        rv = 0.0f;
+        nk = 0;
+        nv = 0;
         if (t0 + lane < T) {
-            rk = f16_to_f32(a.k_norm[r]);
-            rv = f16_to_f32(a.v_norm[r]);
+            nk = a.k_norm[r];
+            nv = a.v_norm[r];
         }
     };
 
@@ -402,14 +416,18 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const uint32_t vbase = oVc + (uint32_t)lane * lds_stride(a.cv);
     const uint32_t kabs = lds0 + kbase, vabs = lds0 + vbase;   // absolute addresses for the decode steps
     int t = start + wave * kTile;
+    int pgn[4] = {0, 0, 0, 0};   // page ids of the next tile's groups, loaded a tile ahead
     if (t < end) {
         // prologue: keys of the first tile
         size_t row[4];
-        tile_rows(row, bt_row, log2p, P, hkv, g, t, T);
+        int pg0[4];
+        tile_pages(pg0, bt_row, log2p, t, T);
+        rows_from_pages(row, pg0, P, hkv, g, t, T);
+        if (t + kStep < end) tile_pages(pgn, bt_row, log2p, t + kStep, T);
         stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
         stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, row, lane);
-        float rk, rv, cm[4], ms;
-        uint32_t mq;
+        float cm[4], ms;
+        uint32_t mq, rk, rv;
         mean_load(t, mq, ms);
         load_norms(t, row, rk, rv);
         wave_lds_sync();
@@ -449,14 +467,16 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         const int tn = t + kStep;
         const bool has_next = tn < end;
         const bool valid = t + lane < T, valid_n = tn + lane < T;
-        float rk_n = 0.0f, rv_n = 0.0f, cm_n[4], ms_n = 0.0f;
-        uint32_t mq_n = 0;
+        float cm_n[4], ms_n = 0.0f;
+        uint32_t mq_n = 0, rk_n = 0, rv_n = 0;
+        int pgnn[4] = {0, 0, 0, 0};
         if (has_next) {
             mean_load(tn, mq_n, ms_n);
             size_t row[4];
-            tile_rows(row, bt_row, log2p, P, hkv, g, tn, T);
+            rows_from_pages(row, pgn, P, hkv, g, tn, T);
             stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
             load_norms(tn, row, rk_n, rv_n);
+            if (tn + kStep < end) tile_pages(pgnn, bt_row, log2p, tn + kStep, T);
         }
         wave_lds_sync();
         RansLane vr, kr;
@@ -477,10 +497,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
             mean_finish(mq_n, ms_n, cm_n);
             softmax(dk, valid_n, rk_n, rv_n, cm_n);
             wave_lds_sync();
-            size_t row[4];   // recomputed (scalar loads) rather than held through the pass
-            tile_rows(row, bt_row, log2p, P, hkv, g, tn, T);
+            size_t row[4];   // from the page ids held through the pass
+            rows_from_pages(row, pgn, P, hkv, g, tn, T);
             stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, row, lane);
         }
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) pgn[gi] = pgnn[gi];
     }
     if (bad && a.err_word) atomicOr(a.err_word, DQ_DEVERR_DECODE);
 
