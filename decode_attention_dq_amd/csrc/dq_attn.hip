@@ -93,6 +93,8 @@ __device__ __forceinline__ void rows_from_pages(size_t* row, const int* pg, int 
     }
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
 // Copy the containers of the tile's 4 token groups into LDS at `dst`, token t
 // at dst + t * lds_stride(C). Lane u (and u + 64 when C > 64) moves 16-byte
 // unit u of every group: a load from the group's uniform base plus 16u, and an
@@ -132,12 +134,33 @@ __device__ __forceinline__ void stage_unit(uint8_t* lds, uint32_t dst, const uin
     }
 }
 
+// Unpadded layout: each 16-byte unit goes from HBM straight into LDS (the
+// direct-to-LDS load writes lane u's 16 bytes at the uniform LDS address plus
+// 16u), with no register round trip and no wait here: the copy completes
+// behind the following work and is waited for (vmcnt) before the tile is read.
+// The padded layout splits units into 8-byte halves and goes through registers.
 template <bool PADDED>
 __device__ __forceinline__ void stage_tile(uint8_t* lds, uint32_t dst, const uint8_t* __restrict__ cache,
                                            int C, uint32_t magic, const size_t* row, int lane) {
+    if (!PADDED) {
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            const uint8_t* gb = cache + row[gi] * (size_t)C;   // uniform
+            lds_ptr d = (lds_ptr)(lds + dst + (uint32_t)gi * 16u * (uint32_t)C);
+            if (lane < C) __builtin_amdgcn_global_load_lds((const void*)(gb + 16u * (uint32_t)lane), d, 16, 0, 0);
+            if (C > 64 && lane + 64 < C)
+                __builtin_amdgcn_global_load_lds((const void*)(gb + 16u * (uint32_t)(lane + 64)),
+                                                 (lds_ptr)(lds + dst + (uint32_t)gi * 16u * (uint32_t)C + 1024u), 16, 0, 0);
+        }
+        return;
+    }
     if (lane < C) stage_unit<PADDED>(lds, dst, cache, C, magic, row, (uint32_t)lane);
     if (C > 64 && lane + 64 < C) stage_unit<PADDED>(lds, dst, cache, C, magic, row, (uint32_t)lane + 64u);
 }
+
+// Waits for this wave's outstanding global loads, the direct-to-LDS copies
+// among them, before their tile is read.
+__device__ __forceinline__ void stage_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -423,9 +446,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         int pg0[4];
         tile_pages(pg0, bt_row, log2p, t, T);
         rows_from_pages(row, pg0, P, hkv, g, t, T);
-        if (t + kStep < end) tile_pages(pgn, bt_row, log2p, t + kStep, T);
         stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
         stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, row, lane);
+        stage_wait();
+        if (t + kStep < end) tile_pages(pgn, bt_row, log2p, t + kStep, T);
         float cm[4], ms;
         uint32_t mq, rk, rv;
         mean_load(t, mq, ms);
@@ -461,7 +485,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         bad |= (valid && (kr.x != kStateLow || rans_consumed(kr, kabs) > (uint32_t)a.ck)) ? 1u : 0u;
         mean_finish(mq, ms, cm);
         softmax(dk, valid, rk, rv, cm);
+        wave_lds_sync();   // the pass is done with the key tile
+        if (t + kStep < end) {
+            rows_from_pages(row, pgn, P, hkv, g, t + kStep, T);
+            stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
+        }
     }
+    // Tiles are staged right after the pass that frees their region, and waited
+    // for just before the pass that decodes them.
     for (; t < end; t += kStep) {
         // values of tile t, interleaved with the keys of tile t + kStep
         const int tn = t + kStep;
@@ -470,11 +501,11 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         float cm_n[4], ms_n = 0.0f;
         uint32_t mq_n = 0, rk_n = 0, rv_n = 0;
         int pgnn[4] = {0, 0, 0, 0};
+        stage_wait();   // this pass's key tile tn and value tile t
         if (has_next) {
             mean_load(tn, mq_n, ms_n);
             size_t row[4];
             rows_from_pages(row, pgn, P, hkv, g, tn, T);
-            stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
             load_norms(tn, row, rk_n, rv_n);
             if (tn + kStep < end) tile_pages(pgnn, bt_row, log2p, tn + kStep, T);
         }
@@ -496,14 +527,23 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         if (has_next) {
             mean_finish(mq_n, ms_n, cm_n);
             softmax(dk, valid_n, rk_n, rv_n, cm_n);
-            wave_lds_sync();
+            wave_lds_sync();   // the pass is done with both container tiles
+            // the prefetched page ids go to scalars before any copy is issued, so
+            // that nothing waits for the copies until the next pass needs them
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) pgnn[gi] = __builtin_amdgcn_readfirstlane(pgnn[gi]);
             size_t row[4];   // from the page ids held through the pass
             rows_from_pages(row, pgn, P, hkv, g, tn, T);
             stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, row, lane);
+            if (tn + kStep < end) {
+                rows_from_pages(row, pgnn, P, hkv, g, tn + kStep, T);
+                stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
+            }
         }
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) pgn[gi] = pgnn[gi];
     }
+    stage_wait();   // no copy into this wave's region may still be in flight
     if (bad && a.err_word) atomicOr(a.err_word, DQ_DEVERR_DECODE);
 
     // ---- merge the 4 waves of this work-group
