@@ -72,9 +72,66 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
     a.out[(size_t)bh * kHeadDim + 64 + lane] = v1;
 }
 
+// One wave per (sequence, query head) row, four rows per work-group, for rows
+// with at most 64 partials: lane i holds (m, l) of partial i, the maxima and
+// the weighted sums of l are wave reductions, and each partial's weight is
+// read from its lane while the accumulator loads of all partials are in
+// flight together.
+template <bool ROTATED>
+__global__ __launch_bounds__(256) void merge_rows_kernel(MergeArgs a, int rows) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int bh = blockIdx.x * 4 + (tid >> 6);
+    if (bh >= rows) return;
+    const float* p = a.partials + (size_t)bh * a.slot_count * kPartStride;
+    const int len = a.context_lens[bh / a.num_q_heads];
+    const int T = covered_tokens(len, a.cap);
+    if (lane == 0 && a.err_word && (len < 0 || len > a.cap)) atomicOr(a.err_word, DQ_DEVERR_CONTEXT);
+    const int n = (T + a.split_len - 1) / a.split_len;
+    const int slots = n + (a.window_slot >= 0 ? 1 : 0);
+    const int my = lane < n ? lane : a.window_slot;   // the partial this lane reads (lane < slots)
+    float mi = -INFINITY, li = 0.0f;
+    if (lane < slots) {
+        mi = p[(size_t)my * kPartStride];
+        li = p[(size_t)my * kPartStride + 1];
+    }
+    float M = mi;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float fi = (mi == -INFINITY) ? 0.0f : exp2f(mi - M);
+    float L = li * fi;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    float v0 = 0.0f, v1 = 0.0f;
+    if (M != -INFINITY) {
+        for (int i = 0; i < slots; ++i) {
+            const float f = __shfl(fi, i);
+            const int s = i < n ? i : a.window_slot;
+            const float* ps = p + (size_t)s * kPartStride;
+            if (f != 0.0f) {   // a partial without tokens (m = -inf) may hold anything
+                v0 += ps[4 + lane] * f;
+                v1 += ps[4 + 64 + lane] * f;
+            }
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / (ROTATED ? L * (float)kHeadDim : L) : 0.0f;
+    v0 *= inv;
+    v1 *= inv;
+    if (ROTATED) fwht128_f32(v0, v1, lane);
+    a.out[(size_t)bh * kHeadDim + lane] = v0;
+    a.out[(size_t)bh * kHeadDim + 64 + lane] = v1;
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int rows, bool rotated, hipStream_t s) {
+    if (a.slot_count <= 64 && !(rows < 1024 && a.slot_count > 32)) {
+        const dim3 grid((unsigned)((rows + 3) / 4));
+        if (rotated)
+            hipLaunchKernelGGL((merge_rows_kernel<true>), grid, dim3(256), 0, s, a, rows);
+        else
+            hipLaunchKernelGGL((merge_rows_kernel<false>), grid, dim3(256), 0, s, a, rows);
+        return hipGetLastError();
+    }
     const bool wide = rows < 1024 && a.slot_count > 32;
     if (wide) {
         if (rotated)
