@@ -319,26 +319,27 @@ static int tables_init(dq_tables** out, const dq_table_params* keys, const dq_ta
     if (rc != DQ_OK) { delete t; return rc; }
     fill_enc_table(t->info[0], &t->enc[0]);
     fill_enc_table(t->info[1], &t->enc[1]);
-    uint32_t host[2 * dq::kTableSlots], wide_k[2 * dq::kTableSlots];
-    fill_entries(t->info[0], host, wide_k);
-    fill_entries(t->info[1], host + dq::kTableSlots, nullptr);
+    // two-dword entries, K then V ([2][kTableSlots][2])
+    uint32_t host[2 * dq::kTableSlots], wide[4 * dq::kTableSlots];
+    fill_entries(t->info[0], host, wide);
+    fill_entries(t->info[1], host + dq::kTableSlots, wide + 2 * dq::kTableSlots);
     hipError_t e = hipGetDevice(&t->device);
     if (e == hipSuccess) e = dq::prepare_attention_kernels();
     if (e == hipSuccess) e = dq::scratch_device_address(&t->d_scratch);
     if (e != hipSuccess) { delete t; return hip_fail(e); }
     const size_t ent_bytes = sizeof(uint32_t) * 2 * dq::kTableSlots;
     const size_t wide_off = ent_bytes + sizeof(dq::EncTable) * 2;   // a multiple of 16 bytes
-    const size_t total = wide_off + sizeof(wide_k);
+    const size_t total = wide_off + sizeof(wide);
     void* d = nullptr;
     e = hipMalloc(&d, total);
     if (e != hipSuccess) { delete t; return hip_fail(e); }
     e = hipMemcpy(d, host, ent_bytes, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy((char*)d + ent_bytes, t->enc, sizeof(dq::EncTable) * 2, hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipMemcpy((char*)d + wide_off, wide_k, sizeof(wide_k), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy((char*)d + wide_off, wide, sizeof(wide), hipMemcpyHostToDevice);
     if (e != hipSuccess) { (void)hipFree(d); delete t; return hip_fail(e); }
     t->d_entries = (uint32_t*)d;
     t->d_enc = (dq::EncTable*)((char*)d + ent_bytes);
-    t->d_wide_k = (uint32_t*)((char*)d + wide_off);
+    t->d_wide = (uint32_t*)((char*)d + wide_off);
     *out = t;
     return DQ_OK;
 }
@@ -492,7 +493,7 @@ static int decode_attention_impl(const dq_tables* t, const void* q, int q_dtype,
     a.step_v = (float)t->info[1].step;
     a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
     a.entries = t->d_entries;
-    a.wide_k = t->d_wide_k;
+    a.wide_k = t->d_wide;
     a.partials = (float*)workspace;
     a.out = out;
     a.err_word = err_word;
@@ -683,7 +684,7 @@ int dq_token_decode_attention_ext(const dq_tables* t, const void* q, int q_dtype
     a.k_mean = mk ? ex->k_mean : nullptr;
     a.k_mean_scale = mk ? ex->k_mean_scale : nullptr;
     a.softmax_scale = softmax_scale > 0 ? softmax_scale : 1.0f / sqrtf((float)dq::kHeadDim);
-    a.entries = t->d_entries;
+    a.wide = t->d_wide;
     a.partials = (float*)workspace;
     a.out = out;
     a.err_word = err_word;

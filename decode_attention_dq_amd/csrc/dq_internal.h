@@ -166,6 +166,6 @@ struct dq_tables {
     dq::EncTable enc[2];
     uint32_t* d_entries;      // [2][kTableSlots] decode tables, the two EncTables, the two-dword key table
     dq::EncTable* d_enc;
-    uint32_t* d_wide_k;       // [kTableSlots][2] key decode table in two-dword form (inside d_entries)
+    uint32_t* d_wide;         // [2][kTableSlots][2] decode tables in two-dword form, K then V (inside d_entries)
     void* d_scratch;          // this device's copy of the fixed attention scratch (not owned)
 };

@@ -49,7 +49,7 @@ struct TokAttnArgs {
     const int8_t* k_mean;               // optional key block means (see TokEncArgs)
     const uint16_t* k_mean_scale;
     float softmax_scale;
-    const uint32_t* entries;            // [2][kTableSlots] decode tables (K then V)
+    const uint32_t* wide;               // [2][kTableSlots][2] decode tables in two-dword form (K then V)
     float* partials;                    // [batch][Hq][slot_count][kPartStride]
     float* out;
     uint32_t* err_word;

@@ -10,6 +10,9 @@
 // of group g, decodes V head g together with K head g + 1 (two independent
 // rANS chains per lane), moves the V levels through an LDS transpose, and
 // accumulates p.v with each lane owning two channels of every query head.
+// The transpose holds 64 channels: p.v runs after each half of V head g.
+// The decode tables are in two-dword form (f_m and the level byte, then the
+// bias), so a decode step extracts no fields.
 // Containers sit in the cache dword-interleaved across the slots of a page
 // (dword j of every slot in row j), so the 64 lanes of a wave read
 // neighbouring dwords of the same few rows and every cache line is shared
@@ -51,13 +54,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // low byte is zero); the centre joins the offset, so the offset is near the
 // values' mean and the products carry only the centred part.
 struct TokShared {
-    uint32_t tab[2][kTableSlots];                 // decode tables, K then V
+    uint32_t tab[2][2 * kTableSlots];             // two-dword decode tables, K then V
     _Float16 qa[kTokHeads][kGrp][kHeadDim];       // rotated queries [KV head][head in group][channel]
     uint32_t zero[64];                            // A operand of the rows without a head (16 blocks of 16 bytes)
     float qsum[kTokHeads][kGrp];                  // their sums over the channels (fp32)
     union alignas(16) {
         struct {
-            uint32_t vt[kHeadDim / 4][kVtRowDw];  // V level bytes: row k holds channels 4k..4k+3, column = token
+            uint32_t vt[kHeadDim / 8][kVtRowDw];  // V level bytes of one 64-channel half: row k holds
+                                                  // channels 4k..4k+3 of the half, column = token
             _Float16 w[kGrp][kTile];              // p * s_v per head and token
         } wave[kWaves];
         struct {
@@ -112,7 +116,8 @@ struct GWin {
 struct GSrc {
     uint32_t row0;          // byte offset of the container's first dword
     uint32_t stride;        // bytes between rows (4 x the page size)
-    uint32_t last;          // index of the container's last row
+    uint32_t last;          // index of the container's last row (>= 3: containers have >= 16 bytes)
+    uint32_t row2;          // row0 + 2 stride: the refill loads row r + 2 as min(r, last - 2) stride + row2
 };
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t cache_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFFu, 0x00020000);
@@ -123,18 +128,21 @@ __device__ __forceinline__ uint32_t row_load(__amdgpu_buffer_rsrc_t rs, const GS
 }
 // Move the window past the consumed bytes. At most 4 bytes went since the
 // last refill, so ptr - g.a is at most 7: the window's 4 bytes lie in rows
-// a/4 + up and a/4 + up + 1, and the new a is g.a + 4 up. Those two rows stay
-// as the new first two; only the third is loaded, for the next refill.
+// a/4 + up and a/4 + up + 1, where up says whether the aligned start moved
+// (to g.a + 4). Those two rows stay as the new first two; only the third is
+// loaded, for the next refill.
 __device__ __forceinline__ void grans_refill(RansLane& r, GWin& g, __amdgpu_buffer_rsrc_t rs, const GSrc& src) {
     r.ptr += r.sel - kSel0;
-    const bool up = r.ptr - g.a >= 4u;
+    const uint32_t na = r.ptr & ~3u;
+    const bool up = na != g.a;
     const uint32_t lo = up ? g.d1 : g.d0, hi = up ? g.d2 : g.d1;
     r.win = __builtin_amdgcn_alignbyte(hi, lo, r.ptr);
     r.sel = kSel0;
-    g.a = r.ptr & ~3u;
+    g.a = na;
     g.d0 = lo;
     g.d1 = hi;
-    g.d2 = row_load(rs, src, (r.ptr >> 2) + 2u);
+    g.d2 = __builtin_amdgcn_raw_buffer_load_b32(rs, __umul24(min(r.ptr >> 2, src.last - 2u), src.stride) + src.row2,
+                                                0, 0);
 }
 // Stream state from the 3-byte flush at the container's start, then the
 // window at byte 3 (byte offsets count from the container's start).
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
     const int end = min(T, start + a.split_len);
 
     // ---- prologue: decode tables, rotated queries q~ = H q and their sums
-    for (int i = tid; i < 2 * kTableSlots; i += kThreads) (&S.tab[0][0])[i] = a.entries[i];
+    for (int i = tid; i < kTableSlots; i += kThreads) ((u32x4*)&S.tab[0][0])[i] = ((const u32x4*)a.wide)[i];
     for (int i = tid; i < kTokHeads * kGrp * kHeadDim / 2; i += kThreads) ((uint32_t*)&S.qa[0][0][0])[i] = 0u;
     if (tid < 64) S.zero[tid] = 0u;
     if (tid < kTokHeads * kGrp) (&S.qsum[0][0])[tid] = 0.0f;
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
     __syncthreads();
 
     const uint32_t tabK = (uint32_t)(size_t)(__attribute__((address_space(3))) uint32_t*)&S.tab[0][0];
-    const uint32_t tabV = tabK + kTableSlots * 4u;
+    const uint32_t tabV = tabK + kTableSlots * 8u;
     const uint32_t maskK = (1u << a.pk) - 1u, maskV = (1u << a.pv) - 1u;
     const __amdgpu_buffer_rsrc_t kres = cache_rsrc(a.k_cache), vres = cache_rsrc(a.v_cache);
     const float cs = a.softmax_scale * kLog2e / (float)kHeadDim;
@@ -229,8 +237,8 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
         const uint32_t ck4 = ((uint32_t)a.ck + 3u) >> 2, cv4 = ((uint32_t)a.cv + 3u) >> 2;
         const uint32_t pg = (uint32_t)page * (uint32_t)a.page_size, po = idx - pg;
         const uint32_t stride = 4u * (uint32_t)a.page_size;
-        const GSrc sk_ = {4u * (pg * ck4 + po), stride, ck4 - 1u};
-        const GSrc sv_ = {4u * (pg * cv4 + po), stride, cv4 - 1u};
+        const GSrc sk_ = {4u * (pg * ck4 + po), stride, ck4 - 1u, 4u * (pg * ck4 + po) + 2u * stride};
+        const GSrc sv_ = {4u * (pg * cv4 + po), stride, cv4 - 1u, 4u * (pg * cv4 + po) + 2u * stride};
         // key block means: lane 4g + hh gets q~ . (q * s16) of query head
         // (g, hh) and the 128-token block the tile lies in
         float qmu = 0.0f;
@@ -274,11 +282,11 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                     if (c8 | hf) grans_refill(rk, gk, kres, sk_);
 #pragma unroll
                     for (int i = 0; i < 4; i += 2) {
-                        const uint32_t e0 = rans_lookup(rk, tabK, maskK);
-                        rans_advance(rk, e0, (uint32_t)a.pk);
-                        const uint32_t e1 = rans_lookup(rk, tabK, maskK);
-                        rans_advance(rk, e1, (uint32_t)a.pk);
-                        kw[2 * hf + i / 2] = pack_levels(e0, e1);
+                        const u32x2 e0 = rans_lookup_wide(rk, tabK, maskK);
+                        rans_advance_wide(rk, e0, (uint32_t)a.pk);
+                        const u32x2 e1 = rans_lookup_wide(rk, tabK, maskK);
+                        rans_advance_wide(rk, e1, (uint32_t)a.pk);
+                        kw[2 * hf + i / 2] = pack_levels_wide(e0.x, e1.x);
                     }
                 }
                 uint32_t qa = qo + 16u * (uint32_t)c8;
@@ -320,74 +328,87 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
 #pragma unroll
             for (int hh = 0; hh < kGrp; ++hh) Wv.w[hh][lane] = (_Float16)wv[hh];
 
+            // p.v of one 64-channel half of V head g, 4 tokens per MFMA: the A
+            // operand is head lane & 3's weights of the 4 tokens, the B operand
+            // channel lane's levels of the same tokens (lane + 64's in the upper half)
+            auto pv_half = [&](float4_t& accv) {
+                wave_lds_sync();
+#pragma unroll 4
+                for (int j = 0; j < kTile; j += 4) {
+                    const u32x4 d = *(const u32x4*)&Wv.vt[vrow][j];
+                    const half4_t aw = *(const half4_t*)&Wv.w[lane & 3][j];
+                    const u32x2 bb = {__builtin_amdgcn_perm(d[1], d[0], vsel), __builtin_amdgcn_perm(d[3], d[2], vsel)};
+                    accv = __builtin_amdgcn_mfma_f32_4x4x4f16(aw, __builtin_bit_cast(half4_t, bb), accv, 0, 0, 0);
+                }
+                wave_lds_sync();
+            };
+            // the level bytes (bits 24..31 of dword 0 of an entry) of 4 channels
+            // of the lane's token, channel 4k first
+            auto vt_word = [](const uint32_t (&ev)[4]) {
+                return __builtin_amdgcn_perm(__builtin_amdgcn_perm(ev[3], ev[2], 0x0C0C0703u),
+                                             __builtin_amdgcn_perm(ev[1], ev[0], 0x0C0C0703u), 0x05040100u);
+            };
+
             dk = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
             if (g + 1 < kTokHeads) {
                 const uint32_t qo = q_off(g + 1);
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
 #pragma unroll 1
-                for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
-                    u32x4 kw;
+                    for (int c8 = 0; c8 < kHeadDim / 16; ++c8) {
+                        u32x4 kw;
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int c4 = 2 * c8 + hf;
-                        if (c4) {
-                            grans_refill(rv, gv, vres, sv_);
-                            grans_refill(rk, gk, kres, sk_);
-                        }
-                        uint32_t ev[4];
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const int c4 = 2 * c8 + hf;   // row of the half's transpose
+                            if (half | c4) {
+                                grans_refill(rv, gv, vres, sv_);
+                                grans_refill(rk, gk, kres, sk_);
+                            }
+                            uint32_t ev[4];
 #pragma unroll
-                        for (int i = 0; i < 4; i += 2) {
-                            ev[i] = rans_lookup(rv, tabV, maskV);
-                            const uint32_t e0 = rans_lookup(rk, tabK, maskK);
-                            rans_advance(rv, ev[i], (uint32_t)a.pv);
-                            rans_advance(rk, e0, (uint32_t)a.pk);
-                            ev[i + 1] = rans_lookup(rv, tabV, maskV);
-                            const uint32_t e1 = rans_lookup(rk, tabK, maskK);
-                            rans_advance(rv, ev[i + 1], (uint32_t)a.pv);
-                            rans_advance(rk, e1, (uint32_t)a.pk);
-                            kw[2 * hf + i / 2] = pack_levels(e0, e1);
+                            for (int i = 0; i < 4; i += 2) {
+                                const u32x2 v0 = rans_lookup_wide(rv, tabV, maskV);
+                                const u32x2 k0 = rans_lookup_wide(rk, tabK, maskK);
+                                rans_advance_wide(rv, v0, (uint32_t)a.pv);
+                                rans_advance_wide(rk, k0, (uint32_t)a.pk);
+                                const u32x2 v1 = rans_lookup_wide(rv, tabV, maskV);
+                                const u32x2 k1 = rans_lookup_wide(rk, tabK, maskK);
+                                rans_advance_wide(rv, v1, (uint32_t)a.pv);
+                                rans_advance_wide(rk, k1, (uint32_t)a.pk);
+                                ev[i] = v0.x;
+                                ev[i + 1] = v1.x;
+                                kw[2 * hf + i / 2] = pack_levels_wide(k0.x, k1.x);
+                            }
+                            Wv.vt[c4][lane] = vt_word(ev);
                         }
-                        Wv.vt[c4][lane] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(ev[3], ev[2], 0x0C0C0400u),
-                                                                __builtin_amdgcn_perm(ev[1], ev[0], 0x0C0C0400u),
-                                                                0x05040100u);
+                        uint32_t qa = qo + 16u * (uint32_t)(c8 + half * (kHeadDim / 16));
+                        asm volatile("" : "+v"(qa));
+                        const half8 aq = *(const half8*)(Sb + qa);
+                        dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, __builtin_bit_cast(half8, kw), dk, 0, 0, 0);
                     }
-                    uint32_t qa = qo + 16u * (uint32_t)c8;
-                    asm volatile("" : "+v"(qa));
-                    const half8 aq = *(const half8*)(Sb + qa);
-                    dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, __builtin_bit_cast(half8, kw), dk, 0, 0, 0);
+                    pv_half(acc[0][half]);
                 }
                 grans_refill(rk, gk, kres, sk_);
             } else {
-#pragma unroll 1
-                for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
-                    if (c4) grans_refill(rv, gv, vres, sv_);
-                    uint32_t ev[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        ev[i] = rans_lookup(rv, tabV, maskV);
-                        rans_advance(rv, ev[i], (uint32_t)a.pv);
+                for (int half = 0; half < 2; ++half) {
+#pragma unroll 1
+                    for (int c4 = 0; c4 < kHeadDim / 8; ++c4) {
+                        if (half | c4) grans_refill(rv, gv, vres, sv_);
+                        uint32_t ev[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const u32x2 e = rans_lookup_wide(rv, tabV, maskV);
+                            rans_advance_wide(rv, e, (uint32_t)a.pv);
+                            ev[i] = e.x;
+                        }
+                        Wv.vt[c4][lane] = vt_word(ev);
                     }
-                    Wv.vt[c4][lane] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(ev[3], ev[2], 0x0C0C0400u),
-                                                            __builtin_amdgcn_perm(ev[1], ev[0], 0x0C0C0400u),
-                                                            0x05040100u);
+                    pv_half(acc[0][half]);
                 }
             }
             grans_refill(rv, gv, vres, sv_);
-            wave_lds_sync();
 
-            // p.v of V head g, 4 tokens per MFMA: the A operand is head lane & 3's
-            // weights of the 4 tokens, the B operand channel lane's (lane + 64's)
-            // levels of the same tokens
-#pragma unroll 4
-            for (int j = 0; j < kTile; j += 4) {
-                const u32x4 d0 = *(const u32x4*)&Wv.vt[vrow][j];
-                const u32x4 d1 = *(const u32x4*)&Wv.vt[16 + vrow][j];
-                const half4_t aw = *(const half4_t*)&Wv.w[lane & 3][j];
-                const u32x2 b0 = {__builtin_amdgcn_perm(d0[1], d0[0], vsel), __builtin_amdgcn_perm(d0[3], d0[2], vsel)};
-                const u32x2 b1 = {__builtin_amdgcn_perm(d1[1], d1[0], vsel), __builtin_amdgcn_perm(d1[3], d1[2], vsel)};
-                acc[0][0] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw, __builtin_bit_cast(half4_t, b0), acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_4x4x4f16(aw, __builtin_bit_cast(half4_t, b1), acc[0][1], 0, 0, 0);
-            }
-            wave_lds_sync();
             // rotate: the next group's accumulators to the front
             const float4_t first0 = acc[0][0], first1 = acc[0][1];
 #pragma unroll
