@@ -323,6 +323,9 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
     if append:
         res["us_per_step_with_append"] = round(full * 1e6, 2)
         res["appended_streams"] = 2 * B * hkv
+        # the cache write of the newest token of each sequence alone (its events
+        # bracket it inside the back-to-back steps)
+        res["append_encode_us"] = round(float(np.mean([a0.elapsed_time(e0) for a0, e0, _ in ev])) * 1e3, 2)
     return res
 
 

@@ -205,12 +205,17 @@ void fill_enc_table(const dq_table_info& t, dq::EncTable* e) {
         e->freq[m] = f;
         e->cum[m] = t.cum[m];
         e->renorm_lim[m] = f << (24 - t.prob_bits);
-        // floor(x / f) = (x * magic) >> (31 + s) with s = floor(log2 f), magic =
-        // ceil(2^(31+s) / f) < 2^32; exact for x < 2^24 because the error
-        // x * (magic * f - 2^(31+s)) / (f * 2^(31+s)) < 2^(24-31-s) < 1/f.
+        // floor(x / f) = (x * magic) >> (31 + s) for x < 2^24, s = floor(log2 f)
+        // (f >= 2), with magic = ceil(2^(31+s) / f) raised by less than 32 so that
+        // its low 5 bits equal the shift s - 1 applied after the high product
+        // (a kernel can shift by the magic itself). Exact: magic = 2^(31+s) / f + d
+        // with 0 <= d < 32, and x d / 2^(31+s) < 2^(24+5-31-s) = 2^-(2+s) < 1/(2f)
+        // because f < 2^(s+1); so x magic / 2^(31+s) stays below floor(x/f) + 1.
+        // magic < 2^32: 2^(31+s) / f <= 2^31 and d < 32.
         int s = 31 - __builtin_clz(f);
         unsigned __int128 num = ((unsigned __int128)1) << (31 + s);
         uint64_t magic = (uint64_t)((num + f - 1) / f);
+        magic += (uint64_t)(((uint32_t)(s - 1) - (uint32_t)magic) & 31u);
         e->div_magic[m] = (uint32_t)magic;
         e->div_shift[m] = (uint32_t)(s - 1);
         e->recon[m] = t.recon[m];
@@ -397,6 +402,7 @@ int encode_impl(const dq_tables* t, const void* k, const void* v, int dtype, int
     a.drift_stats = drift_stats;
     a.err_word = err_word;
     a.tables = t->d_enc;
+    a.max_c = std::max(t->info[0].container, t->info[1].container);
     a.k_mean = k_mean;
     a.k_mean_scale = k_mean_scale;
     hipError_t e = dq::launch_encode(a, (hipStream_t)stream);

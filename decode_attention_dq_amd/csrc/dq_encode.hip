@@ -10,9 +10,12 @@
 //      and their (key, channel) ranks. What stays in LDS per stream is the
 //      symbol row of the minimal candidate prefix and the channels of the
 //      next candidates in order.
-//   2. lane = stream: the serial rANS encodes run side by side. A stream
-//      whose encoding overflows takes the next candidate and encodes again.
-//   3. lane = stream: a last encode writes each container.
+//   2. lane = stream: the serial rANS encodes run side by side, each in one
+//      pass that counts the bytes and keeps them in LDS. A stream whose
+//      encoding overflows takes the next candidate and encodes again.
+//   3. the whole wave, one stream after another: each container is written
+//      from its state and kept bytes, with one store per 64 bytes.
+// The table constants the phases read are staged in LDS once per work-group.
 // A stream that the first drift round cannot fit (no prefix fits, or it needs
 // more extensions than were staged) is redone from scratch by the complete
 // per-stream procedure, which also runs the fallback rounds.
@@ -67,19 +70,36 @@ __device__ __forceinline__ uint64_t order_key(double v) {
     return (b >> 63) ? ~b : (b | (1ull << 63));
 }
 
+// Integer wave reductions by DPP row operations (no LDS round trips; exact in
+// any order). A source lane outside the row reads 0.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xF, true);
+}
+constexpr int kDppRowShr = 0x110, kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141, kDppBcast15 = 0x142,
+              kDppBcast31 = 0x143, kDppQuadSwap1 = 0xB1, kDppQuadSwap2 = 0x4E;
+
+// Sum over the wave, in every lane.
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v += dpp_i<kDppQuadSwap1>(v);       // lane pairs
+    v += dpp_i<kDppQuadSwap2>(v);       // quads
+    v += dpp_i<kDppRowHalfMirror>(v);   // half rows
+    v += dpp_i<kDppRowMirror>(v);       // rows of 16: every lane holds its row's sum
+    v += dpp_i<kDppBcast15, 0xA>(v);    // rows 1, 3 add rows 0, 2
+    v += dpp_i<kDppBcast31, 0xC>(v);    // rows 2, 3 add rows 0 + 1: lane 63 holds the total
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Inclusive prefix sum over the wave's lanes.
+// Inclusive prefix sum over the wave's lanes: shifts by 1, 2, 4, 8 inside each
+// row of 16, then each row adds the totals of the rows before it.
 __device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(v, o);
-        if (lane >= o) v += t;
-    }
+    (void)lane;
+    v += dpp_i<kDppRowShr + 1>(v);
+    v += dpp_i<kDppRowShr + 2>(v);
+    v += dpp_i<kDppRowShr + 4>(v);
+    v += dpp_i<kDppRowShr + 8>(v);
+    v += dpp_i<kDppBcast15, 0xA>(v);
+    v += dpp_i<kDppBcast31, 0xC>(v);
     return v;
 }
 
@@ -103,13 +123,20 @@ struct Scratch {
 };
 
 struct WaveLds {
-    Scratch sc;
+    Scratch sc;                   // phase 1; in phases 2 and 3 the streams' byte buffers
     uint8_t sym[kPerWave][kRow];  // symbol row of each stream
     uint8_t ord[kPerWave][kTail]; // channels of the staged candidates, in (key, channel) order
     int32_t kmin[kPerWave];       // candidates in the minimal prefix
     int32_t staged[kPerWave];     // staged candidates; -1: redo with the per-stream procedure
     int32_t meta[kPerWave];       // bit 0: over budget before drift; bits 16..31: rho16
+    int32_t cnt[kPerWave];        // phase 2 result: emitted bytes, or -1 (nothing to write here)
+    uint32_t xfin[kPerWave];      // phase 2 result: final state
+    uint64_t idx[kPerWave];       // phase 2 result: the container's index in its cache
 };
+// Byte buffer of a phase-2 stream: cap + 1 = C - 2 bytes; the streams of a
+// wave share the Scratch area.
+constexpr int kBufArea = (int)sizeof(Scratch);
+static_assert(kBufArea >= 128 - 2, "a wave must hold the buffer of one stream of the largest container");
 
 // rANS encode of sym[127..0] (section 3.1, Enc) by one lane: before each
 // symbol the state is renormalised into [2^(16-p) f, 2^(24-p) f) by emitting
@@ -133,41 +160,64 @@ __device__ int rans_encode_lane(const uint8_t* sym, const SymConst* sc, int p, i
     return cnt;
 }
 
-// The same encode, counting bytes only.
-__device__ __forceinline__ int rans_count_lane(const uint8_t* sym, const SymConst* sc, int p, int cap) {
-    uint32_t x = kStateLow;
-    int cnt = 0;
-    for (int i = kHeadDim - 1; i >= 0; --i) {
-        const SymConst c = sc[sym[i]];
-        if (x >= c.lim) {
-            ++cnt;
-            x >>= 8;
-        }
-        const uint32_t q = __umulhi(x, c.magic) >> c.shift;
-        x = x + c.cum + q * ((1u << p) - c.freq);
-    }
-    return cnt <= cap ? cnt : -1;
-}
+// Per-symbol encode record, one 16-byte LDS read per step: lim, magic, c_m,
+// 2^p - f_m, where lim = 2^(24-p) f_m is the emission threshold and
+// floor(x / f_m) = umulhi(x, magic) >> (magic & 31) for x < 2^24 (the host
+// chooses the magic so that its low 5 bits are the shift). The records of a
+// table sit in one 256-byte aligned block, 16 bytes per symbol.
+typedef uint32_t u32x4e __attribute__((ext_vector_type(4)));
 
-// The same encode writing the container at dst: the 3-byte state at offset
-// 0, then the cnt emitted bytes in decode order, then zeros up to C.
-__device__ __forceinline__ void rans_write_lane(const uint8_t* sym, const SymConst* sc, int p, int cnt, int C,
-                                                uint8_t* __restrict__ dst) {
-    uint32_t x = kStateLow;
-    int j = kStateBytes + cnt;
-    for (int i = kHeadDim - 1; i >= 0; --i) {
-        const SymConst c = sc[sym[i]];
-        if (x >= c.lim) {
-            dst[--j] = (uint8_t)(x & 255u);
-            x >>= 8;
-        }
-        const uint32_t q = __umulhi(x, c.magic) >> c.shift;
-        x = x + c.cum + q * ((1u << p) - c.freq);
+// The same encode by one lane in a single pass that both counts and keeps the
+// bytes, without branches: the k-th emitted byte goes to buf[cap - k]. Every
+// step stores the state's low byte at the emission pointer e = buf + cap -
+// (bytes emitted so far), clamped to buf[0], and moves e down only when the
+// renormalisation emits; with cnt <= cap emitted bytes they lie in decode
+// order at buf[cap + 1 - cnt .. cap] (buf holds cap + 1 bytes). Two groups of
+// four records alternate: one group is read while the other is encoded.
+// Returns cnt, or -1 when it exceeds cap; xo gets the final state.
+__device__ __forceinline__ void rans_emit_group(uint32_t& x, int& e, int lo, const u32x4e (&c)[4]) {
+#pragma unroll
+    for (int b = 3; b >= 0; --b) {
+        const u32x4e r = c[b];
+        const bool emit = x >= r.x;
+        *(__attribute__((address_space(3))) uint8_t*)(size_t)(uint32_t)max(e, lo) = (uint8_t)(x & 255u);
+        e -= emit ? 1 : 0;
+        x = emit ? x >> 8 : x;
+        const uint32_t q = __umulhi(x, r.y) >> (r.y & 31u);
+        x = x + r.z + __umul24(q, r.w);
     }
-    dst[0] = (uint8_t)x;
-    dst[1] = (uint8_t)(x >> 8);
-    dst[2] = (uint8_t)(x >> 16);
-    for (int k = kStateBytes + cnt; k < C; ++k) dst[k] = 0;
+}
+// The records of the 4 symbols of row word w (sym[i .. i + 3]): symbols are
+// below 16, so in the word shifted left by 4 byte b is 16 x symbol b, and a
+// byte permute puts it under the block's address (whose low byte is zero).
+__device__ __forceinline__ void rans_emit_records(uint32_t w, uint32_t rec, u32x4e (&c)[4]) {
+    const uint32_t w4 = w << 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        c[b] = *(const __attribute__((address_space(3))) u32x4e*)(size_t)__builtin_amdgcn_perm(w4, rec, 0x03020104u + b);
+}
+__device__ __forceinline__ int rans_emit_lane(const uint8_t* sym, uint32_t rec, int cap, uint8_t* buf, uint32_t& xo) {
+    // LDS addresses as int: e goes at most 128 - cap below lo
+    const int lo = (int)(uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)buf;
+    const int top = lo + cap;
+    const uint32_t* words = (const uint32_t*)sym;
+    uint32_t x = kStateLow;
+    int e = top;
+    u32x4e ca[4], cb[4];
+    rans_emit_records(words[kHeadDim / 4 - 1], rec, ca);
+    uint32_t wb = words[kHeadDim / 4 - 2];
+    // word k holds symbols 4k .. 4k + 3; each word is read a group before its records
+    for (int k = kHeadDim / 4 - 1; k >= 1; k -= 2) {
+        rans_emit_records(wb, rec, cb);
+        const uint32_t wa = words[max(k - 2, 0)];   // (clamped reads: no branch, so no early wait)
+        rans_emit_group(x, e, lo, ca);
+        rans_emit_records(wa, rec, ca);
+        wb = words[max(k - 3, 0)];
+        rans_emit_group(x, e, lo, cb);
+    }
+    xo = x;
+    // e went below lo only after more than cap emissions
+    return e >= lo ? top - e : -1;
 }
 
 struct StreamId {
@@ -531,35 +581,64 @@ __global__ __launch_bounds__(64 * kWaves) void mean_kernel(EncArgs a) {
 __global__ __launch_bounds__(64 * kWaves, 6) void encode_kernel(EncArgs a, int per_wave) {
     __shared__ WaveLds wl_all[kWaves];
     __shared__ SymConst sconst[2][16];
+    __shared__ __attribute__((aligned(256))) u32x4e erec[2][16];
+    __shared__ EncTable tl[2];   // the tables' constants, read by phase 1 from LDS
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < 32) {
-        const EncTable* t = a.tables + (tid >> 4);
-        const int m = tid & 15;
-        SymConst c;
-        c.freq = t->freq[m];
-        c.cum = t->cum[m];
-        c.lim = t->renorm_lim[m];
-        c.magic = t->div_magic[m];
-        c.shift = t->div_shift[m];
-        c.inner = (uint32_t)t->inner[m];
-        c.pad0 = c.pad1 = 0;
-        sconst[tid >> 4][m] = c;
-    }
-    __syncthreads();
-
     WaveLds& W = wl_all[wave];
     const long total = 2l * a.num_tokens * a.num_kv_heads;
     const long sid0 = ((long)blockIdx.x * kWaves + wave) * per_wave;
-    if (sid0 >= total) return;
-    const int nb = (int)min((long)per_wave, total - sid0);   // streams of this wave, <= kPerWave
+    const int nb = (int)max(0l, min((long)per_wave, total - sid0));   // streams of this wave, <= kPerWave
 
-    // ---- phase 1: lane = channel, one stream at a time
+    // the first stream's inputs go out before the tables are staged (a row is
+    // read whatever its slot: every token of the call has one), and the
+    // table loads go out before the first stream's rotation and norm, which
+    // need no table (no branch before them: the loads are clamped instead)
     int slot_n = -1;
     double y0n = 0.0, y1n = 0.0, mh0n = 0.0, mh1n = 0.0;
-    StreamId idn = stream_id(a, sid0);
-    slot_n = a.slot_mapping[idn.token];
-    bool ok_n = stream_mean(a, idn, lane, mh0n, mh1n);
-    if (slot_n >= 0 && ok_n) load_row(a, idn, lane, y0n, y1n);
+    bool ok_n = false;
+    StreamId idn = {0, 0, 0};
+    if (nb > 0) {
+        idn = stream_id(a, sid0);
+        slot_n = a.slot_mapping[idn.token];
+        load_row(a, idn, lane, y0n, y1n);
+        ok_n = stream_mean(a, idn, lane, mh0n, mh1n);
+    }
+    constexpr int kTabDw = (int)(2 * sizeof(EncTable) / 4);
+    static_assert(kTabDw <= 2 * 64 * kWaves, "two table dwords per thread");
+    const uint32_t* tsrc = (const uint32_t*)a.tables;
+    const uint32_t tv0 = tsrc[min(tid, kTabDw - 1)], tv1 = tsrc[min(tid + 64 * kWaves, kTabDw - 1)];
+    const EncTable* tt = a.tables + ((tid >> 4) & 1);
+    const int tm = tid & 15;
+    const uint32_t cfreq = tt->freq[tm], ccum = tt->cum[tm], clim = tt->renorm_lim[tm], cmagic = tt->div_magic[tm],
+                   cshift = tt->div_shift[tm], cinner = (uint32_t)tt->inner[tm], cp = (uint32_t)tt->prob_bits;
+    double z0f = 0.0, z1f = 0.0;
+    uint16_t rho16f = 0;
+    if (nb > 0) {
+        double y0 = y0n, y1 = y1n;
+        fwht_f64(y0, y1, lane);
+        y0 = y0 - mh0n;
+        y1 = y1 - mh1n;
+        normalise(y0, y1, lane, z0f, z1f, rho16f);
+    }
+    if (tid < kTabDw) ((uint32_t*)tl)[tid] = tv0;
+    if (tid + 64 * kWaves < kTabDw) ((uint32_t*)tl)[tid + 64 * kWaves] = tv1;
+    if (tid < 32) {
+        SymConst c;
+        c.freq = cfreq;
+        c.cum = ccum;
+        c.lim = clim;
+        c.magic = cmagic;
+        c.shift = cshift;
+        c.inner = cinner;
+        c.pad0 = c.pad1 = 0;
+        sconst[tid >> 4][tm] = c;
+        erec[tid >> 4][tm] = u32x4e{clim, cmagic, ccum, (1u << cp) - cfreq};
+    }
+    __syncthreads();
+    if (nb == 0) return;
+    auto rec_addr = [&](int kv) { return (uint32_t)(size_t)(__attribute__((address_space(3))) u32x4e*)&erec[kv][0]; };
+
+    // ---- phase 1: lane = channel, one stream at a time
     for (int s = 0; s < nb; ++s) {
         const StreamId id = idn;
         const int slot = slot_n;
@@ -569,21 +648,23 @@ __global__ __launch_bounds__(64 * kWaves, 6) void encode_kernel(EncArgs a, int p
         if (s + 1 < nb) {   // the next stream's inputs go out before this one's work
             idn = stream_id(a, sid0 + s + 1);
             slot_n = a.slot_mapping[idn.token];
+            load_row(a, idn, lane, y0n, y1n);
             ok_n = stream_mean(a, idn, lane, mh0n, mh1n);
-            if (slot_n >= 0 && ok_n) load_row(a, idn, lane, y0n, y1n);
         }
         if (slot < 0 || !ok) {
             if (lane == 0) W.staged[s] = -2;   // no slot, or a flagged key block: nothing is written
             continue;
         }
-        const EncTable* T = a.tables + id.kv;
+        const EncTable* T = &tl[id.kv];
         const int M = T->levels;
-        double z0, z1;
-        uint16_t rho16;
-        fwht_f64(y0, y1, lane);
-        y0 = y0 - mh0;
-        y1 = y1 - mh1;
-        normalise(y0, y1, lane, z0, z1, rho16);
+        double z0 = z0f, z1 = z1f;   // stream 0's, computed before the barrier
+        uint16_t rho16 = rho16f;
+        if (s > 0) {
+            fwht_f64(y0, y1, lane);
+            y0 = y0 - mh0;
+            y1 = y1 - mh1;
+            normalise(y0, y1, lane, z0, z1, rho16);
+        }
         const int m0 = nearest_level(z0, T, M), m1 = nearest_level(z1, T, M);
         const int R = wave_sum_i(T->cost[m0] + T->cost[m1]);
         const Cands c = rank_candidates(T, z0, z1, m0, m1, lane, W.sc);
@@ -604,39 +685,126 @@ __global__ __launch_bounds__(64 * kWaves, 6) void encode_kernel(EncArgs a, int p
     }
     wave_sync();
 
-    // ---- phases 2 and 3: lane = stream
+    // ---- phase 2: lane = stream, the bytes kept in the Scratch area. A wave
+    // with a single stream runs its trials side by side instead: lane j
+    // encodes the row with the first j staged candidates moved (in a symbol
+    // row of its own), and the smallest j that fits is the serial loop's choice.
+    const int bstride = a.max_c - 2;
+    uint8_t* const bufs = (uint8_t*)&W.sc;
     bool slow = false;
-    if (lane < nb && W.staged[lane] >= 0) {
-        const StreamId id = stream_id(a, sid0 + lane);
-        const EncTable* T = a.tables + id.kv;
+    int bsel0 = 0;   // buffer of stream 0 (the fitting trial's, with trials side by side)
+    const int staged0 = W.staged[0];
+    if (nb == 1 && staged0 >= 0 && (staged0 + 1) * bstride <= kBufArea) {
+        const StreamId id = stream_id(a, sid0);
+        const EncTable* T = &tl[id.kv];
         const SymConst* sc = sconst[id.kv];
-        const int C = T->container, p = T->prob_bits;
-        uint8_t* row = W.sym[lane];
-        const int staged = W.staged[lane];
-        int used = 0, cnt;
-        while ((cnt = rans_count_lane(row, sc, p, C - kStateBytes)) < 0 && used < staged) {
-            const int ch = W.ord[lane][used++];   // the next candidate moves one level inward
-            row[ch] = (uint8_t)sc[row[ch]].inner;
-        }
-        if (cnt < 0) {
-            slow = true;   // the staged candidates did not suffice
-        } else {
-            const int slot = a.slot_mapping[id.token];
-            const int page = slot / a.page_size, po = slot - page * a.page_size;
-            const size_t idx = ((size_t)page * a.num_kv_heads + id.head) * a.page_size + po;
-            rans_write_lane(row, sc, p, cnt, C, a.cache[id.kv] + idx * C);
-            const int meta = W.meta[lane];
-            a.norm[id.kv][idx] = (uint16_t)((uint32_t)meta >> 16);
-            if (a.drift_stats) {
-                const int k = W.kmin[lane] + used;
-                const int rounds = ((meta & 1) || k > 0) ? 1 : 0;
-                a.drift_stats[((size_t)id.token * a.num_kv_heads + id.head) * 2 + id.kv] =
-                    (uint16_t)((k & 255) | (rounds << 8));
+        const int C = T->container;
+        {   // rows 1 .. staged0 start as copies of row 0: lane l copies dwords 8 (l % 4) .. + 7 into row 1 + l / 4
+            const uint32_t* src = (const uint32_t*)W.sym[0] + 8 * (lane & 3);
+            uint32_t d[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) d[u] = src[u];
+            if ((lane >> 2) < staged0) {
+                uint32_t* dst = (uint32_t*)W.sym[1 + (lane >> 2)] + 8 * (lane & 3);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) dst[u] = d[u];
             }
         }
-    } else if (lane < nb && W.staged[lane] == -1) {
-        slow = true;
+        wave_sync();
+        // candidate m moves in the rows of trials j > m: lane m writes its
+        // channel's inner level into each of those rows
+        if (lane < staged0) {
+            const int ch = W.ord[0][lane];
+            const uint8_t alt = (uint8_t)sc[W.sym[0][ch]].inner;
+            for (int j = lane + 1; j <= staged0; ++j) W.sym[j][ch] = alt;
+        }
+        wave_sync();
+        int cnt = -1;
+        uint32_t xo = 0;
+        if (lane <= staged0) cnt = rans_emit_lane(W.sym[lane], rec_addr(id.kv), C - kStateBytes, bufs + lane * bstride, xo);
+        const uint64_t fit = __ballot(cnt >= 0);
+        if (!fit) {
+            slow = lane == 0;   // no staged prefix suffices
+            if (lane == 0) W.cnt[0] = -1;
+        } else {
+            bsel0 = __ffsll((long long)fit) - 1;
+            if (lane == bsel0) {
+                const int slot = a.slot_mapping[id.token];
+                const int page = slot / a.page_size, po = slot - page * a.page_size;
+                const size_t idx = ((size_t)page * a.num_kv_heads + id.head) * a.page_size + po;
+                W.xfin[0] = xo;
+                W.idx[0] = idx;
+                W.cnt[0] = cnt;
+                const int meta = W.meta[0];
+                a.norm[id.kv][idx] = (uint16_t)((uint32_t)meta >> 16);
+                if (a.drift_stats) {
+                    const int k = W.kmin[0] + bsel0;
+                    const int rounds = ((meta & 1) || k > 0) ? 1 : 0;
+                    a.drift_stats[((size_t)id.token * a.num_kv_heads + id.head) * 2 + id.kv] =
+                        (uint16_t)((k & 255) | (rounds << 8));
+                }
+            }
+        }
+    } else if (lane < nb) {
+        int res = -1;
+        if (W.staged[lane] >= 0) {
+            const StreamId id = stream_id(a, sid0 + lane);
+            const EncTable* T = &tl[id.kv];
+            const SymConst* sc = sconst[id.kv];
+            const int C = T->container;
+            uint8_t* row = W.sym[lane];
+            uint8_t* buf = bufs + lane * bstride;
+            const int staged = W.staged[lane];
+            int used = 0, cnt;
+            uint32_t xo = 0;
+            while ((cnt = rans_emit_lane(row, rec_addr(id.kv), C - kStateBytes, buf, xo)) < 0 && used < staged) {
+                const int ch = W.ord[lane][used++];   // the next candidate moves one level inward
+                row[ch] = (uint8_t)sc[row[ch]].inner;
+            }
+            if (cnt < 0) {
+                slow = true;   // the staged candidates did not suffice
+            } else {
+                const int slot = a.slot_mapping[id.token];
+                const int page = slot / a.page_size, po = slot - page * a.page_size;
+                const size_t idx = ((size_t)page * a.num_kv_heads + id.head) * a.page_size + po;
+                W.xfin[lane] = xo;
+                W.idx[lane] = idx;
+                res = cnt;
+                const int meta = W.meta[lane];
+                a.norm[id.kv][idx] = (uint16_t)((uint32_t)meta >> 16);
+                if (a.drift_stats) {
+                    const int k = W.kmin[lane] + used;
+                    const int rounds = ((meta & 1) || k > 0) ? 1 : 0;
+                    a.drift_stats[((size_t)id.token * a.num_kv_heads + id.head) * 2 + id.kv] =
+                        (uint16_t)((k & 255) | (rounds << 8));
+                }
+            }
+        } else if (W.staged[lane] == -1) {
+            slow = true;
+        }
+        W.cnt[lane] = res;
     }
+    wave_sync();
+
+    // ---- phase 3: the whole wave writes each container: [state, 3 bytes LE]
+    // [bytes in decode order][zeros]
+    for (int s = 0; s < nb; ++s) {
+        const int cnt = W.cnt[s];
+        if (cnt < 0) continue;
+        const StreamId id = stream_id(a, sid0 + s);
+        const int C = tl[id.kv].container, cap = C - kStateBytes;
+        const uint32_t x = W.xfin[s];
+        const uint8_t* buf = bufs + (s == 0 ? bsel0 : s) * bstride;
+        uint8_t* dst = a.cache[id.kv] + W.idx[s] * (size_t)C;
+        for (int j = lane; j < C; j += 64) {
+            uint8_t v = 0;
+            if (j < kStateBytes) v = (uint8_t)(x >> (8 * j));
+            else if (j < kStateBytes + cnt) v = buf[cap + 1 - cnt + (j - kStateBytes)];
+            dst[j] = v;
+        }
+    }
+    wave_sync();   // the slow path below reuses the Scratch area
+
     // streams handed back: the complete per-stream procedure, from scratch
     uint64_t back = __ballot(slow);
     while (back) {
@@ -1194,7 +1362,9 @@ hipError_t launch_encode(const EncArgs& a, hipStream_t s) {
     }
     const long streams = 2l * a.num_tokens * a.num_kv_heads;
     const long waves_wanted = 6144;
-    const int per_wave = (int)std::min((long)kPerWave, std::max(1l, (streams + waves_wanted - 1) / waves_wanted));
+    const int buf_streams = kBufArea / (a.max_c - 2);   // byte buffers that fit in a wave's Scratch area
+    const int per_wave = (int)std::min((long)std::min(kPerWave, buf_streams),
+                                       std::max(1l, (streams + waves_wanted - 1) / waves_wanted));
     const long per_block = (long)per_wave * kWaves;
     dim3 grid((unsigned)((streams + per_block - 1) / per_block));
     hipLaunchKernelGGL(encode_kernel, grid, dim3(64 * kWaves), 0, s, a, per_wave);

@@ -61,6 +61,7 @@ struct EncArgs {
     uint16_t* drift_stats;
     uint32_t* err_word;
     const EncTable* tables;       // device copy: [0] keys, [1] values
+    int max_c;                    // the larger of the two container sizes
     // key channel-mean removal: tokens form blocks of 128 (block j = tokens
     // 128j .. 128j+127 of the call); null when off
     int8_t* k_mean;               // [pages][Hkv][mean_rows_per_page][128]

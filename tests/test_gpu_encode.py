@@ -185,6 +185,45 @@ def test_encode_paged_and_skipped_slots(gpu_lib):
         assert (untouched == 0xAB).all()
 
 
+def test_encode_append_newest_token_per_sequence(gpu_lib):
+    """The decode step's cache write on the ragged 1.96-bit workload: the
+    newest token of each of 64 sequences (8 KV heads, 8 / 6 levels, 32-byte
+    containers, 16-token pages scattered over the cache). 1024 streams run one
+    per wave with their drift trials side by side; containers, norms and drift
+    statistics are byte-identical to the oracle and no other slot is touched."""
+    dq = gpu_lib
+    w = workloads.WORKLOADS["ragged_1p96"]
+    tk, tv = oracle.make_table(w.k_levels, w.container), oracle.make_table(w.v_levels, w.cv)
+    tabs = dq.dq_tables_init(dq.make_params(w.k_levels, w.container), dq.make_params(w.v_levels, w.cv))
+    B, H, P = w.batch, w.num_kv_heads, w.page_size
+    lens = workloads.context_lengths(w)
+    pages = 2 * B
+    page_of = np.random.default_rng(21).permutation(pages)[:B]
+    slots = (page_of * P + (lens - 1) % P).astype(np.int32)
+    k = synth.gaussian_kv(11, synth.T_K, B, H)
+    v = synth.gaussian_kv(11, synth.T_V, B, H)
+    C = w.container
+    kc, vc, kn, vn, st, err = _encode(dq, tabs, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                                      page_size=P, slots=torch.from_numpy(slots).cuda(), num_pages=pages,
+                                      C=(C, C))
+    assert err == 0
+    used = np.zeros(pages * P, bool)
+    used[slots] = True
+    for which, rows, t, cache, norm in ((0, k, tk, kc, kn), (1, v, tv, vc, vn)):
+        r = oracle_encode(rows, t)
+        got = _unpage(cache, slots, P).reshape(-1, C)
+        bad = np.flatnonzero((got != r.containers).any(axis=1))
+        assert bad.size == 0, f"{'KV'[which]}: {bad.size} containers differ, first stream {bad[:3]}"
+        assert np.array_equal(_unpage(norm, slots, P).reshape(-1), rho16_bits(r))
+        s = st[:, :, which].reshape(-1)
+        assert np.array_equal(s & 255, r.changed.astype(np.uint16))
+        assert np.array_equal(s >> 8, np.minimum(r.rounds, 255).astype(np.uint16))
+        untouched = cache.transpose(0, 2, 1, 3).reshape(pages * P, H, C)[~used]
+        assert (untouched == 0xAB).all()
+    # the budget makes drift move symbols in many streams: several trials ran side by side
+    assert (st[:, :, 1] & 255).astype(int).max() >= 2
+
+
 def test_encode_full_llama_layer_sampled(gpu_lib):
     """Full cache-write workload (16 x 8192 tokens, 8 KV heads, bf16 with
     outlier channels) in the benchmark's launch configuration; two sampled
