@@ -323,10 +323,38 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
     if append:
         res["us_per_step_with_append"] = round(full * 1e6, 2)
         res["appended_streams"] = 2 * B * hkv
-        # the cache write of the newest token of each sequence alone (its events
-        # bracket it inside the back-to-back steps)
-        res["append_encode_us"] = round(float(np.mean([a0.elapsed_time(e0) for a0, e0, _ in ev])) * 1e3, 2)
+        # what the cache write of each sequence's newest token adds to a decode
+        # step: runs of back-to-back steps with and without it, each run between
+        # one pair of events (no markers between the calls)
+        def run(with_append: bool) -> float:
+            n = reps * copies
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(n):
+                l = i % copies
+                c = caches[l]
+                if with_append:
+                    dq.dq_encode_kv(tables, new_k[l], new_v[l], new_slots, c.k_cache, c.v_cache, c.k_norm, c.v_norm,
+                                    P, err_word=err, stream=stream)
+                dq.dq_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
+                                       c.context_lens, hkv, P, w.context, out, ws, err_word=err, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+        plain = min(run(False) for _ in range(3))
+        both = min(run(True) for _ in range(3))
+        res["append_encode_us"] = round(both - plain, 2)
     return res
+
+
+def other_workloads(dq, torch, workloads) -> dict:
+    return {
+        "long_llama_b4": config_measurement(dq, torch, workloads, "long_llama_b4", copies=4),
+        "long_llama_b1": config_measurement(dq, torch, workloads, "long_llama_b1", copies=8),
+        "ragged_1p96": config_measurement(dq, torch, workloads, "ragged_1p96", copies=2),
+        "window_split_qwen3_8b": config_measurement(dq, torch, workloads, "window_split_qwen3_8b", copies=2),
+        "mean_qwen3_8b": config_measurement(dq, torch, workloads, "mean_qwen3_8b", copies=2),
+    }
 
 
 def token_attention_time(dq, torch, workloads, tables, name: str, copies: int, reps: int):
@@ -588,7 +616,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=0,
                     help="counter collection only: build and run this many layer caches (marked in the output)")
-    ap.add_argument("--section", choices=["encode", "bf16", "token"], default=None,
+    ap.add_argument("--section", choices=["encode", "bf16", "token", "workloads"], default=None,
                     help="profiling only: run just this measurement and print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device-to-device copy of BYTES (reference for HBM byte counters)")
@@ -633,6 +661,9 @@ def main() -> int:
         return 0
     if args.section == "token":
         print(json.dumps({"token_format": token_measurement(dq, torch, workloads)}), flush=True)
+        return 0
+    if args.section == "workloads":
+        print(json.dumps({"other_workloads": other_workloads(dq, torch, workloads)}), flush=True)
         return 0
     if args.section == "bf16":
         print(json.dumps({"bf16_reference": bf16_measurement(dq, torch, workloads, args.workload, copies=2,
@@ -753,13 +784,7 @@ def main() -> int:
         cp["compressed_frac_of_copy"] = round(gbs / cp["read_plus_write_GBps"], 4)
         result["copy_reference"] = cp
         result["encode"] = encode_measurement(dq, torch, workloads)
-        result["other_workloads"] = {
-            "long_llama_b4": config_measurement(dq, torch, workloads, "long_llama_b4", copies=4),
-            "long_llama_b1": config_measurement(dq, torch, workloads, "long_llama_b1", copies=8),
-            "ragged_1p96": config_measurement(dq, torch, workloads, "ragged_1p96", copies=2),
-            "window_split_qwen3_8b": config_measurement(dq, torch, workloads, "window_split_qwen3_8b", copies=2),
-            "mean_qwen3_8b": config_measurement(dq, torch, workloads, "mean_qwen3_8b", copies=2),
-        }
+        result["other_workloads"] = other_workloads(dq, torch, workloads)
         result["bf16_reference"] = bf16_measurement(dq, torch, workloads, w.name, copies=2,
                                                     dq_us=per_call_s * 1e6)
         torch.cuda.empty_cache()

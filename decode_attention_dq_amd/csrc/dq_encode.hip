@@ -223,13 +223,14 @@ __device__ __forceinline__ int rans_emit_lane(const uint8_t* sym, uint32_t rec, 
 struct StreamId {
     int kv, token, head;
 };
+// (32-bit arithmetic: the host keeps 2 num_tokens num_kv_heads below 2^30)
 __device__ __forceinline__ StreamId stream_id(const EncArgs& a, long sid) {
-    const long nstreams = (long)a.num_tokens * a.num_kv_heads;
+    const int nstreams = a.num_tokens * a.num_kv_heads;
     StreamId s;
-    s.kv = sid >= nstreams ? 1 : 0;
-    const long rem = sid - s.kv * nstreams;
-    s.token = (int)(rem / a.num_kv_heads);
-    s.head = (int)(rem % a.num_kv_heads);
+    s.kv = (int)sid >= nstreams ? 1 : 0;
+    const int rem = (int)sid - s.kv * nstreams;
+    s.token = rem / a.num_kv_heads;
+    s.head = rem - s.token * a.num_kv_heads;
     return s;
 }
 
@@ -328,12 +329,15 @@ __device__ __forceinline__ void normalise(double y0, double y1, int lane, double
 }
 
 // Nearest level; an exact midpoint goes to the inner level.
+// (unrolled over the largest table, so the boundary reads go out together)
 __device__ __forceinline__ int nearest_level(double z, const EncTable* T, int M) {
     int m = 0;
-    for (int j = 0; j + 1 < M; ++j) {
-        const double bj = T->bounds[j];
-        if (bj >= 0.0) m += z > bj;
-        else m += z >= bj;
+#pragma unroll
+    for (int j = 0; j + 1 < kMaxLevels; ++j) {
+        if (j + 1 < M) {
+            const double bj = T->bounds[j];
+            m += (bj >= 0.0 ? z > bj : z >= bj) ? 1 : 0;
+        }
     }
     return m;
 }
@@ -583,7 +587,7 @@ __global__ __launch_bounds__(64 * kWaves, 6) void encode_kernel(EncArgs a, int p
     __shared__ SymConst sconst[2][16];
     __shared__ __attribute__((aligned(256))) u32x4e erec[2][16];
     __shared__ EncTable tl[2];   // the tables' constants, read by phase 1 from LDS
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     WaveLds& W = wl_all[wave];
     const long total = 2l * a.num_tokens * a.num_kv_heads;
     const long sid0 = ((long)blockIdx.x * kWaves + wave) * per_wave;

@@ -72,6 +72,76 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
     a.out[(size_t)bh * kHeadDim + 64 + lane] = v1;
 }
 
+// The same merge for few rows with up to 128 partials: 16 waves per row, wave
+// w holding partials w, w + 16, ..., w + 112 in registers. Every load of a
+// wave goes out before the row maximum is known (one memory round trip
+// instead of two per partial); the partials are added in the same order as
+// merge_kernel's.
+template <bool ROTATED>
+__global__ __launch_bounds__(64 * 16) void merge_wide_kernel(MergeArgs a) {
+    constexpr int kW = 16, kPer = 8;
+    __shared__ float red[kW][132];
+    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const float* p = a.partials + (size_t)bh * a.slot_count * kPartStride;
+    const int len = a.context_lens[bh / a.num_q_heads];
+    const int T = covered_tokens(len, a.cap);
+    if (tid == 0 && a.err_word && (len < 0 || len > a.cap)) atomicOr(a.err_word, DQ_DEVERR_CONTEXT);
+    const int n = (T + a.split_len - 1) / a.split_len;
+    const int slots = n + (a.window_slot >= 0 ? 1 : 0);   // <= kW * kPer (the host's choice)
+    float ms[kPer], ls[kPer], x0[kPer], x1[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+        const int i = wave + c * kW;
+        ms[c] = -INFINITY;
+        ls[c] = x0[c] = x1[c] = 0.0f;
+        if (i < slots) {
+            const float* ps = p + (size_t)(i < n ? i : a.window_slot) * kPartStride;
+            ms[c] = ps[0];
+            ls[c] = ps[1];
+            x0[c] = ps[4 + lane];
+            x1[c] = ps[4 + 64 + lane];
+        }
+    }
+    float M = ms[0];
+#pragma unroll
+    for (int c = 1; c < kPer; ++c) M = fmaxf(M, ms[c]);
+    if (lane == 0) red[wave][0] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, red[w][0]);
+    __syncthreads();
+    float L = 0.0f, v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+        if (ms[c] != -INFINITY) {   // a partial without tokens may hold anything
+            const float f = exp2f(ms[c] - M);
+            L += ls[c] * f;
+            v0 += x0[c] * f;
+            v1 += x1[c] * f;
+        }
+    }
+    red[wave][lane] = v0;
+    red[wave][64 + lane] = v1;
+    if (lane == 0) red[wave][128] = L;
+    __syncthreads();
+    if (wave != 0) return;
+    v0 = 0.0f;
+    v1 = 0.0f;
+    L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        v0 += red[w][lane];
+        v1 += red[w][64 + lane];
+        L += red[w][128];
+    }
+    const float inv = L > 0.0f ? 1.0f / (ROTATED ? L * (float)kHeadDim : L) : 0.0f;
+    v0 *= inv;
+    v1 *= inv;
+    if (ROTATED) fwht128_f32(v0, v1, lane);
+    a.out[(size_t)bh * kHeadDim + lane] = v0;
+    a.out[(size_t)bh * kHeadDim + 64 + lane] = v1;
+}
+
 // One wave per (sequence, query head) row, four rows per work-group, for rows
 // with at most 64 partials: lane i holds (m, l) of partial i, the maxima and
 // the weighted sums of l are wave reductions, and each partial's weight is
@@ -133,6 +203,13 @@ hipError_t launch_merge(const MergeArgs& a, int rows, bool rotated, hipStream_t 
         return hipGetLastError();
     }
     const bool wide = rows < 1024 && a.slot_count > 32;
+    if (wide && a.slot_count <= 128) {
+        if (rotated)
+            hipLaunchKernelGGL((merge_wide_kernel<true>), dim3(rows), dim3(64 * 16), 0, s, a);
+        else
+            hipLaunchKernelGGL((merge_wide_kernel<false>), dim3(rows), dim3(64 * 16), 0, s, a);
+        return hipGetLastError();
+    }
     if (wide) {
         if (rotated)
             hipLaunchKernelGGL((merge_kernel<true, 16>), dim3(rows), dim3(64 * 16), 0, s, a);
