@@ -347,14 +347,13 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
     return res
 
 
-def other_workloads(dq, torch, workloads) -> dict:
-    return {
-        "long_llama_b4": config_measurement(dq, torch, workloads, "long_llama_b4", copies=4),
-        "long_llama_b1": config_measurement(dq, torch, workloads, "long_llama_b1", copies=8),
-        "ragged_1p96": config_measurement(dq, torch, workloads, "ragged_1p96", copies=2),
-        "window_split_qwen3_8b": config_measurement(dq, torch, workloads, "window_split_qwen3_8b", copies=2),
-        "mean_qwen3_8b": config_measurement(dq, torch, workloads, "mean_qwen3_8b", copies=2),
-    }
+OTHER_WORKLOADS = {"long_llama_b4": 4, "long_llama_b1": 8, "ragged_1p96": 2, "window_split_qwen3_8b": 2,
+                   "mean_qwen3_8b": 2}   # name: cache copies (their total above the 256 MB MALL)
+
+
+def other_workloads(dq, torch, workloads, only=None) -> dict:
+    return {name: config_measurement(dq, torch, workloads, name, copies=c)
+            for name, c in OTHER_WORKLOADS.items() if only is None or name == only}
 
 
 def token_attention_time(dq, torch, workloads, tables, name: str, copies: int, reps: int):
@@ -663,7 +662,9 @@ def main() -> int:
         print(json.dumps({"token_format": token_measurement(dq, torch, workloads)}), flush=True)
         return 0
     if args.section == "workloads":
-        print(json.dumps({"other_workloads": other_workloads(dq, torch, workloads)}), flush=True)
+        # --workload names one of them alone (the default runs all)
+        only = args.workload if args.workload in OTHER_WORKLOADS else None
+        print(json.dumps({"other_workloads": other_workloads(dq, torch, workloads, only)}), flush=True)
         return 0
     if args.section == "bf16":
         print(json.dumps({"bf16_reference": bf16_measurement(dq, torch, workloads, args.workload, copies=2,

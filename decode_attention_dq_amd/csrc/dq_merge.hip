@@ -194,7 +194,10 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(MergeArgs a, int rows) 
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int rows, bool rotated, hipStream_t s) {
-    if (a.slot_count <= 64 && !(rows < 1024 && a.slot_count > 32)) {
+    // partials a row can hold: the splits, plus the window's (slot_count also
+    // counts a window slot when there is no window)
+    const int slots = a.slot_count - 1 + (a.window_slot >= 0 ? 1 : 0);
+    if (slots <= 64 && !(rows < 1024 && slots > 32)) {
         const dim3 grid((unsigned)((rows + 3) / 4));
         if (rotated)
             hipLaunchKernelGGL((merge_rows_kernel<true>), grid, dim3(256), 0, s, a, rows);
@@ -202,8 +205,8 @@ hipError_t launch_merge(const MergeArgs& a, int rows, bool rotated, hipStream_t 
             hipLaunchKernelGGL((merge_rows_kernel<false>), grid, dim3(256), 0, s, a, rows);
         return hipGetLastError();
     }
-    const bool wide = rows < 1024 && a.slot_count > 32;
-    if (wide && a.slot_count <= 128) {
+    const bool wide = rows < 1024 && slots > 32;
+    if (wide && slots <= 128) {
         if (rotated)
             hipLaunchKernelGGL((merge_wide_kernel<true>), dim3(rows), dim3(64 * 16), 0, s, a);
         else
