@@ -253,10 +253,12 @@ namespace dq {
 // Split rule. Work-groups are taken longest job first, so a launch ends well
 // when its last jobs are short ones: 1536-token splits (whose last split per
 // sequence is shorter) when they give at least four work-groups per slot (4
-// resident work-groups on each of 256 CUs); otherwise 2048-token splits, so
-// that a launch of about one round still fills every slot with equal jobs;
-// and shorter splits, down to one 256-token tile, when even that would leave
-// fewer than 1024 work-groups.
+// resident work-groups on each of 256 CUs). Otherwise 2048-token splits fill
+// every slot with equal jobs; when those make fewer than two rounds, 1024-token
+// splits instead (two rounds of 4-tile waves finish sooner than one of 8-tile
+// waves, whose key-only first and value-only last passes all run at once); and
+// shorter splits, down to one 256-token tile, when even 2048-token splits would
+// leave fewer than 1024 work-groups.
 int choose_splits(int batch, int num_kv_heads, int max_context) {
     const long units = (long)batch * num_kv_heads;
     const int tile = 256, slots = 1024;
@@ -264,7 +266,10 @@ int choose_splits(int batch, int num_kv_heads, int max_context) {
     long s = (max_context + 1535) / 1536;
     if (units * s < 4L * slots) {
         s = (max_context + 2047) / 2048;
-        if (units * s < slots) s = (slots + units - 1) / units;
+        if (units * s < slots)
+            s = (slots + units - 1) / units;
+        else if (units * s < 2L * slots)
+            s = (max_context + 1023) / 1024;
     }
     if (s > max_by_len) s = max_by_len;
     if (s < 1) s = 1;

@@ -111,7 +111,9 @@ def test_workspace_size(dq):
 @pytest.mark.parametrize("B,hkv,ctx,splits", [
     (128, 8, 8192, 6),      # >= 4 work-groups per slot: 1536-token splits
     (64, 8, 16384, 11),
-    (4, 8, 65536, 32),      # about one round: 2048-token splits, 1024 work-groups
+    (4, 8, 65536, 64),      # 2048-token splits would make one round: 1024-token splits, two rounds
+    (16, 8, 16384, 16),     # the same at 16 x 16K
+    (8, 8, 65536, 32),      # two rounds of 2048-token splits
     (1, 8, 131072, 128),    # fewer: shorter splits up to 1024 work-groups
     (1, 1, 300, 2),         # never below one 256-token tile
 ])
