@@ -312,7 +312,6 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
             ev.append(step(l))
     torch.cuda.synchronize()
     attn = float(np.mean([e0.elapsed_time(e1) for _, e0, e1 in ev])) / 1e3
-    full = float(np.mean([a0.elapsed_time(e1) for a0, _, e1 in ev])) / 1e3
     nbytes = algorithmic_bytes(w, lens, wl)
     res = {"batch": B, "context": "ragged %d..%d" % w.ragged if append else w.context,
            "container_bytes": [w.container, w.cv], "page_size": P, "cache_copies": copies,
@@ -321,11 +320,11 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
            "us_per_call": round(attn * 1e6, 2), "GBps": round(nbytes / attn / 1e9, 2),
            "hbm_frac": round(nbytes / attn / 1e9 / HBM_PEAK_GBS, 4), "device_errors": int(err.item())}
     if append:
-        res["us_per_step_with_append"] = round(full * 1e6, 2)
         res["appended_streams"] = 2 * B * hkv
         # what the cache write of each sequence's newest token adds to a decode
         # step: runs of back-to-back steps with and without it, each run between
-        # one pair of events (no markers between the calls)
+        # one pair of events (no markers between the calls; a marker between the
+        # write and the attention call would add its own gap)
         def run(with_append: bool) -> float:
             n = reps * copies
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -343,6 +342,8 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
             return e0.elapsed_time(e1) * 1e3 / n
         plain = min(run(False) for _ in range(3))
         both = min(run(True) for _ in range(3))
+        res["us_per_step_without_append"] = round(plain, 2)
+        res["us_per_step_with_append"] = round(both, 2)
         res["append_encode_us"] = round(both - plain, 2)
     return res
 
