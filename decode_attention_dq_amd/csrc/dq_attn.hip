@@ -199,11 +199,27 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const uint32_t oW = kOffWaves + (uint32_t)wave * wave_bytes(a.ck, a.cv);
     const uint32_t oKc = oW, oVc = oW + kcB, oVt = oVc + vcB, oWl = oVt;
 
+    // Issue priority. A SIMD issues to its oldest ready wave first, so in a
+    // launch of about one round the work-groups dispatched first run ahead and
+    // each CU ends with its later ones at falling occupancy. Waves start at the
+    // highest priority and step down after each of their first three tiles, so
+    // the waves that are behind take the issue slots.
+    __builtin_amdgcn_s_setprio(3);
+
     // ---- prologue: tables, zero regions, rotated queries
     {
-        uint32_t* tab = (uint32_t*)lds;
-        for (int i = tid; i < 2 * kTableSlots; i += kThreads) tab[i] = a.wide_k[i];
-        for (int i = tid; i < kTableSlots; i += kThreads) tab[2 * kTableSlots + i] = a.entries[kTableSlots + i];
+        // 768 16-byte units straight into LDS (no registers): units 0..511 the
+        // two-dword key table, 512..767 the value table; each wave instruction
+        // fills 1 KB
+        static_assert(kOffTabK == 0 && kOffTabV == 8192 && kThreads == 256, "table units map to LDS 16 u");
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int u = tid + k * kThreads;
+            const uint8_t* src = u < 512 ? (const uint8_t*)a.wide_k + 16 * u
+                                         : (const uint8_t*)(a.entries + kTableSlots) + 16 * (u - 512);
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(lds + 16 * (uint32_t)(k * kThreads + wave * 64)),
+                                             16, 0, 0);
+        }
         uint32_t* z = (uint32_t*)(lds + kOffZero);
         if (tid < 64) z[tid] = 0u;
     }
@@ -231,6 +247,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
             ((float*)(lds + kOffKappa))[wave] =
                 __builtin_amdgcn_ldexpf(a.softmax_scale * kLog2e * a.step_k / (float)kHeadDim, e);
     }
+    stage_wait();   // the table copies
     __syncthreads();
 
     const uint32_t lds0 = (uint32_t)(size_t)lds_base;      // absolute LDS address of the dynamic allocation
@@ -493,6 +510,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     }
     // Tiles are staged right after the pass that frees their region, and waited
     // for just before the pass that decodes them.
+    int done = 0;   // tiles finished by this wave (for the issue priority)
     for (; t < end; t += kStep) {
         // values of tile t, interleaved with the keys of tile t + kStep
         const int tn = t + kStep;
@@ -542,6 +560,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         }
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) pgn[gi] = pgnn[gi];
+        ++done;
+        if (done == 1) __builtin_amdgcn_s_setprio(2);
+        else if (done == 2) __builtin_amdgcn_s_setprio(1);
+        else if (done == 3) __builtin_amdgcn_s_setprio(0);
     }
     stage_wait();   // no copy into this wave's region may still be in flight
     if (bad && a.err_word) atomicOr(a.err_word, DQ_DEVERR_DECODE);
