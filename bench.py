@@ -279,17 +279,12 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
     ws = torch.empty(dq.dq_workspace_size(B, hq, hkv, w.context), dtype=torch.uint8, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    ev = []
 
-    def step(l):
+    def call(l, with_append=False):
         c = caches[l]
-        if append:
-            a0 = torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
+        if with_append:
             dq.dq_encode_kv(tables, new_k[l], new_v[l], new_slots, c.k_cache, c.v_cache, c.k_norm, c.v_norm, P,
                             err_word=err, stream=stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
         if w.means:
             dq.dq_decode_attention_ext(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
                                        c.context_lens, hkv, P, w.context, out, ws, k_mean=c.k_mean,
@@ -301,50 +296,46 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
         else:
             dq.dq_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
                                    c.context_lens, hkv, P, w.context, out, ws, err_word=err, stream=stream)
+
+    # Runs of reps x copies back-to-back calls, each run between one pair of
+    # events (as the headline's timed region; an event pair around every call
+    # adds its own gaps); the median run.
+    def run(with_append=False, scale=1) -> float:
+        n = reps * copies * scale
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            call(i % copies, with_append)
         e1.record(stream)
-        return (a0 if append else e0, e0, e1)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
 
     for l in range(copies):
-        step(l)
+        call(l)
     torch.cuda.synchronize()
-    for _ in range(reps):
-        for l in range(copies):
-            ev.append(step(l))
-    torch.cuda.synchronize()
-    attn = float(np.mean([e0.elapsed_time(e1) for _, e0, e1 in ev])) / 1e3
+    attn = float(np.median([run() for _ in range(3)]))
     nbytes = algorithmic_bytes(w, lens, wl)
     res = {"batch": B, "context": "ragged %d..%d" % w.ragged if append else w.context,
            "container_bytes": [w.container, w.cv], "page_size": P, "cache_copies": copies,
            **({"bf16_window": w.window} if w.window else {}),
            **({"key_block_means": True} if w.means else {}),
            "us_per_call": round(attn * 1e6, 2), "GBps": round(nbytes / attn / 1e9, 2),
-           "hbm_frac": round(nbytes / attn / 1e9 / HBM_PEAK_GBS, 4), "device_errors": int(err.item())}
+           "hbm_frac": round(nbytes / attn / 1e9 / HBM_PEAK_GBS, 4)}
     if append:
         res["appended_streams"] = 2 * B * hkv
         # what the cache write of each sequence's newest token adds to a decode
-        # step: runs of back-to-back steps with and without it, each run between
-        # one pair of events (no markers between the calls; a marker between the
-        # write and the attention call would add its own gap)
-        def run(with_append: bool) -> float:
-            n = reps * copies
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(n):
-                l = i % copies
-                c = caches[l]
-                if with_append:
-                    dq.dq_encode_kv(tables, new_k[l], new_v[l], new_slots, c.k_cache, c.v_cache, c.k_norm, c.v_norm,
-                                    P, err_word=err, stream=stream)
-                dq.dq_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
-                                       c.context_lens, hkv, P, w.context, out, ws, err_word=err, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / n
-        plain = min(run(False) for _ in range(3))
-        both = min(run(True) for _ in range(3))
+        # step: runs with and without it, timed the same way, four times longer
+        # and alternated (a difference of two runs is what is reported)
+        plain_runs, both_runs = [], []
+        for _ in range(5):
+            plain_runs.append(run(False, 4))
+            both_runs.append(run(True, 4))
+        plain = float(np.median(plain_runs)) * 1e6
+        both = float(np.median(both_runs)) * 1e6
         res["us_per_step_without_append"] = round(plain, 2)
         res["us_per_step_with_append"] = round(both, 2)
         res["append_encode_us"] = round(both - plain, 2)
+    res["device_errors"] = int(err.item())
     return res
 
 
@@ -370,24 +361,32 @@ def token_attention_time(dq, torch, workloads, tables, name: str, copies: int, r
     ws = torch.empty(dq.dq_token_workspace_size(B, hq, w.context), dtype=torch.uint8, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    ev = []
-    for it in range(reps + 2):
-        for l in range(copies):
-            c = caches[l]
-            kw = {}
-            if w.window:
-                kw.update(window_k=c.win_k, window_v=c.win_v, window_lens=c.win_lens)
-            if w.means:
-                kw.update(k_mean=c.k_mean, k_mean_scale=c.k_mean_scale)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            dq.dq_token_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
-                                         c.context_lens, P, w.context, out, ws, err_word=err, stream=stream, **kw)
-            e1.record(stream)
-            if it >= 2:
-                ev.append((e0, e1))
+
+    def call(l):
+        c = caches[l]
+        kw = {}
+        if w.window:
+            kw.update(window_k=c.win_k, window_v=c.win_v, window_lens=c.win_lens)
+        if w.means:
+            kw.update(k_mean=c.k_mean, k_mean_scale=c.k_mean_scale)
+        dq.dq_token_decode_attention(tables, qs[l], c.k_cache, c.v_cache, c.k_norm, c.v_norm, c.block_table,
+                                     c.context_lens, P, w.context, out, ws, err_word=err, stream=stream, **kw)
+
+    # runs of reps x copies back-to-back calls, each between one pair of events; the median run
+    def run() -> float:
+        n = reps * copies
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            call(i % copies)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    for l in range(copies):
+        call(l)
     torch.cuda.synchronize()
-    t = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    t = float(np.median([run() for _ in range(3)]))
     ntok = int(np.sum(caches[0].lens))
     nbytes = ntok * (w.container + 4 + w.cv + 4)
     if w.means:
@@ -703,28 +702,31 @@ def main() -> int:
             call(l)
     torch.cuda.synchronize()
 
-    n_calls = args.steps * w.layers
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_calls)]
+    # the timed region: exactly K steps of one call per layer, back to back
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_all0.record(stream)
-    i = 0
     for _ in range(args.steps):
         for l in range(w.layers):
-            ev[i][0].record(stream)
             call(l)
-            ev[i][1].record(stream)
-            i += 1
     t_all1.record(stream)
     torch.cuda.synchronize()
     if int(err.item()) != 0:
         print("[bench] device integrity error", file=sys.stderr)
         return 1
     ms_total = t_all0.elapsed_time(t_all1)
-    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ms_per_step = ms_total / args.steps
-    per_call_s = float(call_ms.mean()) / 1e3
+    per_call_s = ms_per_step / 1e3 / w.layers
+    # the spread of single calls, from one more step with an event pair around each
+    # call (after the timed region; the markers add their own gaps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.layers)]
+    for l in range(w.layers):
+        ev[l][0].record(stream)
+        call(l)
+        ev[l][1].record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
     nbytes = algorithmic_bytes(w, lens)
     symbols = int(np.sum(lens)) * hkv * 128 * 2
