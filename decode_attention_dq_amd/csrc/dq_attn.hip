@@ -96,49 +96,19 @@ __device__ __forceinline__ void rows_from_pages(size_t* row, const int* pg, int 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // Copy the containers of the tile's 4 token groups into LDS at `dst`, token t
-// at dst + t * lds_stride(C). Lane u (and u + 64 when C > 64) moves 16-byte
-// unit u of every group: a load from the group's uniform base plus 16u, and an
-// LDS store at a per-lane offset. With a padded stride (C a multiple of 8) a
-// unit is stored as two 8-byte halves, each inside one container; the token
-// of byte b of a group is (b * magic) >> 21, exact for b < 2^11 with
-// magic = ceil(2^21 / C).
-template <bool PADDED>
-__device__ __forceinline__ void stage_unit(uint8_t* lds, uint32_t dst, const uint8_t* __restrict__ cache, int C,
-                                           uint32_t magic, const size_t* row, uint32_t u) {
-    const uint32_t S = lds_stride(C);
-    asm volatile("" : "+v"(u));   // recomputed per tile: hoisted, the offsets would stay live through the pass
-    uint32_t o0 = 16u * u, o1 = 0;
-    if (PADDED) {
-        const uint32_t b0 = 16u * u, b1 = b0 + 8u;
-        const uint32_t t0 = __umul24(b0, magic) >> 21, t1 = __umul24(b1, magic) >> 21;
-        o0 = t0 * S + (b0 - t0 * (uint32_t)C);
-        o1 = t1 * S + (b1 - t1 * (uint32_t)C);
-    }
-    u32x4 v[4];
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-        const uint8_t* gb = cache + row[gi] * (size_t)C;   // uniform
-        v[gi] = *(const u32x4*)(gb + 16u * u);
-    }
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-        const uint32_t base = dst + (uint32_t)gi * 16u * S;
-        if (!PADDED) {
-            *(u32x4*)(lds + base + o0) = v[gi];
-        } else {
-            *(uint32_t*)(lds + base + o0) = v[gi][0];
-            *(uint32_t*)(lds + base + o0 + 4u) = v[gi][1];
-            *(uint32_t*)(lds + base + o1) = v[gi][2];
-            *(uint32_t*)(lds + base + o1 + 4u) = v[gi][3];
-        }
-    }
-}
-
-// Unpadded layout: each 16-byte unit goes from HBM straight into LDS (the
-// direct-to-LDS load writes lane u's 16 bytes at the uniform LDS address plus
-// 16u), with no register round trip and no wait here: the copy completes
-// behind the following work and is waited for (vmcnt) before the tile is read.
-// The padded layout splits units into 8-byte halves and goes through registers.
+// at dst + t * lds_stride(C), straight from HBM into LDS (a direct-to-LDS load
+// writes lane u's bytes at the uniform LDS address plus u times the unit size),
+// with no register round trip and no wait here: the copy completes behind the
+// following work and is waited for (vmcnt) before the tile is read.
+// Unpadded layout: lane u (and u + 64 when C > 64) moves 16-byte unit u of
+// every group.
+// Padded layout (C a multiple of 8; stride S = C + 4, an odd dword count, so
+// that the lanes' window reads fall in distinct banks): the S/4 words of each
+// padded row come in 4-byte units. Word k of a group's padded rows is word
+// k - t (S/4) of token t = k / (S/4) (t = (k * magic) >> 16, exact for these k
+// with magic = ceil(2^16 / (S/4))); the row's last word, the padding, repeats
+// the container's last dword. The loads go through a buffer resource over the
+// group's 16 C bytes, so a lane's source is one 32-bit offset.
 template <bool PADDED>
 __device__ __forceinline__ void stage_tile(uint8_t* lds, uint32_t dst, const uint8_t* __restrict__ cache,
                                            int C, uint32_t magic, const size_t* row, int lane) {
@@ -154,8 +124,26 @@ __device__ __forceinline__ void stage_tile(uint8_t* lds, uint32_t dst, const uin
         }
         return;
     }
-    if (lane < C) stage_unit<PADDED>(lds, dst, cache, C, magic, row, (uint32_t)lane);
-    if (C > 64 && lane + 64 < C) stage_unit<PADDED>(lds, dst, cache, C, magic, row, (uint32_t)lane + 64u);
+    const uint32_t n = (uint32_t)C / 4u + 1u;   // words per padded row
+    const uint32_t words = 16u * n;             // per group
+    __amdgpu_buffer_rsrc_t rs[4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+        rs[gi] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cache + row[gi] * (size_t)C), (short)0,
+                                                   16 * C, 0x00020000);
+    for (uint32_t i = 0; 64u * i < words; ++i) {
+        uint32_t k = 64u * i + (uint32_t)lane;
+        asm volatile("" : "+v"(k));   // recomputed per tile: hoisted, the offsets would stay live through the pass
+        const uint32_t t = __umul24(k, magic) >> 16;
+        const uint32_t j = min(k - __umul24(t, n), n - 2u);
+        const uint32_t off = __umul24(t, (uint32_t)C) + 4u * j;
+        if (k < words) {
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs[gi], (lds_ptr)(lds + dst + (uint32_t)gi * 16u * (n * 4u) + 256u * i), 4, off, 0, 0, 0);
+        }
+    }
 }
 
 // Waits for this wave's outstanding global loads, the direct-to-LDS copies
@@ -169,7 +157,7 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 struct AttnLaunch {
     AttnArgs a;
     int log2p;
-    uint32_t magic_k, magic_v;   // ceil(2^21 / C) for the padded staging
+    uint32_t magic_k, magic_v;   // ceil(2^16 / (C / 4 + 1)) for the padded staging
 };
 
 // PAD_K / PAD_V: containers laid out at the padded LDS stride; MEANS: key
@@ -684,8 +672,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     L.log2p = 31 - __builtin_clz((unsigned)a.page_size);
     if ((1 << L.log2p) != a.page_size) return hipErrorInvalidValue;
     const size_t lds = kOffWaves + (size_t)kWaves * wave_bytes(a.ck, a.cv);
-    L.magic_k = ((1u << 21) + (uint32_t)a.ck - 1u) / (uint32_t)a.ck;
-    L.magic_v = ((1u << 21) + (uint32_t)a.cv - 1u) / (uint32_t)a.cv;
+    L.magic_k = ((1u << 16) + (uint32_t)a.ck / 4u) / ((uint32_t)a.ck / 4u + 1u);
+    L.magic_v = ((1u << 16) + (uint32_t)a.cv / 4u) / ((uint32_t)a.cv / 4u + 1u);
     const bool pk = lds_stride(a.ck) != (uint32_t)a.ck, pv = lds_stride(a.cv) != (uint32_t)a.cv;
     const bool mk = a.k_mean != nullptr;
     const int which = (mk ? 4 : 0) + (pk ? 2 : 0) + (pv ? 1 : 0);
