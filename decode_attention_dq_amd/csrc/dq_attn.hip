@@ -401,12 +401,15 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     // one 128-token block).
     // mean_load issues the loads (the lane's two INT8 means packed in one
     // register, and the block's scale) well before mean_finish uses them.
-    auto mean_load = [&](int t0, uint32_t& mq, float& s16) {
+    // pg_t0 is the page id of token t0 (already loaded with the tile's pages):
+    // with pages of 128 tokens or more the block lies in that page, so only
+    // smaller pages read the block table here (a dependent load).
+    auto mean_load = [&](int t0, int pg_t0, uint32_t& mq, float& s16) {
         mq = 0;
         s16 = 0.0f;
         if (!MEANS) return;
         const int tb = t0 & ~(kMeanBlock - 1);
-        const int page = bt_row[tb >> log2p];
+        const int page = P >= kMeanBlock ? __builtin_amdgcn_readfirstlane(pg_t0) : bt_row[tb >> log2p];
         const size_t mrow = ((size_t)page * hkv + g) * (size_t)mean_rows_per_page(P) + (size_t)((tb & (P - 1)) >> 7);
         s16 = f16_to_f32(a.k_mean_scale[mrow]);
         const uint8_t* mb = (const uint8_t*)a.k_mean + mrow * kHeadDim;
@@ -457,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         if (t + kStep < end) tile_pages(pgn, bt_row, log2p, t + kStep, T);
         float cm[4], ms;
         uint32_t mq, rk, rv;
-        mean_load(t, mq, ms);
+        mean_load(t, pg0[0], mq, ms);
         load_norms(t, row, rk, rv);
         wave_lds_sync();
         const bool valid = t + lane < T;
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         int pgnn[4] = {0, 0, 0, 0};
         stage_wait();   // this pass's key tile tn and value tile t
         if (has_next) {
-            mean_load(tn, mq_n, ms_n);
+            mean_load(tn, pgn[0], mq_n, ms_n);
             size_t row[4];
             rows_from_pages(row, pgn, P, hkv, g, tn, T);
             load_norms(tn, row, rk_n, rv_n);
