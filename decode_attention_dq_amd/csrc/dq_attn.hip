@@ -244,7 +244,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const uint32_t pk = (uint32_t)a.pk, pv = (uint32_t)a.pv;
     float kap[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) kap[r] = r < G ? ((const float*)(lds + kOffKappa))[r] : 0.0f;
+    for (int r = 0; r < 4; ++r)   // uniform: kept in scalar registers
+        kap[r] = r < G ? __int_as_float(__builtin_amdgcn_readfirstlane(((const int*)(lds + kOffKappa))[r])) : 0.0f;
 
     // MFMA operand addresses (bytes into LDS)
     const int r16 = lane & 15, grp = lane >> 4;
