@@ -310,9 +310,12 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
                 const int hl = 4 * g + hh;
                 const float qm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qmu), hl));
                 const float L = valid ? (ok * S.qsum[g][hh] + (sk * dk[hh] + qm)) * cs : -INFINITY;
-                const float mt = tok_wave_max(L);
                 const float mo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), hl));
-                const float mn = fmaxf(mo, mt);
+                // the running maximum moves only when a logit of the tile exceeds
+                // it (after the first tiles, rarely); otherwise the maximum
+                // reduction is skipped, and the result is the same
+                float mn = mo;
+                if (__builtin_amdgcn_ballot_w64(L > mo)) mn = fmaxf(mo, tok_wave_max(L));
                 // both arguments are <= 0 (or -inf): v_exp_f32 as it stands
                 const float fac = __builtin_amdgcn_exp2f(mo - mn);
                 const float p = valid ? __builtin_amdgcn_exp2f(L - mn) : 0.0f;
