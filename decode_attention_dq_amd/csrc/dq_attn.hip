@@ -34,16 +34,16 @@ constexpr int kRowH = 72;                 // fp16 per LDS row of the level / wei
 constexpr int kRowB = kRowH * 2;          // bytes
 constexpr int kPad = 144;                 // bytes after a container tile of the symbol-decode hook: lane 63 of a
                                           // corrupt tile reads < 63C + 132
-constexpr int kVtRow = 32;                // bytes per token row of the V level tile (16 fp16 channels)
-// LDS of attn_kernel. The key table is held in two-dword form (8 KB), the
-// value table in one-dword form (4 KB): that keeps a work-group at 40 KB, four
-// per CU, while the key chain's decode step needs no field extraction.
+constexpr int kVtRow = 16;                // bytes per token row of the V level tile (8 fp16 channels)
+// LDS of attn_kernel. Both tables are held in two-dword form (8 KB each), so
+// that neither chain's decode step needs a field extraction; with a value level
+// tile of 8 channels a work-group stays at 40 KB, four per CU.
 constexpr uint32_t kOffTabK = 0;          // [1024][2] two-dword key entries
-constexpr uint32_t kOffTabV = 8192;       // [1024] value entries
-constexpr uint32_t kOffQt = 12288;        // [4][128] fp16 rotated queries
-constexpr uint32_t kOffZero = 13312;      // 256 zero bytes: A operand of rows without a head
-constexpr uint32_t kOffKappa = 13568;     // [4] floats
-constexpr uint32_t kOffWaves = 13584;
+constexpr uint32_t kOffTabV = 8192;       // [1024][2] two-dword value entries
+constexpr uint32_t kOffQt = 16384;        // [4][128] fp16 rotated queries
+constexpr uint32_t kOffZero = 17408;      // 256 zero bytes: A operand of rows without a head
+constexpr uint32_t kOffKappa = 17664;     // [4] floats
+constexpr uint32_t kOffWaves = 17680;
 
 __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
 
@@ -53,7 +53,7 @@ __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15
 // row is written). No padding separates the regions: the byte window of a
 // corrupt stream can read up to 138 - C bytes past its tile, which stays
 // inside the next region of the same wave (the value container tile, or the
-// 2048-byte level tile).
+// 1024-byte level tile).
 // LDS stride of one token's container: C itself unless C is a multiple of 8,
 // in which case C + 4 keeps the stride an odd number of dwords, so that the
 // lanes' byte-window reads spread over the LDS banks (a stride of 8 dwords
@@ -196,15 +196,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
 
     // ---- prologue: tables, zero regions, rotated queries
     {
-        // 768 16-byte units straight into LDS (no registers): units 0..511 the
-        // two-dword key table, 512..767 the value table; each wave instruction
-        // fills 1 KB
+        // 1024 16-byte units straight into LDS (no registers): the two-dword key
+        // table, then the two-dword value table, as they lie in memory; each
+        // wave instruction fills 1 KB
         static_assert(kOffTabK == 0 && kOffTabV == 8192 && kThreads == 256, "table units map to LDS 16 u");
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
+        for (int k = 0; k < 4; ++k) {
             const int u = tid + k * kThreads;
-            const uint8_t* src = u < 512 ? (const uint8_t*)a.wide_k + 16 * u
-                                         : (const uint8_t*)(a.entries + kTableSlots) + 16 * (u - 512);
+            const uint8_t* src = (const uint8_t*)a.wide_k + 16 * u;
             __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(lds + 16 * (uint32_t)(k * kThreads + wave * 64)),
                                              16, 0, 0);
         }
@@ -250,7 +249,15 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     // MFMA operand addresses (bytes into LDS)
     const int r16 = lane & 15, grp = lane >> 4;
     const uint32_t aq_off = (grp == (r16 >> 2) && (r16 & 3) < G) ? kOffQt + (uint32_t)(r16 & 3) * 256u : kOffZero;
-    const uint32_t ap_off = r16 < G ? oWl + (uint32_t)r16 * kRowB + (uint32_t)grp * 16u : kOffZero;
+    // p.v A operand: the 16 rows are four groups of 4 heads, group 2c + h for
+    // the value channels of half c of a 16-channel block and the tokens of half
+    // h of the tile (row 4(2c + h) + r: head r's weights of tokens 32h + k);
+    // ap_off addresses the lane's row for its group, ap_hi says which channel
+    // half that group serves
+    const bool ap_hi = (r16 >> 3) != 0;
+    const uint32_t ap_off = (r16 & 3) < G ? oWl + (uint32_t)(r16 & 3) * kRowB + (uint32_t)((r16 >> 2) & 1) * 64u +
+                                                (uint32_t)grp * 16u
+                                          : kOffZero;
 
     const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages_per_seq;
     const int P = a.page_size, log2p = L.log2p, hkv = a.num_kv_heads;
@@ -264,22 +271,32 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     for (int i = 0; i < 8; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
     uint32_t bad = 0;
 
-    // V level tile: row = token (this lane), 16 channels of fp16 = 32 bytes
-    const uint32_t vt_row = oVt + (uint32_t)lane * kVtRow;
-    // transpose-load sources for the p.v B operand: lane s of a 16-lane group
-    // points at 4 channels (8 bytes) of token 8*group + s/4 (+4 for the
-    // second load), so that result lane n gets channel n of 4 tokens
-    const uint32_t tr0 = oVt + (uint32_t)(8 * grp + (r16 >> 2)) * kVtRow + 8u * (uint32_t)(r16 & 3);
+    // V level tile: 8 channels of fp16 (16 bytes) per token, token t in row t
+    // for the first half of the tile and in row t ^ 8 for the second, so that
+    // the two halves' rows read by one 16-lane group of a transposed load lie
+    // 32 banks apart
+    auto vt_row_of = [](int t) { return (uint32_t)(t < 32 ? t : t ^ 8); };
+    const uint32_t vt_row = oVt + vt_row_of(lane) * kVtRow;
+    // transpose-load sources for the p.v B operand, whose 16 columns are the
+    // tile's 8 channels for the tokens of half 0 (columns 0..7) and of half 1
+    // (8..15): lane s of a 16-lane group points at 4 channels (8 bytes, half
+    // s & 1 of the row) of token 8*group + 32*((s & 3) >> 1) + s/4 (+4 tokens,
+    // 4 rows, for the second load), so that result lane n gets channel n % 8 of
+    // 4 tokens of half n / 8
+    const uint32_t tr0 = oVt + vt_row_of(8 * grp + 32 * ((r16 & 3) >> 1) + (r16 >> 2)) * kVtRow +
+                         8u * (uint32_t)(r16 & 1);
 
     // One pass over the 128 channels of a key tile (do_k) and/or a value tile
     // (do_v): two independent decode chains per lane, the q.k MFMA after each
     // 8 key channels, the p.v MFMAs after each 16 value channels.
     auto pass = [&](bool do_k, bool do_v, RansLane& kr, RansLane& vr, float4v& dk) {
-        // the weights are the same A operand for every 16 channels of the tile
+        // the weights are the same A operand for every 16 channels of the tile:
+        // for channel half c, the lane's row, or zeros when its group serves
+        // the other half
         half8 av[2];
         if (do_v) {
-            av[0] = *(const half8*)(lds + ap_off);
-            av[1] = *(const half8*)(lds + ap_off + 64u);
+            av[0] = *(const half8*)(lds + (ap_hi ? kOffZero : ap_off));
+            av[1] = *(const half8*)(lds + (ap_hi ? ap_off : kOffZero));
         }
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
@@ -295,18 +312,23 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
                     if (do_k && do_v) {
                         // both table reads in flight before either chain advances
                         const u32x2 wk = rans_lookup_wide(kr, tabK, maskK);
-                        ev[jj] = rans_lookup(vr, tabV, maskV);
+                        const u32x2 wv = rans_lookup_wide(vr, tabV, maskV);
                         __builtin_amdgcn_sched_barrier(0);
                         rans_advance_wide(kr, wk, pk);
                         ek[jj] = wk.x;
-                        rans_advance(vr, ev[jj], pv);
+                        rans_advance_wide(vr, wv, pv);
+                        ev[jj] = wv.x;
                     } else {
                         if (do_k) {
                             const u32x2 wk = rans_lookup_wide(kr, tabK, maskK);
                             rans_advance_wide(kr, wk, pk);
                             ek[jj] = wk.x;
                         }
-                        if (do_v) ev[jj] = rans_dec_step(vr, tabV, maskV, pv);
+                        if (do_v) {
+                            const u32x2 wv = rans_lookup_wide(vr, tabV, maskV);
+                            rans_advance_wide(vr, wv, pv);
+                            ev[jj] = wv.x;
+                        }
                     }
                 }
                 if (do_k) {
@@ -322,25 +344,36 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
                     dk = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, __builtin_bit_cast(half8, bw), dk, 0, 0, 0);
                 }
                 if (do_v) {
+                    // the 8 channels of this half into the level tile; one MFMA
+                    // per half covers all 64 tokens: B column n takes channel
+                    // n % 8 of the tokens of half n / 8, and the rows of the
+                    // groups of channel half hh pick the matching token half.
+                    // Half 0's operand is read only after half 1's decode,
+                    // just before half 1's levels overwrite the tile (a wave's
+                    // LDS operations complete in order), and both MFMAs follow.
                     u32x4 vw;
-                    vw[0] = pack_levels(ev[0], ev[1]);
-                    vw[1] = pack_levels(ev[2], ev[3]);
-                    vw[2] = pack_levels(ev[4], ev[5]);
-                    vw[3] = pack_levels(ev[6], ev[7]);
-                    *(u32x4*)(lds + vt_row + 16u * hh) = vw;
+                    vw[0] = pack_levels_wide(ev[0], ev[1]);
+                    vw[1] = pack_levels_wide(ev[2], ev[3]);
+                    vw[2] = pack_levels_wide(ev[4], ev[5]);
+                    vw[3] = pack_levels_wide(ev[6], ev[7]);
+                    if (hh == 0) {
+                        *(u32x4*)(lds + vt_row) = vw;
+                    } else {
+                        wave_lds_sync();
+                        const v4i16 lo0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_base + tr0));
+                        const v4i16 hi0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_base + tr0 + 4u * kVtRow));
+                        wave_lds_sync();
+                        *(u32x4*)(lds + vt_row) = vw;
+                        wave_lds_sync();
+                        const v4i16 lo1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_base + tr0));
+                        const v4i16 hi1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_base + tr0 + 4u * kVtRow));
+                        const half8 b0 = __builtin_bit_cast(half8, i16x8{lo0[0], lo0[1], lo0[2], lo0[3], hi0[0], hi0[1], hi0[2], hi0[3]});
+                        const half8 b1 = __builtin_bit_cast(half8, i16x8{lo1[0], lo1[1], lo1[2], lo1[3], hi1[0], hi1[1], hi1[2], hi1[3]});
+                        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[0], b0, acc[blk], 0, 0, 0);
+                        acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[1], b1, acc[blk], 0, 0, 0);
+                        wave_lds_sync();
+                    }
                 }
-            }
-            if (do_v) {
-                wave_lds_sync();
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const uint32_t src = tr0 + (uint32_t)hf * 32u * kVtRow;
-                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_base + src));
-                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds_base + src + 4u * kVtRow));
-                    const half8 bv = __builtin_bit_cast(half8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[hf], bv, acc[blk], 0, 0, 0);
-                }
-                wave_lds_sync();
             }
         }
     };
@@ -566,12 +599,17 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     for (int r = 0; r < 4; ++r) lsum[r] = wave_sum(l_lane[r]);
     __syncthreads();   // every wave is done with its LDS tiles
     float* mg = (float*)(lds + oW);   // reuse this wave's own region: [0..3] m, [4..7] l, [8] e, [16..] acc[4][128]
-    if (lane < 16) {
+    // acc[i][r] of lane l is row 4(l/16) + r, column l % 16 of block i's p.v
+    // tile: group l/16 = 2c + h holds channel half c summed over the tokens of
+    // half h, in the columns of that token half. Channel 16i + 8c + e is then
+    // lane 32c + e (h = 0, column e) plus lane 32c + 24 + e (h = 1, column 8 + e).
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mg[16 + r * kHeadDim + i * 16 + lane] = acc[i][r];
-    }
+        for (int r = 0; r < 4; ++r) {
+            const float o = __shfl(acc[i][r], (lane + 24) & 63);
+            if ((lane & 31) < 8) mg[16 + r * kHeadDim + i * 16 + 8 * (lane >> 5) + (lane & 7)] = acc[i][r] + o;
+        }
     if (lane == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) { mg[r] = m_run[r]; mg[4 + r] = lsum[r]; }
