@@ -43,7 +43,8 @@ constexpr uint32_t kOffTabV = 8192;       // [1024][2] two-dword value entries
 constexpr uint32_t kOffQt = 16384;        // [4][128] fp16 rotated queries
 constexpr uint32_t kOffZero = 17408;      // 256 zero bytes: A operand of rows without a head
 constexpr uint32_t kOffKappa = 17664;     // [4] floats
-constexpr uint32_t kOffWaves = 17680;
+constexpr uint32_t kOffLsum = 17680;      // [4 waves][4] floats: each wave's running sums of the weights per head
+constexpr uint32_t kOffWaves = 17744;
 
 __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
 
@@ -81,6 +82,13 @@ __device__ __forceinline__ void tile_pages(int* pg, const int32_t* __restrict__ 
         pg[gi] = bt_row[(gi == 0 || tok < T ? tok : t0) >> log2p];
     }
 }
+// The same page ids held in one register: lane gi (gi < 4) loads group gi's;
+// page_of(v, gi) reads it back as a scalar.
+__device__ __forceinline__ int tile_pages_lane(const int32_t* __restrict__ bt_row, int log2p, int t0, int T, int lane) {
+    const int gi = lane & 3, tok = t0 + 16 * gi;
+    return bt_row[(gi == 0 || tok < T ? tok : t0) >> log2p];
+}
+__device__ __forceinline__ int page_of(int v, int gi) { return __builtin_amdgcn_readlane(v, gi); }
 
 // Row indices of the tile's 4 token groups from their page ids (uniform).
 __device__ __forceinline__ void rows_from_pages(size_t* row, const int* pg, int P, int hkv, int g, int t0, int T) {
@@ -262,11 +270,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages_per_seq;
     const int P = a.page_size, log2p = L.log2p, hkv = a.num_kv_heads;
 
-    float m_run[4], l_lane[4];
+    float m_run[4];   // per head, wave-uniform: the running maximum
+    // the running sums of the weights per head, in LDS: a register for them
+    // would be held through every pass
+    float* l_run = (float*)(lds + kOffLsum) + 4 * wave;
     int e_run = -127;
     float4v acc[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_lane[r] = 0.0f; }
+    for (int r = 0; r < 4; ++r) { m_run[r] = -INFINITY; l_run[r] = 0.0f; }   // every lane writes the same value
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
     uint32_t bad = 0;
@@ -406,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
                     const float mn = fmaxf(m_run[r], wave_max_uniform(sv[r]));
                     alpha[r] = exp2f(m_run[r] - mn);
                     m_run[r] = mn;
-                    l_lane[r] *= alpha[r];
+                    l_run[r] *= alpha[r];
                 }
             }
             const int e_new = max(e_run, wave_max_uniform_i(ev));
@@ -423,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         for (int r = 0; r < 4; ++r) {
             if (r < G) {
                 const float w = __builtin_amdgcn_exp2f(sv[r] - m_run[r]);   // 0 for a masked token
-                l_lane[r] += w;
+                l_run[r] += wave_sum_uniform(w);
                 wl[r * kRowH + lane] = (_Float16)(w * rvs);
             }
         }
@@ -481,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const uint32_t vbase = oVc + (uint32_t)lane * lds_stride(a.cv);
     const uint32_t kabs = lds0 + kbase, vabs = lds0 + vbase;   // absolute addresses for the decode steps
     int t = start + wave * kTile;
-    int pgn[4] = {0, 0, 0, 0};   // page ids of the next tile's groups, loaded a tile ahead
+    int pgn[4] = {0, 0, 0, 0};   // page ids of the next tile's groups (scalars), loaded a tile ahead
     if (t < end) {
         // prologue: keys of the first tile
         size_t row[4];
@@ -491,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         stage_tile<PAD_K>(lds, oKc, a.k_cache, a.ck, L.magic_k, row, lane);
         stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, row, lane);
         stage_wait();
-        if (t + kStep < end) tile_pages(pgn, bt_row, log2p, t + kStep, T);
+        if (t + kStep < end) tile_pages(pgn, bt_row, log2p, t + kStep, T);   // waited for below, before the pass
         float cm[4], ms;
         uint32_t mq, rk, rv;
         mean_load(t, pg0[0], mq, ms);
@@ -543,6 +554,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         const bool valid = t + lane < T, valid_n = tn + lane < T;
         float cm_n[4], ms_n = 0.0f;
         uint32_t mq_n = 0, rk_n = 0, rv_n = 0;
+        int pgv = 0;   // the page ids of tile tn + kStep, one per lane (lanes 0..3)
         int pgnn[4] = {0, 0, 0, 0};
         stage_wait();   // this pass's key tile tn and value tile t
         if (has_next) {
@@ -550,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
             size_t row[4];
             rows_from_pages(row, pgn, P, hkv, g, tn, T);
             load_norms(tn, row, rk_n, rv_n);
-            if (tn + kStep < end) tile_pages(pgnn, bt_row, log2p, tn + kStep, T);
+            if (tn + kStep < end) pgv = tile_pages_lane(bt_row, log2p, tn + kStep, T, lane);
         }
         wave_lds_sync();
         RansLane vr, kr;
@@ -574,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
             // the prefetched page ids go to scalars before any copy is issued, so
             // that nothing waits for the copies until the next pass needs them
 #pragma unroll
-            for (int gi = 0; gi < 4; ++gi) pgnn[gi] = __builtin_amdgcn_readfirstlane(pgnn[gi]);
+            for (int gi = 0; gi < 4; ++gi) pgnn[gi] = page_of(pgv, gi);
             size_t row[4];   // from the page ids held through the pass
             rows_from_pages(row, pgn, P, hkv, g, tn, T);
             stage_tile<PAD_V>(lds, oVc, a.v_cache, a.cv, L.magic_v, row, lane);
@@ -596,7 +608,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     // ---- merge the 4 waves of this work-group
     float lsum[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lsum[r] = wave_sum(l_lane[r]);
+    for (int r = 0; r < 4; ++r) lsum[r] = l_run[r];
     __syncthreads();   // every wave is done with its LDS tiles
     float* mg = (float*)(lds + oW);   // reuse this wave's own region: [0..3] m, [4..7] l, [8] e, [16..] acc[4][128]
     // acc[i][r] of lane l is row 4(l/16) + r, column l % 16 of block i's p.v
