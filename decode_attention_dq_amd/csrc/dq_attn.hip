@@ -85,6 +85,7 @@ __device__ __forceinline__ void tile_pages(int* pg, const int32_t* __restrict__ 
 // The same page ids held in one register: lane gi (gi < 4) loads group gi's;
 // page_of(v, gi) reads it back as a scalar.
 __device__ __forceinline__ int tile_pages_lane(const int32_t* __restrict__ bt_row, int log2p, int t0, int T, int lane) {
+    asm volatile("" : "+v"(lane));   // recomputed here: hoisted, the offset would be held through the passes
     const int gi = lane & 3, tok = t0 + 16 * gi;
     return bt_row[(gi == 0 || tok < T ? tok : t0) >> log2p];
 }
@@ -491,6 +492,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     const uint32_t kbase = oKc + (uint32_t)lane * lds_stride(a.ck);
     const uint32_t vbase = oVc + (uint32_t)lane * lds_stride(a.cv);
     const uint32_t kabs = lds0 + kbase, vabs = lds0 + vbase;   // absolute addresses for the decode steps
+    // a stream's state bytes start at its tile row: the address is formed where it
+    // is needed (computed once and held, it would be spilled)
+    auto stream_base = [](uint32_t base) {
+        asm volatile("" : "+v"(base));
+        return base;
+    };
     int t = start + wave * kTile;
     int pgn[4] = {0, 0, 0, 0};   // page ids of the next tile's groups (scalars), loaded a tile ahead
     if (t < end) {
@@ -510,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         wave_lds_sync();
         const bool valid = t + lane < T;
         RansLane kr;
-        rans_init(kr, kabs);
+        rans_init(kr, stream_base(kabs));
         bad |= (valid && kr.x < kStateLow) ? 1u : 0u;
         float4v dk = float4v{0.f, 0.f, 0.f, 0.f};
         // keys only, as a rolled loop: it touches no accumulator array, and keeping
@@ -566,12 +573,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         }
         wave_lds_sync();
         RansLane vr, kr;
-        rans_init(vr, vabs);
+        rans_init(vr, stream_base(vabs));
         kr = vr;
         bad |= (valid && vr.x < kStateLow) ? 1u : 0u;
         float4v dk = float4v{0.f, 0.f, 0.f, 0.f};
         if (has_next) {
-            rans_init(kr, kabs);
+            rans_init(kr, stream_base(kabs));
             bad |= (valid_n && kr.x < kStateLow) ? 1u : 0u;
             pass(true, true, kr, vr, dk);
             bad |= (valid_n && (kr.x != kStateLow || rans_consumed(kr, kabs) > (uint32_t)a.ck)) ? 1u : 0u;
