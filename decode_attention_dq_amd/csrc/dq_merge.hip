@@ -145,24 +145,42 @@ __global__ __launch_bounds__(64 * 16) void merge_wide_kernel(MergeArgs a) {
 // One wave per (sequence, query head) row, four rows per work-group, for rows
 // with at most 64 partials: lane i holds (m, l) of partial i, the maxima and
 // the weighted sums of l are wave reductions, and each partial's weight is
-// read from its lane while the accumulator loads of all partials are in
-// flight together.
+// read from its lane. Every load goes out at once, before the row's context
+// length is known: the (m, l) of the partials, and the lane's two channels of
+// the first kPre partials (later ones are read in the sum); which partials hold
+// tokens (the first ceil(T_b / split_len), and the window slot, the last, when
+// there is one) is settled when the loads are back. The partials are added in
+// slot order, skipping those without weight.
 template <bool ROTATED>
 __global__ __launch_bounds__(256) void merge_rows_kernel(MergeArgs a, int rows) {
+    constexpr int kPre = 16;
     const int tid = threadIdx.x, lane = tid & 63;
     const int bh = blockIdx.x * 4 + (tid >> 6);
     if (bh >= rows) return;
     const float* p = a.partials + (size_t)bh * a.slot_count * kPartStride;
+    // slot_count <= 65; slot 64 can only be the unused window slot of a row without a window
+    const int sc = min(a.slot_count, 64);
+    float mi = -INFINITY, li = 0.0f;
+    if (lane < sc) {
+        mi = p[(size_t)lane * kPartStride];
+        li = p[(size_t)lane * kPartStride + 1];
+    }
+    float x0[kPre], x1[kPre];
+#pragma unroll
+    for (int c = 0; c < kPre; ++c) {
+        x0[c] = x1[c] = 0.0f;
+        if (c < sc) {
+            x0[c] = p[(size_t)c * kPartStride + 4 + lane];
+            x1[c] = p[(size_t)c * kPartStride + 4 + 64 + lane];
+        }
+    }
     const int len = a.context_lens[bh / a.num_q_heads];
     const int T = covered_tokens(len, a.cap);
     if (lane == 0 && a.err_word && (len < 0 || len > a.cap)) atomicOr(a.err_word, DQ_DEVERR_CONTEXT);
     const int n = (T + a.split_len - 1) / a.split_len;
-    const int slots = n + (a.window_slot >= 0 ? 1 : 0);
-    const int my = lane < n ? lane : a.window_slot;   // the partial this lane reads (lane < slots)
-    float mi = -INFINITY, li = 0.0f;
-    if (lane < slots) {
-        mi = p[(size_t)my * kPartStride];
-        li = p[(size_t)my * kPartStride + 1];
+    if (!(lane < n || lane == a.window_slot)) {   // a partial without tokens may hold anything
+        mi = -INFINITY;
+        li = 0.0f;
     }
     float M = mi;
 #pragma unroll
@@ -173,11 +191,18 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(MergeArgs a, int rows) 
     for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
     float v0 = 0.0f, v1 = 0.0f;
     if (M != -INFINITY) {
-        for (int i = 0; i < slots; ++i) {
-            const float f = __shfl(fi, i);
-            const int s = i < n ? i : a.window_slot;
-            const float* ps = p + (size_t)s * kPartStride;
-            if (f != 0.0f) {   // a partial without tokens (m = -inf) may hold anything
+#pragma unroll
+        for (int c = 0; c < kPre; ++c) {
+            const float f = __shfl(fi, c);
+            if (c < sc && f != 0.0f) {
+                v0 += x0[c] * f;
+                v1 += x1[c] * f;
+            }
+        }
+        for (int c = kPre; c < sc; ++c) {
+            const float f = __shfl(fi, c);
+            if (f != 0.0f) {
+                const float* ps = p + (size_t)c * kPartStride;
                 v0 += ps[4 + lane] * f;
                 v1 += ps[4 + 64 + lane] * f;
             }
