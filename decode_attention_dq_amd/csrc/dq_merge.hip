@@ -73,34 +73,41 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
 }
 
 // The same merge for few rows with up to 128 partials: 16 waves per row, wave
-// w holding partials w, w + 16, ..., w + 112 in registers. Every load of a
-// wave goes out before the row maximum is known (one memory round trip
-// instead of two per partial); the partials are added in the same order as
-// merge_kernel's.
+// w holding slots w, w + 16, ..., w + 112 in registers. Every load of a wave
+// goes out at once, before the row's context length and maximum are known
+// (one memory round trip); slots without tokens are dropped afterwards.
 template <bool ROTATED>
 __global__ __launch_bounds__(64 * 16) void merge_wide_kernel(MergeArgs a) {
     constexpr int kW = 16, kPer = 8;
     __shared__ float red[kW][132];
     const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const float* p = a.partials + (size_t)bh * a.slot_count * kPartStride;
-    const int len = a.context_lens[bh / a.num_q_heads];
-    const int T = covered_tokens(len, a.cap);
-    if (tid == 0 && a.err_word && (len < 0 || len > a.cap)) atomicOr(a.err_word, DQ_DEVERR_CONTEXT);
-    const int n = (T + a.split_len - 1) / a.split_len;
-    const int slots = n + (a.window_slot >= 0 ? 1 : 0);   // <= kW * kPer (the host's choice)
+    // the loads go out before the context length is known: slots i < min(slot_count,
+    // 128) (the host picks this kernel when a row's partials fit; a slot past them
+    // can only be the unused window slot); which hold tokens is settled after
+    const int sc = min(a.slot_count, kW * kPer);
     float ms[kPer], ls[kPer], x0[kPer], x1[kPer];
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
         const int i = wave + c * kW;
         ms[c] = -INFINITY;
         ls[c] = x0[c] = x1[c] = 0.0f;
-        if (i < slots) {
-            const float* ps = p + (size_t)(i < n ? i : a.window_slot) * kPartStride;
+        if (i < sc) {
+            const float* ps = p + (size_t)i * kPartStride;
             ms[c] = ps[0];
             ls[c] = ps[1];
             x0[c] = ps[4 + lane];
             x1[c] = ps[4 + 64 + lane];
         }
+    }
+    const int len = a.context_lens[bh / a.num_q_heads];
+    const int T = covered_tokens(len, a.cap);
+    if (tid == 0 && a.err_word && (len < 0 || len > a.cap)) atomicOr(a.err_word, DQ_DEVERR_CONTEXT);
+    const int n = (T + a.split_len - 1) / a.split_len;
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+        const int i = wave + c * kW;
+        if (!(i < n || i == a.window_slot)) ms[c] = -INFINITY;   // a partial without tokens may hold anything
     }
     float M = ms[0];
 #pragma unroll
