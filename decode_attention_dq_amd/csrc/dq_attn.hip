@@ -167,6 +167,7 @@ struct AttnLaunch {
     AttnArgs a;
     int log2p;
     uint32_t magic_k, magic_v;   // ceil(2^16 / (C / 4 + 1)) for the padded staging
+    int prio;                    // step the issue priority down per tile (launches of at most two rounds)
 };
 
 // PAD_K / PAD_V: containers laid out at the padded LDS stride; MEANS: key
@@ -198,10 +199,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
 
     // Issue priority. A SIMD issues to its oldest ready wave first, so in a
     // launch of about one round the work-groups dispatched first run ahead and
-    // each CU ends with its later ones at falling occupancy. Waves start at the
-    // highest priority and step down after each of their first three tiles, so
-    // the waves that are behind take the issue slots.
-    __builtin_amdgcn_s_setprio(3);
+    // each CU ends with its later ones at falling occupancy. In such launches
+    // waves start at the highest priority and step down after each of their
+    // first three tiles, so the waves that are behind take the issue slots. In
+    // longer launches the later rounds already mix the phases, and the steps
+    // cost time.
+    if (L.prio) __builtin_amdgcn_s_setprio(3);
 
     // ---- prologue: tables, zero regions, rotated queries
     {
@@ -605,9 +608,11 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) pgn[gi] = pgnn[gi];
         ++done;
-        if (done == 1) __builtin_amdgcn_s_setprio(2);
-        else if (done == 2) __builtin_amdgcn_s_setprio(1);
-        else if (done == 3) __builtin_amdgcn_s_setprio(0);
+        if (L.prio) {
+            if (done == 1) __builtin_amdgcn_s_setprio(2);
+            else if (done == 2) __builtin_amdgcn_s_setprio(1);
+            else if (done == 3) __builtin_amdgcn_s_setprio(0);
+        }
     }
     stage_wait();   // no copy into this wave's region may still be in flight
     if (bad && a.err_word) atomicOr(a.err_word, DQ_DEVERR_DECODE);
@@ -743,7 +748,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
         hipError_t e = launch_window(a, a.num_splits, s);
         if (e != hipSuccess) return e;
     }
-    dim3 grid((unsigned)(a.num_splits * a.num_kv_heads * a.batch));
+    const long wgs = (long)a.num_splits * a.num_kv_heads * a.batch;
+    L.prio = wgs <= 2L * 1024 ? 1 : 0;   // 4 resident work-groups on each of 256 CUs per round
+    dim3 grid((unsigned)wgs);
     hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, s, L);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
