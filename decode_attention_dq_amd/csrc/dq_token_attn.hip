@@ -298,11 +298,12 @@ __global__ __launch_bounds__(kThreads, 3) void token_attn_kernel(TokAttnArgs a) 
         grans_refill(rk, gk, kres, sk_);
 
         // KV heads in order: the softmax of group g, V head g (fused with K
-        // head g + 1 while there is one), the group's p.v. The loop is not
-        // unrolled (the kernel stays small in the instruction cache); acc[0]
-        // holds the current group's accumulators and the array rotates by one
-        // group per head, back to its order after the eighth.
-#pragma unroll 1
+        // head g + 1 while there is one), the group's p.v. acc[0] holds the
+        // current group's accumulators and the array rotates by one group per
+        // head, back to its order after the eighth. The loop is unrolled by
+        // two, so every other rotation is only a renaming of registers; fully
+        // unrolled, the kernel no longer fits the instruction cache.
+#pragma unroll 2
         for (int g = 0; g < kTokHeads; ++g) {
             float4_t wv;
 #pragma unroll
