@@ -253,6 +253,22 @@ def workloads_slots(bt, lens, P, b):
     return bt[b, t // P] * P + (t % P)
 
 
+def warm_up(torch, call, copies: int, seconds: float = 0.5) -> None:
+    """Back-to-back calls for about `seconds` before a workload is timed. The
+    cache builds before it leave the GPU idle, and the first calls after an
+    idle spell run at lower clocks (a workload timed right after its build
+    measured 3-10% slower than the same calls a few hundred ms later)."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(8 * copies):
+            call(i % copies)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int = 5) -> dict:
     """One decode-attention call per step on another workload, rotating through
     `copies` distinct caches (their total above the 256 MB MALL). For a ragged
@@ -310,9 +326,7 @@ def config_measurement(dq, torch, workloads, name: str, copies: int, reps: int =
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3 / n
 
-    for l in range(copies):
-        call(l)
-    torch.cuda.synchronize()
+    warm_up(torch, call, copies)
     attn = float(np.median([run() for _ in range(3)]))
     nbytes = algorithmic_bytes(w, lens, wl)
     res = {"batch": B, "context": "ragged %d..%d" % w.ragged if append else w.context,
@@ -383,9 +397,7 @@ def token_attention_time(dq, torch, workloads, tables, name: str, copies: int, r
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3 / n
 
-    for l in range(copies):
-        call(l)
-    torch.cuda.synchronize()
+    warm_up(torch, call, copies)
     t = float(np.median([run() for _ in range(3)]))
     ntok = int(np.sum(caches[0].lens))
     nbytes = ntok * (w.container + 4 + w.cv + 4)
@@ -463,9 +475,7 @@ def bf16_measurement(dq, torch, workloads, name: str, copies: int, dq_us: float,
         kc, vc, bt, cl = caches[l]
         dq.dq_bf16_decode_attention(qs[l], kc, vc, bt, cl, hkv, w.page_size, w.context, out, ws, stream=stream)
 
-    for l in range(copies):
-        call(l)
-    torch.cuda.synchronize()
+    warm_up(torch, call, copies)
     ev = []
     for _ in range(reps):
         for l in range(copies):
