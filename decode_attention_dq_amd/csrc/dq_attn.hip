@@ -175,6 +175,11 @@ struct AttnLaunch {
 // kernels without them keep their own register allocation).
 template <bool PAD_K, bool PAD_V, bool MEANS>
 __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
+    // Decoder lanes with the carried window. The unpadded instantiation
+    // without key means keeps all its values in registers only when the refill
+    // holds no aligned start (one more VALU instruction per refill); the
+    // others run faster holding it.
+    using Lane = RansLaneCarry<PAD_K || PAD_V || MEANS>;
     const AttnArgs& a = L.a;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // Work-groups reach the eight XCDs round-robin by linear index; with the KV
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
     // One pass over the 128 channels of a key tile (do_k) and/or a value tile
     // (do_v): two independent decode chains per lane, the q.k MFMA after each
     // 8 key channels, the p.v MFMAs after each 16 value channels.
-    auto pass = [&](bool do_k, bool do_v, RansLane& kr, RansLane& vr, float4v& dk) {
+    auto pass = [&](bool do_k, bool do_v, Lane& kr, Lane& vr, float4v& dk) {
         // the weights are the same A operand for every 16 channels of the tile:
         // for channel half c, the lane's row, or zeros when its group serves
         // the other half
@@ -519,7 +524,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
         load_norms(t, row, rk, rv);
         wave_lds_sync();
         const bool valid = t + lane < T;
-        RansLane kr;
+        Lane kr;
         rans_init(kr, stream_base(kabs));
         bad |= (valid && kr.x < kStateLow) ? 1u : 0u;
         float4v dk = float4v{0.f, 0.f, 0.f, 0.f};
@@ -575,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_kernel(AttnLaunch L) {
             if (tn + kStep < end) pgv = tile_pages_lane(bt_row, log2p, tn + kStep, T, lane);
         }
         wave_lds_sync();
-        RansLane vr, kr;
+        Lane vr, kr;
         rans_init(vr, stream_base(vabs));
         kr = vr;
         bad |= (valid && vr.x < kStateLow) ? 1u : 0u;

@@ -60,6 +60,52 @@ __device__ __forceinline__ uint32_t rans_consumed(const RansLane& r, uint32_t ba
     return r.ptr + (r.sel - kSel0) - base;
 }
 
+// The same decoder for a tile in LDS whose refills carry the window's two
+// aligned dwords (lo at a, hi at a + 4) from one refill to the next. At most 4
+// bytes go between refills, so the new aligned start is a or a + 4: the new lo
+// is the old lo or the old hi, and only the dword after it is read. One 4-byte
+// read per refill costs the LDS about half of a two-dword read when the lanes'
+// windows sit at different offsets (6 against 12 cycles per wave instruction
+// at a 37-byte lane stride, by the SQ counters of a microbenchmark).
+// KEEP_A holds the aligned start a in a register; without it the refill
+// compares the old and new window addresses instead (one VALU instruction
+// more per refill, one register less per chain).
+template <bool KEEP_A>
+struct RansLaneCarry {
+    uint32_t x, ptr, win, sel;   // as in RansLane
+    uint32_t a;                  // ptr rounded down to a dword (held when KEEP_A)
+    uint32_t lo, hi;             // the dwords at a and a + 4
+};
+template <bool KEEP_A>
+__device__ __forceinline__ void rans_init(RansLaneCarry<KEEP_A>& r, uint32_t base) {
+    r.x = (uint32_t)(*(lds_u8*)(size_t)base) | ((uint32_t)(*(lds_u8*)(size_t)(base + 1)) << 8) |
+          ((uint32_t)(*(lds_u8*)(size_t)(base + 2)) << 16);
+    r.ptr = base + kStateBytes;
+    r.win = 0;
+    r.sel = kSel0;
+    r.a = r.ptr & ~3u;
+    r.lo = *(lds_u32*)(size_t)r.a;
+    r.hi = 0;   // read by the first refill (its aligned start is still a)
+}
+template <bool KEEP_A>
+__device__ __forceinline__ void rans_refill(RansLaneCarry<KEEP_A>& r) {
+    const uint32_t np = r.ptr + (r.sel - kSel0);
+    const uint32_t na = np & ~3u;
+    // the window moved to the next dword when its address crossed a multiple of
+    // 4 (it moved by at most 4 bytes)
+    const bool up = KEEP_A ? na != r.a : (np ^ r.ptr) >= 4u;
+    r.lo = up ? r.hi : r.lo;
+    r.hi = *(lds_u32*)(size_t)(na + 4u);
+    r.win = __builtin_amdgcn_alignbyte(r.hi, r.lo, np);
+    r.ptr = np;
+    r.a = na;
+    r.sel = kSel0;
+}
+template <bool KEEP_A>
+__device__ __forceinline__ uint32_t rans_consumed(const RansLaneCarry<KEEP_A>& r, uint32_t base) {
+    return r.ptr + (r.sel - kSel0) - base;
+}
+
 // One rANS decode step (D-Quant section 3.1, Dec): the slot x mod 2^p selects
 // the table entry of the symbol m that owns it, the state becomes
 // f_m * floor(x / 2^p) + (slot - c_m), and one byte is shifted in when the
@@ -96,10 +142,12 @@ __device__ __forceinline__ uint32_t rans_dec_step(RansLane& r, uint32_t tab, uin
 // The same step from a two-dword entry (wide_entry_pack): one 8-byte table
 // read, and the 24-bit multiply-add takes f_m and the bias straight from it.
 // The entry's dword 0 carries the level's fp16 high byte in bits 24..31.
-__device__ __forceinline__ u32x2 rans_lookup_wide(const RansLane& r, uint32_t tab, uint32_t mask) {
+template <class Lane>
+__device__ __forceinline__ u32x2 rans_lookup_wide(const Lane& r, uint32_t tab, uint32_t mask) {
     return *(lds_u32x2*)(size_t)(tab + ((r.x & mask) << 3));
 }
-__device__ __forceinline__ void rans_advance_wide(RansLane& r, u32x2 e, uint32_t p) {
+template <class Lane>
+__device__ __forceinline__ void rans_advance_wide(Lane& r, u32x2 e, uint32_t p) {
     const uint32_t xn = __umul24(e.x, r.x >> p) + e.y;      // e.x & 0xFFFFFF = f_m
     const uint32_t t = __builtin_amdgcn_perm(xn, r.win, r.sel);
     const bool need = xn < kStateLow;
