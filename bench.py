@@ -550,7 +550,9 @@ def record_issue(sq_csv: str, workload: str = "decode_qwen3_8b", cus: int = 256,
     SQ_BUSY_CU_CYCLES and SQ_LDS_IDX_ACTIVE for the headline kernel, the VALU
     issue cycles per SIMD (4 per wave instruction) and the LDS-active cycles as
     fractions of the busy cycles per CU, written to profiles/traffic.json with
-    the hash of the current kernel sources."""
+    the hash of the current kernel sources. The VALU figure counts every wave
+    instruction at 4 cycles; simple VOP2 instructions issue in fewer, so it can
+    pass 1 when the VALU is saturated."""
     import csv
     sums = {}
     for r in csv.DictReader(open(sq_csv)):

@@ -62,7 +62,9 @@ def test_issue_record_follows_sources(monkeypatch):
     got = bench.recorded_issue("attn_kernel", "decode_qwen3_8b")
     if sq is not None and sq["source_sha256"] == bench.attn_source_hash():
         assert got == {"valu_issue_frac": sq["valu_issue_frac"], "lds_active_frac": sq["lds_active_frac"]}
-        assert 0.0 < got["valu_issue_frac"] <= 1.0 and 0.0 < got["lds_active_frac"] <= 1.0
+        # the VALU figure counts 4 cycles per wave instruction and can pass 1 (simple
+        # VOP2 instructions issue in fewer); the LDS figure is a true fraction
+        assert 0.0 < got["valu_issue_frac"] < 1.5 and 0.0 < got["lds_active_frac"] <= 1.0
     else:
         assert got is None
     monkeypatch.setattr(bench, "attn_source_hash", lambda: "0" * 64)
