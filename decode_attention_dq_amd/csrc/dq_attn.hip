@@ -688,20 +688,30 @@ __global__ __launch_bounds__(kThreads) void decode_symbols_kernel(const uint32_t
     const long s = s0 + lane;
     if (s >= n) return;
     const uint32_t base = lds0 + oT + (uint32_t)lane * (uint32_t)C;
-    RansLane r;
-    rans_init(r, base);
-    const bool bad_init = r.x < kStateLow;
+    // the decoder lanes of the attention kernel, both forms of the carried
+    // window refill (odd waves hold the aligned start, even waves do not)
     const uint32_t mask = (1u << p) - 1u;
     uint32_t* o = (uint32_t*)(out + s * kHeadDim);
-    for (int i = 0; i < kHeadDim / 4; ++i) {
-        rans_refill(r);
-        uint32_t w = 0;
+    auto run = [&](auto& r) {
+        rans_init(r, base);
+        const bool bad_init = r.x < kStateLow;
+        for (int i = 0; i < kHeadDim / 4; ++i) {
+            rans_refill(r);
+            uint32_t w = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w |= (rans_dec_step(r, lds0, mask, (uint32_t)p) >> 28) << (8 * k);
-        o[i] = w;
+            for (int k = 0; k < 4; ++k) w |= (rans_dec_step(r, lds0, mask, (uint32_t)p) >> 28) << (8 * k);
+            o[i] = w;
+        }
+        if ((bad_init || r.x != kStateLow || rans_consumed(r, base) > (uint32_t)C) && err)
+            atomicOr(err, DQ_DEVERR_DECODE);
+    };
+    if (wave & 1) {
+        RansLaneCarry<true> r;
+        run(r);
+    } else {
+        RansLaneCarry<false> r;
+        run(r);
     }
-    if ((bad_init || r.x != kStateLow || rans_consumed(r, base) > (uint32_t)C) && err)
-        atomicOr(err, DQ_DEVERR_DECODE);
 }
 
 // Split partials of dq_decode_attention_noalloc, for callers that cannot

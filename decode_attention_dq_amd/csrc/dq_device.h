@@ -25,48 +25,23 @@ typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
 
 // Per-lane rANS decoder state. The container bytes are read through a
 // 4-byte window refilled every 4 steps (at most one byte is consumed per
-// step), so a step needs one LDS access (the table) instead of two.
+// step), so a step needs one LDS access (the table) instead of two. The
+// per-token kernel refills it from HBM; tiles staged in LDS use RansLaneCarry.
 struct RansLane {
     uint32_t x;     // state, in [2^16, 2^24) between steps
-    uint32_t ptr;   // LDS address of the window's first byte
+    uint32_t ptr;   // address of the window's first byte
     uint32_t win;   // the 4 bytes at ptr (first byte in bits 0..7)
     uint32_t sel;   // v_perm selector kSel0 + bytes consumed from the window
 };
 constexpr uint32_t kSel0 = 0x06050400u;   // result bytes: win[k], x[0], x[1], x[2]
 
-// State from the 3-byte little-endian flush at LDS address `base`.
-__device__ __forceinline__ void rans_init(RansLane& r, uint32_t base) {
-    r.x = (uint32_t)(*(lds_u8*)(size_t)base) | ((uint32_t)(*(lds_u8*)(size_t)(base + 1)) << 8) |
-          ((uint32_t)(*(lds_u8*)(size_t)(base + 2)) << 16);
-    r.ptr = base + kStateBytes;
-    r.win = 0;
-    r.sel = kSel0;
-}
-
-// Advance the window past the bytes consumed since the last refill and load
-// the next 4 bytes (two aligned dwords and a byte-align).
-__device__ __forceinline__ void rans_refill(RansLane& r) {
-    r.ptr += r.sel - kSel0;
-    asm volatile("" : "+v"(r.ptr));
-    const uint32_t a = r.ptr & ~3u;
-    const uint32_t lo = *(lds_u32*)(size_t)a;
-    const uint32_t hi = *(lds_u32*)(size_t)(a + 4);
-    r.win = __builtin_amdgcn_alignbyte(hi, lo, r.ptr);
-    r.sel = kSel0;
-}
-
-// Bytes consumed since rans_init.
-__device__ __forceinline__ uint32_t rans_consumed(const RansLane& r, uint32_t base) {
-    return r.ptr + (r.sel - kSel0) - base;
-}
-
-// The same decoder for a tile in LDS whose refills carry the window's two
-// aligned dwords (lo at a, hi at a + 4) from one refill to the next. At most 4
+// The decoder for a tile in LDS. A refill carries the window's two aligned
+// dwords (lo at a, hi at a + 4) on to the next refill. At most 4
 // bytes go between refills, so the new aligned start is a or a + 4: the new lo
 // is the old lo or the old hi, and only the dword after it is read. One 4-byte
-// read per refill costs the LDS about half of a two-dword read when the lanes'
-// windows sit at different offsets (6 against 12 cycles per wave instruction
-// at a 37-byte lane stride, by the SQ counters of a microbenchmark).
+// read per refill costs the LDS about half of reading both dwords when the
+// lanes' windows sit at different offsets (6 against 12 cycles per wave
+// instruction at a 37-byte lane stride, by the SQ counters of a microbenchmark).
 // KEEP_A holds the aligned start a in a register; without it the refill
 // compares the old and new window addresses instead (one VALU instruction
 // more per refill, one register less per chain).
@@ -76,6 +51,7 @@ struct RansLaneCarry {
     uint32_t a;                  // ptr rounded down to a dword (held when KEEP_A)
     uint32_t lo, hi;             // the dwords at a and a + 4
 };
+// State from the 3-byte little-endian flush at LDS address `base`.
 template <bool KEEP_A>
 __device__ __forceinline__ void rans_init(RansLaneCarry<KEEP_A>& r, uint32_t base) {
     r.x = (uint32_t)(*(lds_u8*)(size_t)base) | ((uint32_t)(*(lds_u8*)(size_t)(base + 1)) << 8) |
@@ -101,6 +77,7 @@ __device__ __forceinline__ void rans_refill(RansLaneCarry<KEEP_A>& r) {
     r.a = na;
     r.sel = kSel0;
 }
+// Bytes consumed since rans_init.
 template <bool KEEP_A>
 __device__ __forceinline__ uint32_t rans_consumed(const RansLaneCarry<KEEP_A>& r, uint32_t base) {
     return r.ptr + (r.sel - kSel0) - base;
@@ -113,20 +90,8 @@ __device__ __forceinline__ uint32_t rans_consumed(const RansLaneCarry<KEEP_A>& r
 // from the window; the shift-in is a v_perm whose selector counts the bytes
 // already taken, so the step has no branch. `tab` is the table's absolute
 // LDS address. Returns the entry. At most 4 steps may run between refills.
-__device__ __forceinline__ uint32_t rans_lookup(const RansLane& r, uint32_t tab, uint32_t mask) {
-    return *(lds_u32*)(size_t)(tab + ((r.x & mask) << 2));
-}
-__device__ __forceinline__ void rans_advance(RansLane& r, uint32_t e, uint32_t p) {
-    const uint32_t f = (e >> 18) & 1023u;
-    const uint32_t bias = (e >> 8) & 1023u;
-    const uint32_t xn = __umul24(f, r.x >> p) + bias;       // f < 2^10, x >> p < 2^14
-    const uint32_t t = __builtin_amdgcn_perm(xn, r.win, r.sel);
-    const bool need = xn < kStateLow;
-    r.x = need ? t : xn;
-    r.sel += need ? 1u : 0u;
-    asm volatile("" : "+v"(r.sel));   // one carry-in add per step (no 0/1 temporaries summed in a tree)
-}
-__device__ __forceinline__ uint32_t rans_dec_step(RansLane& r, uint32_t tab, uint32_t mask, uint32_t p) {
+template <class Lane>
+__device__ __forceinline__ uint32_t rans_dec_step(Lane& r, uint32_t tab, uint32_t mask, uint32_t p) {
     const uint32_t e = *(lds_u32*)(size_t)(tab + ((r.x & mask) << 2));
     const uint32_t f = (e >> 18) & 1023u;
     const uint32_t bias = (e >> 8) & 1023u;
@@ -156,13 +121,9 @@ __device__ __forceinline__ void rans_advance_wide(Lane& r, u32x2 e, uint32_t p) 
     asm volatile("" : "+v"(r.sel));
 }
 
-// Two fp16 levels (entries e0 for the lower channel, e1 for the upper) packed
-// into one dword: the level's high byte sits in bits 0..7 of an entry and its
-// low byte is zero.
-__device__ __forceinline__ uint32_t pack_levels(uint32_t e0, uint32_t e1) {
-    return __builtin_amdgcn_perm(e1, e0, 0x040C000Cu);
-}
-// The same from dword 0 of two-dword entries (level byte in bits 24..31).
+// Two fp16 levels (dword 0 of the two-dword entries e0 for the lower channel
+// and e1 for the upper) packed into one dword: the level's high byte sits in
+// bits 24..31 of an entry and its low byte is zero.
 __device__ __forceinline__ uint32_t pack_levels_wide(uint32_t e0, uint32_t e1) {
     return __builtin_amdgcn_perm(e1, e0, 0x070C030Cu);
 }
